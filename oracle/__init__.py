@@ -1,0 +1,41 @@
+"""Float64 CPU oracle for paged GQA decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import, call or run anything in this package.  The product
+path (the HIP library and its Python binding) never does, and shares no code
+with it: no kernels, helpers, constants or tables.
+
+What it computes is fixed by the PersistentKV pages (arXiv 2606.26666):
+  * GQA decode: G = Hq/Hkv query heads share one KV head, one new query token
+    per row (gist.science explainer, "Technische Samenvatting" > Methodologie >
+    "1. Native Block-Table Decode Engine"; Lattice and fugumt.com abstracts).
+  * The KV cache is read in place through a per-row block table of 16-token
+    pages (same section, item "Layout"; abstracts: page size 16).
+  * Sequence splitting into disjoint ranges with an exact merge of partial
+    online-softmax states, row-local bounds from the true lengths, and a
+    compact list of non-empty (row, KV head, split) tasks (same section, items
+    "Sequentie Splitting", "Row-Local Bounds", "Compact Workqueue").
+  * A host policy choosing split or workqueue scheduling from the batch size
+    and lengths (same page, "2. Calibrated Adaptive Policy").
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  scale = 1/sqrt(d); query head h reads KV head floor(h/G); token t of a row
+  lives in page block_table[b, t // 16] at slot t % 16; K and V pools are
+  [num_pages, Hkv, 16, d]; a row with N_b = 0 yields out = 0, lse = -inf.
+
+Pins: every function here is checked against something other than itself in
+``tests/test_oracle_pins.py`` (brute force, closed forms, a library special
+case, invariances) -- except ``policy``, whose thresholds are this project's
+own calibration choice: parity unpinned for the policy constants (its
+structural properties are still tested).
+"""
+from .ref import (  # noqa: F401
+    MODE_SPLIT,
+    MODE_WORKQUEUE,
+    attend,
+    merge_states,
+    partial_state,
+    plan_tasks,
+    policy,
+    split_merge,
+)

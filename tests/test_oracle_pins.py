@@ -1,0 +1,145 @@
+"""Pin the float64 oracle to brute force, closed forms, a library special case,
+invariances and hand-derived fixtures (CPU only)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_attend_pins(pin):
+    pin(oracle.attend)
+
+
+def test_hand_fixture():
+    with open(os.path.join(GOLDEN, "two_token_attention.json")) as f:
+        fx = json.load(f)
+    pins.pin_hand_fixture(oracle.attend, fx)
+
+
+# --------------------------------------------------------------------------- split + merge
+
+@pytest.mark.parametrize("mode,params", [(oracle.MODE_SPLIT, [1, 2, 3, 4, 7, 16]),
+                                         (oracle.MODE_WORKQUEUE, [1, 2, 3, 5, 64])])
+def test_split_merge_equals_dense(mode, params):
+    """The exact merge of split states reproduces the dense result for any split."""
+    rng = np.random.default_rng(21)
+    c = pins.rand_case(rng, B=3, Hq=4, Hkv=2, D=8, page_size=4, lens=[0, 1, 97])
+    ref_out, ref_lse = oracle.attend(c["q"], c["k_pool"], c["v_pool"], c["block_table"],
+                                     c["seq_lens"], c["scale"], page_size=4)
+    for p in params:
+        tasks, offs = oracle.plan_tasks(c["seq_lens"], 2, 4, mode, p)
+        out, lse = oracle.split_merge(c["q"], c["k_pool"], c["v_pool"], c["block_table"],
+                                      c["seq_lens"], c["scale"], tasks, offs, page_size=4)
+        assert pins._rel(out, ref_out) < 1e-12, p
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isneginf(lse), np.isneginf(ref_lse))
+        assert np.max(np.abs(lse[fin] - ref_lse[fin])) < 1e-12, p
+
+
+def test_neutral_injection_is_identity():
+    """Neutral states (m=-inf, l=0, o=0) change no bit of the merged result."""
+    rng = np.random.default_rng(22)
+    c = pins.rand_case(rng, B=2, Hq=4, Hkv=2, D=8, page_size=4, lens=[50, 13])
+    tasks, offs = oracle.plan_tasks(c["seq_lens"], 2, 4, oracle.MODE_SPLIT, 4)
+    args = (c["q"], c["k_pool"], c["v_pool"], c["block_table"], c["seq_lens"], c["scale"],
+            tasks, offs)
+    a = oracle.split_merge(*args, page_size=4)
+    b = oracle.split_merge(*args, page_size=4, extra_neutral=3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_merge_states_two_halves_closed_form():
+    """Merging the states of two halves equals the state of the whole range."""
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((3, 5))
+    K = rng.standard_normal((11, 5))
+    V = rng.standard_normal((11, 5))
+    m, l, o = oracle.partial_state(q, K, V, 0.7)
+    m1, l1, o1 = oracle.partial_state(q, K[:4], V[:4], 0.7)
+    m2, l2, o2 = oracle.partial_state(q, K[4:], V[4:], 0.7)
+    for h in range(3):
+        out, lse = oracle.merge_states([m1[h], m2[h]], [l1[h], l2[h]], np.stack([o1[h], o2[h]]))
+        assert np.allclose(out, o[h] / l[h], rtol=1e-13, atol=0)
+        assert abs(lse - (m[h] + math.log(l[h]))) < 1e-13
+    out, lse = oracle.merge_states([-np.inf, -np.inf], [0.0, 0.0], np.zeros((2, 5)))
+    assert np.all(out == 0) and lse == -np.inf
+
+
+# --------------------------------------------------------------------------- task list
+
+def _check_coverage(seq_lens, Hkv, P, tasks, offs):
+    n = [-(-int(x) // P) for x in seq_lens]
+    seen = {}
+    for b, g, s, c in tasks:
+        p0, p1 = s * c, min((s + 1) * c, n[b])
+        assert p0 < p1, "empty task emitted"
+        for p in range(p0, p1):
+            key = (b, g, p)
+            assert key not in seen, "page covered twice"
+            seen[key] = 1
+    assert len(seen) == Hkv * sum(n), "pages missed"
+    S = [int(offs[b + 1] - offs[b]) for b in range(len(seq_lens))]
+    assert len(tasks) == Hkv * sum(S)
+    assert offs[0] == 0 and all(offs[i] <= offs[i + 1] for i in range(len(seq_lens)))
+
+
+def test_task_list_golden():
+    with open(os.path.join(GOLDEN, "task_lists.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        tasks, offs = oracle.plan_tasks(case["seq_lens"], case["Hkv"], 16, case["mode"],
+                                        case["param"])
+        assert tasks.tolist() == case["tasks"], case["name"]
+        assert offs.tolist() == case["split_offsets"], case["name"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_task_list_vs_walking_enumerator(seed):
+    rng = np.random.default_rng(300 + seed)
+    B = int(rng.integers(1, 9))
+    lens = rng.integers(0, 700, size=B)
+    lens[rng.integers(0, B)] = 0
+    Hkv = int(rng.integers(1, 5))
+    for S in (1, 2, 3, 4, 8, 64):
+        tasks, offs = oracle.plan_tasks(lens, Hkv, 16, oracle.MODE_SPLIT, S)
+        walk = brute.tasks_by_walking(lens, Hkv, 16, lambda b, n: -(-n // S))
+        assert tasks.tolist() == walk
+        _check_coverage(lens, Hkv, 16, tasks.tolist(), offs)
+        assert max(offs[1:] - offs[:-1]) <= S
+    for c in (1, 3, 4, 16, 1000):
+        tasks, offs = oracle.plan_tasks(lens, Hkv, 16, oracle.MODE_WORKQUEUE, c)
+        walk = brute.tasks_by_walking(lens, Hkv, 16, lambda b, n: c)
+        assert tasks.tolist() == walk
+        _check_coverage(lens, Hkv, 16, tasks.tolist(), offs)
+
+
+def test_task_list_errors():
+    with pytest.raises(ValueError):
+        oracle.plan_tasks([16], 1, 16, 7, 1)
+    with pytest.raises(ValueError):
+        oracle.plan_tasks([16], 1, 16, oracle.MODE_SPLIT, 0)
+
+
+# --------------------------------------------------------------------------- policy (structure)
+
+def test_policy_structure():
+    """The pages: one long row -> sequence splitting; 8 long ragged rows ->
+    workqueue.  Thresholds are this project's own (parity unpinned)."""
+    from workloads import CONFIGS, make_lengths
+    m, p = oracle.policy([32768], 8, 16, 256)
+    assert m == oracle.MODE_SPLIT and p & (p - 1) == 0 and p >= 64
+    lens = make_lengths(CONFIGS["b8_bimodal"], 20260623)
+    m, p = oracle.policy(lens, 8, 16, 256)
+    assert m == oracle.MODE_WORKQUEUE and 4 <= p <= 256 and p & (p - 1) == 0
+    assert oracle.policy([0, 0], 8, 16, 256) == (oracle.MODE_SPLIT, 1)
+    m, p = oracle.policy([100, 0], 8, 16, 256)
+    assert m == oracle.MODE_SPLIT
