@@ -1,0 +1,280 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged grouped-query-attention decode for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (PersistentKV, arXiv 2606.26666):
+ *   single-query (decode) attention for grouped-query attention.  G = Hq/Hkv
+ *   query heads share one KV head (gist.science explainer, "Technische
+ *   Samenvatting" > Methodologie > "1. Native Block-Table Decode Engine").  It
+ *   runs in place over a paged KV cache through a block table, without
+ *   repacking pages (same section, item "Layout").  Work is mapped by
+ *   (batch row, KV head, sequence split), so one K/V page tile serves all G
+ *   query heads of its group (Lattice and fugumt.com abstracts).  Long rows
+ *   are split into disjoint ranges whose partial online-softmax states a
+ *   separate merge combines exactly (item "Sequentie Splitting").  Ranges
+ *   follow each row's true length (item "Row-Local Bounds").  Only non-empty
+ *   (row, KV head, split) tasks are emitted, as a 1-D list (item "Compact
+ *   Workqueue").
+ *
+ * For row b and query head h, with g = floor(h / G) and N_b = seq_lens[b]:
+ *   s_t = scale * <q[b,h,:], K[page(b,t), g, t%16, :]>     t in [0, N_b)
+ *   out[b,h,:] = sum_t softmax(s)_t * V[page(b,t), g, t%16, :]
+ *   lse[b,h]   = log sum_t exp(s_t)
+ *   with page(b,t) = block_table[b, t/16].
+ * A row with N_b = 0 gets out = 0 and lse = -inf.
+ *
+ * Conventions
+ *   - Every call returns an int status (pkv_status).  No exception crosses
+ *     the ABI.  The library allocates no device memory and keeps no per-call
+ *     state.  The caller owns every buffer.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously and never synchronised.
+ *   - Supported shapes: page_size = 16, head_dim in {64, 128},
+ *     G = Hq/Hkv in {1, 2, 4, 8}.  Others return PKV_ERR_UNSUPPORTED.
+ *   - Data types: q, K, V and out are IEEE fp16.  lse and the partial states
+ *     are fp32.  Indices are int32.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* Status codes. */
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,      /* null pointer, negative size, inconsistent shapes */
+  PKV_ERR_UNSUPPORTED = 2,      /* head_dim, page_size or G outside the supported set */
+  PKV_ERR_BUFFER_TOO_SMALL = 3, /* caller buffer too small; size outputs hold the need */
+  PKV_ERR_BAD_INDEX = 4,        /* block-table entry outside [0, num_pages) */
+  PKV_ERR_HIP = 5               /* a HIP runtime call failed; see pkv_last_hip_error */
+};
+
+/* Scheduling modes of the task list (gist.science explainer, "2. Calibrated
+ * Adaptive Policy": sequence splitting for one long row, the compact
+ * workqueue for batches of 8 or more long rows). */
+enum pkv_mode {
+  PKV_MODE_SPLIT = 0,     /* param = S: every row is cut into at most S splits */
+  PKV_MODE_WORKQUEUE = 1  /* param = c: every split holds c pages (the last may hold fewer) */
+};
+
+/* Bits of the device error word that pkv_decode's kernels set (sticky until
+ * pkv_workspace_init).  A flagged task or page is skipped, never read. */
+enum pkv_device_error {
+  PKV_DEVERR_TASK = 1u,        /* task record out of range for B, Hkv or the row length */
+  PKV_DEVERR_PAGE = 2u,        /* block-table entry outside [0, num_pages) */
+  PKV_DEVERR_ROW = 4u,         /* seq_lens[b] < 0 or above max_pages_per_row * 16 */
+  PKV_DEVERR_SLOT = 8u         /* split_offsets points outside the partial-state slots */
+};
+
+/* Policy constants.  The pages print no thresholds.  These are this
+ * library's own calibration; see pkv_policy. */
+typedef struct pkv_policy_params {
+  float tasks_per_cu;   /* target task count T* = tasks_per_cu * num_cus */
+  int32_t chunk_min;    /* workqueue chunk bounds, in pages */
+  int32_t chunk_max;
+  int32_t split_max;    /* split-mode cap on S */
+  float uniform_ratio;  /* lengths within this max/min ratio count as uniform */
+} pkv_policy_params;
+
+/* ABI version (PKV_ABI_VERSION of the built library). */
+int pkv_abi_version(void);
+
+/* Static, human-readable text of a status code.  Never NULL. */
+const char* pkv_status_string(int status);
+
+/* hipError_t of the last PKV_ERR_HIP returned on this thread (0 if none). */
+int pkv_last_hip_error(void);
+
+/* Fill *params with the default policy constants.  Returns PKV_ERR_INVALID_ARG
+ * if params is NULL. */
+int pkv_policy_defaults(pkv_policy_params* params);
+
+/*
+ * pkv_policy -- choose the scheduling mode and its parameter for one step.
+ * Host only and deterministic.  The device is not touched.
+ *
+ * Source: gist.science explainer, "2. Calibrated Adaptive Policy".  A single
+ * long row uses sequence splitting to open enough parallel work.  A batch of
+ * 8 or more long rows uses the compact workqueue, which amortises the
+ * split+merge overhead.  The fugumt.com (v2) abstract calls the calibrated
+ * policy "roofline-style".  The branches that hand work to another library
+ * are outside this library.
+ *
+ * Rule, with n_b = ceil(N_b / page_size), active rows having n_b > 0, and
+ * T* = tasks_per_cu * num_cus:
+ *   - no active row: (SPLIT, 1).
+ *   - one active row, or max n_b <= uniform_ratio * min n_b over active rows:
+ *     SPLIT with S = the smallest power of two >= T* / (B_active * Hkv),
+ *     capped at split_max.
+ *   - otherwise: WORKQUEUE with c = the largest power of two
+ *     <= Hkv * sum n_b / T*, clamped to [chunk_min, chunk_max].
+ *
+ * seq_lens: host int32 [B].  params: NULL selects the defaults.
+ * Outputs *mode (pkv_mode) and *param.
+ * Errors: PKV_ERR_INVALID_ARG for a NULL pointer, B < 0, Hkv < 1,
+ * page_size < 1, num_cus < 1 or a negative length.
+ */
+int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
+               int32_t num_cus, const pkv_policy_params* params, int32_t* mode,
+               int32_t* param);
+
+/*
+ * pkv_plan -- build the compact task list and the per-row split offsets.
+ * Host only and deterministic.
+ *
+ * Source: gist.science explainer, Methodologie, items "Row-Local Bounds" and
+ * "Compact Workqueue".  Tile counts and split ranges follow each row's true
+ * length, and only non-empty (row, KV head, split) intervals become tasks.
+ * The Lattice and fugumt.com abstracts say the same.
+ *
+ * With n_b = ceil(N_b / page_size):
+ *   chunk c_b = ceil(n_b / param)   in PKV_MODE_SPLIT
+ *             = param               in PKV_MODE_WORKQUEUE
+ *   S_b = ceil(n_b / c_b), or 0 when N_b = 0.
+ *   Task record = int32[4] {row b, kv_head g, split s, c_b}, ordered by b,
+ *   then g, then s.  Split s covers pages [s*c_b, min((s+1)*c_b, n_b)), that
+ *   is tokens [s*c_b*16, min((s+1)*c_b*16, N_b)).
+ *   num_tasks = Hkv * sum_b S_b.
+ *   split_offsets[0..B] = the exclusive prefix sum of S_b.
+ *   num_partial_slots = split_offsets[B].  Split s of row b owns slot
+ *   split_offsets[b] + s.
+ *
+ * Arguments:
+ *   seq_lens          host int32 [B]
+ *   max_pages_per_row row stride of block_table.  Every n_b must be <= it.
+ *   block_table       host int32 [B, max_pages_per_row], or NULL.  If given,
+ *                     every entry a task will read (p < n_b) must lie in
+ *                     [0, num_pages).  Otherwise PKV_ERR_BAD_INDEX.
+ *   num_pages         pool size in pages.  Checked only when block_table != NULL.
+ *   tasks             host int32 [task_cap][4], or NULL for a size query
+ *   split_offsets     host int32 [B+1], or NULL
+ *   num_tasks, num_partial_slots  outputs, always written on PKV_OK and on
+ *                     PKV_ERR_BUFFER_TOO_SMALL
+ * Errors: PKV_ERR_INVALID_ARG (NULL seq_lens / outputs, negative length,
+ * n_b > max_pages_per_row, unknown mode, param < 1, page_size != 16,
+ * more than 2^31-1 tasks); PKV_ERR_BAD_INDEX; PKV_ERR_BUFFER_TOO_SMALL when
+ * tasks != NULL and task_cap < num_tasks.
+ */
+int pkv_plan(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
+             int32_t max_pages_per_row, const int32_t* block_table, int64_t num_pages,
+             int32_t mode, int32_t param, int32_t* tasks, int64_t task_cap,
+             int32_t* split_offsets, int64_t* num_tasks, int64_t* num_partial_slots);
+
+/*
+ * pkv_workspace_size -- device workspace bytes that pkv_decode needs.
+ * Layout: a 256-byte control block (task counter, exit counter, error word),
+ * then the fp32 partial outputs [num_partial_slots][Hq][head_dim], then the
+ * fp32 (max, sum) pairs [num_partial_slots][Hq][2].  The total is rounded up
+ * to 256 bytes.
+ * Errors: PKV_ERR_INVALID_ARG for NULL bytes or a negative size.
+ */
+int pkv_workspace_size(int64_t num_partial_slots, int32_t Hq, int32_t head_dim,
+                       size_t* bytes);
+
+/*
+ * pkv_workspace_init -- zero the workspace's control block on `stream`.
+ * Call it once after allocating a workspace.  It also clears the device
+ * error word.  pkv_decode leaves the counters at zero when it completes, so
+ * one init serves any number of later decodes on that workspace.
+ * Errors: PKV_ERR_INVALID_ARG (NULL or fewer than 256 bytes), PKV_ERR_HIP.
+ */
+int pkv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_workspace_error_flags -- copy the device error word (pkv_device_error
+ * bits) to *flags.  This synchronises `stream`, so it is for tests and
+ * debugging, not the hot path.
+ */
+int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stream);
+
+/*
+ * pkv_decode -- run one decode step: the persistent decode kernel over the
+ * task list, then the merge kernel.  This makes two launches on `stream`.
+ *
+ * Source: gist.science explainer, Methodologie, item "Sequentie Splitting".
+ * Each split computes a partial online-softmax state and a separate merge
+ * combines the states exactly.  Item "Compact Workqueue": one 1-D grid runs
+ * the task list.  The fugumt.com abstract reports 2 launches per step for
+ * this schedule.  A row with a single split writes its output directly.
+ *
+ * All pointers are device pointers.  Tensors are contiguous, row-major:
+ *   q            fp16  [B, Hq, head_dim]
+ *   k_pool       fp16  [num_pages, Hkv, page_size, head_dim]
+ *   v_pool       fp16  [num_pages, Hkv, page_size, head_dim]
+ *   block_table  int32 [B, max_pages_per_row]
+ *   seq_lens     int32 [B]
+ *   tasks        int32 [num_tasks][4] and split_offsets int32 [B+1], as
+ *                written by pkv_plan for the same seq_lens, Hkv and
+ *                page_size
+ *   out          fp16  [B, Hq, head_dim]
+ *   lse          fp32  [B, Hq] natural-log log-sum-exp, or NULL
+ *   workspace    >= pkv_workspace_size(num_partial_slots, Hq, head_dim)
+ *                bytes, 256-byte aligned, initialised once by
+ *                pkv_workspace_init.  Calls that share a workspace must be
+ *                ordered on one stream.  Concurrent calls need separate
+ *                workspaces.
+ * scale is the softmax scale (1/sqrt(head_dim) for standard attention).
+ * q, k_pool, v_pool and out must be 16-byte aligned.
+ *
+ * Validation: scalar arguments and the alignment are checked on the host.
+ * Device data is checked by the kernels.  A bad task record, block-table
+ * entry, row length or slot is skipped and flagged in the device error word
+ * (pkv_workspace_error_flags).  It is never dereferenced.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_BUFFER_TOO_SMALL
+ * (workspace), PKV_ERR_HIP (launch failure).
+ */
+int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
+               const int32_t* block_table, int32_t max_pages_per_row,
+               const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
+               const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
+               int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, float scale,
+               void* out, float* lse, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * pkv_decode_splits -- the first of pkv_decode's two launches: the persistent
+ * decode kernel alone.  It takes the same arguments and has the same rules.
+ * Rows with one split get their final out (and lse).  Rows with several
+ * splits get partial states in the workspace, which pkv_merge then combines.
+ * Source: as for pkv_decode.  The split state items are "Sequentie
+ * Splitting" and "Row-Local Bounds".
+ */
+int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
+                      const int32_t* block_table, int32_t max_pages_per_row,
+                      const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
+                      const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
+                      int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                      float scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_merge -- the second launch: the exact log-sum-exp merge (gist.science
+ * explainer, Methodologie, "Sequentie Splitting": a separate merge kernel
+ * combines the split states exactly).  For every row b with S_b =
+ * split_offsets[b+1] - split_offsets[b] != 1 and every query head h:
+ *   M = max_s m_s,  w_s = 2^(m_s - M),
+ *   out[b,h] = sum_s w_s o_s / sum_s w_s l_s   (fp16),
+ *   lse[b,h] = (M + log2 sum_s w_s l_s) * ln 2.
+ * Here (m_s, l_s, o_s) are the base-2 partial states that pkv_decode_splits
+ * left in the workspace.  S_b = 0 (an empty row) writes out = 0 and lse =
+ * -inf.  Rows with S_b = 1 are not touched.
+ * Pointers are device pointers, laid out as for pkv_decode.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_dim),
+ * PKV_ERR_BUFFER_TOO_SMALL, PKV_ERR_HIP.
+ */
+int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B, int32_t Hq,
+              int32_t head_dim, void* out, float* lse, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,374 @@
+"""Python binding of libpkv.so: paged GQA decode attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the decode path runs in the
+library: the host planner and policy (C++) and the HIP kernels.  PyTorch
+supplies device memory and streams.  The functions mirror the C ABI of
+``include/pkv.h`` under the same names.
+
+If ``libpkv.so`` has not been built (``python -m paged_gqa_decode_pkv_amd.build``),
+the first call raises ``ImportError``.  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_BUFFER_TOO_SMALL = 3
+PKV_ERR_BAD_INDEX = 4
+PKV_ERR_HIP = 5
+
+PKV_MODE_SPLIT = 0
+PKV_MODE_WORKQUEUE = 1
+
+PKV_DEVERR_TASK = 1
+PKV_DEVERR_PAGE = 2
+PKV_DEVERR_ROW = 4
+PKV_DEVERR_SLOT = 8
+
+PAGE_SIZE = 16
+
+# Every symbol include/pkv.h declares.
+ABI_SYMBOLS = (
+    "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_policy_defaults",
+    "pkv_policy", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
+    "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_splits", "pkv_merge",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {pkv_status_string(status)} (status {status})"
+        if status == PKV_ERR_HIP:
+            msg += f", hipError {pkv_last_hip_error()}"
+        super().__init__(msg)
+
+
+class pkv_policy_params(ctypes.Structure):
+    _fields_ = [("tasks_per_cu", ctypes.c_float), ("chunk_min", ctypes.c_int32),
+                ("chunk_max", ctypes.c_int32), ("split_max", ctypes.c_int32),
+                ("uniform_ratio", ctypes.c_float)]
+
+
+_lib = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_gqa_decode_pkv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "pkv_abi_version": ([], ctypes.c_int),
+        "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "pkv_last_hip_error": ([], ctypes.c_int),
+        "pkv_policy_defaults": ([ctypes.POINTER(pkv_policy_params)], ctypes.c_int),
+        "pkv_policy": ([_vp, i32, i32, i32, i32, ctypes.POINTER(pkv_policy_params), _i32p, _i32p],
+                       ctypes.c_int),
+        "pkv_plan": ([_vp, i32, i32, i32, i32, _vp, i64, i32, i32, _vp, i64, _vp, _i64p, _i64p],
+                     ctypes.c_int),
+        "pkv_workspace_size": ([i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "pkv_workspace_init": ([_vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "pkv_workspace_error_flags": ([_vp, ctypes.POINTER(ctypes.c_uint32), _vp], ctypes.c_int),
+        "pkv_decode": ([_vp, _vp, _vp, i64, _vp, i32, _vp, _vp, i64, _vp, i64, i32, i32, i32, i32,
+                        i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "pkv_merge": ([_vp, i64, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    }
+    sig["pkv_decode_splits"] = sig["pkv_decode"]
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+def _host_i32(x) -> np.ndarray:
+    if hasattr(x, "cpu"):
+        x = x.cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------- host calls
+
+def pkv_abi_version() -> int:
+    return _load().pkv_abi_version()
+
+
+def pkv_status_string(status: int) -> str:
+    return _load().pkv_status_string(status).decode()
+
+
+def pkv_last_hip_error() -> int:
+    return _load().pkv_last_hip_error()
+
+
+def pkv_policy_defaults() -> pkv_policy_params:
+    p = pkv_policy_params()
+    _check(_load().pkv_policy_defaults(ctypes.byref(p)), "pkv_policy_defaults")
+    return p
+
+
+def pkv_policy(seq_lens, Hkv: int, num_cus: int, params: Optional[pkv_policy_params] = None,
+               page_size: int = PAGE_SIZE) -> Tuple[int, int]:
+    """(mode, param) for this batch; see pkv_policy in include/pkv.h."""
+    sl = _host_i32(seq_lens)
+    mode, param = ctypes.c_int32(), ctypes.c_int32()
+    pp = ctypes.byref(params) if params is not None else None
+    _check(_load().pkv_policy(_ptr(sl), sl.size, Hkv, page_size, num_cus, pp, ctypes.byref(mode),
+                              ctypes.byref(param)), "pkv_policy")
+    return mode.value, param.value
+
+
+def pkv_plan(seq_lens, Hkv: int, max_pages_per_row: int, mode: int, param: int,
+             block_table=None, num_pages: int = 0, page_size: int = PAGE_SIZE,
+             tasks_out: Optional[np.ndarray] = None, offsets_out: Optional[np.ndarray] = None):
+    """Compact task list.  Returns (tasks int32 [T,4], split_offsets int32 [B+1],
+    num_partial_slots).  ``tasks_out`` / ``offsets_out`` (e.g. pinned host
+    memory viewed as numpy) are filled in place when given and large enough."""
+    lib = _load()
+    sl = _host_i32(seq_lens)
+    B = sl.size
+    bt = _host_i32(block_table) if block_table is not None else None
+    if bt is not None and bt.shape != (B, max_pages_per_row):
+        raise ValueError("block_table shape must be [B, max_pages_per_row]")
+    nt, ns = ctypes.c_int64(), ctypes.c_int64()
+    args = (_ptr(sl), B, Hkv, page_size, max_pages_per_row, _ptr(bt) if bt is not None else None,
+            num_pages)
+    _check(lib.pkv_plan(*args, mode, param, None, 0, None, ctypes.byref(nt), ctypes.byref(ns)),
+           "pkv_plan")
+    T = nt.value
+    if tasks_out is not None and tasks_out.size >= 4 * T and tasks_out.dtype == np.int32:
+        tasks = tasks_out.reshape(-1)[:4 * T].reshape(T, 4)
+    else:
+        tasks = np.empty((T, 4), dtype=np.int32)
+    if offsets_out is not None and offsets_out.size >= B + 1 and offsets_out.dtype == np.int32:
+        offs = offsets_out.reshape(-1)[:B + 1]
+    else:
+        offs = np.empty(B + 1, dtype=np.int32)
+    _check(lib.pkv_plan(*args, mode, param, _ptr(tasks), T, _ptr(offs), ctypes.byref(nt),
+                        ctypes.byref(ns)), "pkv_plan")
+    return tasks, offs, ns.value
+
+
+def pkv_workspace_size(num_partial_slots: int, Hq: int, head_dim: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_load().pkv_workspace_size(num_partial_slots, Hq, head_dim, ctypes.byref(n)),
+           "pkv_workspace_size")
+    return n.value
+
+
+# --------------------------------------------------------------------------- device calls
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pkv_workspace_init(workspace, stream=None):
+    import torch
+    _dev(workspace, torch.uint8, "workspace")
+    _check(_load().pkv_workspace_init(ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                      _stream_ptr(stream)), "pkv_workspace_init")
+
+
+def pkv_workspace_error_flags(workspace, stream=None) -> int:
+    flags = ctypes.c_uint32()
+    _check(_load().pkv_workspace_error_flags(ctypes.c_void_p(workspace.data_ptr()),
+                                             ctypes.byref(flags), _stream_ptr(stream)),
+           "pkv_workspace_error_flags")
+    return flags.value
+
+
+def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+                 num_partial_slots, scale, out, workspace, lse, stream):
+    """Checked ctypes argument tuple shared by pkv_decode and pkv_decode_splits.
+
+    q [B,Hq,d] fp16, k_pool / v_pool [pages,Hkv,16,d] fp16, block_table
+    [B,max_pages] int32, seq_lens [B] int32, tasks [T,4] int32, split_offsets
+    [B+1] int32, out [B,Hq,d] fp16, lse [B,Hq] fp32 or None, workspace uint8.
+    """
+    import torch
+    f16, i32 = torch.float16, torch.int32
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_pool.shape
+    if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("shape mismatch between q, k_pool, v_pool and out")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if split_offsets.shape != (B + 1,) or tasks.dim() != 2 or tasks.shape[1] != 4:
+        raise ValueError("tasks must be [T, 4] and split_offsets [B+1]")
+    if lse is not None and tuple(lse.shape) != (B, Hq):
+        raise ValueError("lse must be [B, Hq]")
+    args = (
+        _dev(q, f16, "q"), _dev(k_pool, f16, "k_pool"), _dev(v_pool, f16, "v_pool"), num_pages,
+        _dev(block_table, i32, "block_table"), block_table.shape[1],
+        _dev(seq_lens, i32, "seq_lens"), _dev(tasks, i32, "tasks"), tasks.shape[0],
+        _dev(split_offsets, i32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D, P,
+        float(scale), _dev(out, f16, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None,
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream),
+    )
+    return args
+
+
+def pkv_decode(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+               num_partial_slots: int, scale: float, out, workspace, lse=None, stream=None):
+    """Enqueue decode + merge on ``stream``; see pkv_decode in include/pkv.h."""
+    args = _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+                        num_partial_slots, scale, out, workspace, lse, stream)
+    _check(_load().pkv_decode(*args), "pkv_decode")
+
+
+def pkv_decode_splits(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+                      num_partial_slots: int, scale: float, out, workspace, lse=None, stream=None):
+    """Enqueue the decode kernel only; see pkv_decode_splits in include/pkv.h."""
+    args = _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+                        num_partial_slots, scale, out, workspace, lse, stream)
+    _check(_load().pkv_decode_splits(*args), "pkv_decode_splits")
+
+
+def pkv_merge(split_offsets, num_partial_slots: int, out, workspace, lse=None, stream=None):
+    """Enqueue the merge kernel only; see pkv_merge in include/pkv.h."""
+    import torch
+    B, Hq, D = out.shape
+    if split_offsets.shape != (B + 1,):
+        raise ValueError("split_offsets must be [B+1]")
+    if lse is not None and tuple(lse.shape) != (B, Hq):
+        raise ValueError("lse must be [B, Hq]")
+    _check(_load().pkv_merge(
+        _dev(split_offsets, torch.int32, "split_offsets"), num_partial_slots, B, Hq, D,
+        _dev(out, torch.float16, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None,
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
+        "pkv_merge")
+
+
+# --------------------------------------------------------------------------- convenience
+
+class PagedDecoder:
+    """One decode step = policy -> plan (host C++) -> H2D copy of the task list
+    -> decode + merge kernels, all enqueued on the current stream.
+
+    Owns pinned host staging for the plan, device copies of it, and the
+    workspace.  These grow on demand.  The pinned staging is reused only after
+    the copy that read it has completed (an event per ring slot), so steps can
+    be enqueued back to back without host synchronisation.
+    """
+
+    def __init__(self, Hq: int, Hkv: int, head_dim: int, max_batch: int, max_pages_per_row: int,
+                 device=None, num_cus: Optional[int] = None, ring: int = 4,
+                 policy_params: Optional[pkv_policy_params] = None):
+        import torch
+        self.Hq, self.Hkv, self.D = Hq, Hkv, head_dim
+        self.max_pages = max_pages_per_row
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+        self.num_cus = num_cus
+        self.params = policy_params
+        self._ring = []
+        for _ in range(ring):
+            self._ring.append(dict(tasks_h=None, offs_h=torch.empty(max_batch + 1, dtype=torch.int32,
+                                                                   pin_memory=True),
+                                   event=None))
+        self._slot = 0
+        self.tasks_d = torch.empty((0, 4), dtype=torch.int32, device=self.device)
+        self.offs_d = torch.empty(max_batch + 1, dtype=torch.int32, device=self.device)
+        self.workspace = torch.zeros(256, dtype=torch.uint8, device=self.device)
+        pkv_workspace_init(self.workspace)
+        self.last = None
+
+    def _ensure_ws(self, slots):
+        import torch
+        need = pkv_workspace_size(slots, self.Hq, self.D)
+        if self.workspace.numel() < need:
+            torch.cuda.current_stream().synchronize()
+            self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            pkv_workspace_init(self.workspace)
+
+    def plan(self, seq_lens_h: np.ndarray, mode: Optional[int] = None, param: Optional[int] = None,
+             block_table_h: Optional[np.ndarray] = None, num_pages: int = 0):
+        """Host planning + async upload.  Returns (mode, param, T, slots)."""
+        import torch
+        if len(seq_lens_h) + 1 > self._ring[0]["offs_h"].numel():
+            raise ValueError("batch larger than max_batch")
+        if mode is None:
+            mode, param = pkv_policy(seq_lens_h, self.Hkv, self.num_cus, self.params)
+        slot = self._ring[self._slot]
+        self._slot = (self._slot + 1) % len(self._ring)
+        if slot["event"] is not None:
+            slot["event"].synchronize()
+        tasks_np, offs_np, nslots = pkv_plan(
+            seq_lens_h, self.Hkv, self.max_pages, mode, param, block_table_h, num_pages,
+            tasks_out=slot["tasks_h"].numpy() if slot["tasks_h"] is not None else None,
+            offsets_out=slot["offs_h"].numpy())
+        T = tasks_np.shape[0]
+        if slot["tasks_h"] is None or slot["tasks_h"].shape[0] < T:
+            slot["tasks_h"] = torch.empty((max(T, 1), 4), dtype=torch.int32, pin_memory=True)
+            slot["tasks_h"][:T].numpy()[:] = tasks_np
+        if self.tasks_d.shape[0] < T:
+            self.tasks_d = torch.empty((max(T, 1), 4), dtype=torch.int32, device=self.device)
+        B = offs_np.size - 1
+        self._ensure_ws(nslots)
+        self.tasks_d[:T].copy_(slot["tasks_h"][:T], non_blocking=True)
+        self.offs_d[:B + 1].copy_(slot["offs_h"][:B + 1], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        slot["event"] = ev
+        self.last = (mode, param, T, nslots, B)
+        return mode, param, T, nslots
+
+    def decode(self, q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None, lse=None):
+        import torch
+        mode, param, T, nslots, B = self.last
+        if out is None:
+            out = torch.empty_like(q)
+        pkv_decode(q, k_pool, v_pool, block_table, seq_lens, self.tasks_d[:T], self.offs_d[:B + 1],
+                   nslots, scale, out, self.workspace, lse=lse)
+        return out
+
+    def step(self, q, k_pool, v_pool, block_table, seq_lens, seq_lens_h, scale: float, out=None,
+             lse=None, mode=None, param=None):
+        self.plan(seq_lens_h, mode, param)
+        return self.decode(q, k_pool, v_pool, block_table, seq_lens, scale, out=out, lse=lse)
+
+    def error_flags(self) -> int:
+        return pkv_workspace_error_flags(self.workspace)

@@ -1,0 +1,75 @@
+"""Build libpkv.so in-tree with hipcc for gfx950.
+
+    python -m paged_gqa_decode_pkv_amd.build [--asm]
+
+Host-only C++ (planner, policy) and the HIP kernels link into one shared
+library next to this file.  ``--asm`` also writes the gfx950 assembly of the
+kernels under ``_build/`` for inspection.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libpkv.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are switched off for every device compile.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed: {' '.join(cmd[:3])} ...")
+    if verbose and r.stderr.strip():
+        sys.stderr.write(r.stderr)
+
+
+def build(verbose: bool = False, asm: bool = False) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    common = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall"]
+    objs = []
+    plan_o = os.path.join(BUILD_DIR, "plan.o")
+    _run([hipcc, "-x", "c++", *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o],
+         verbose)
+    objs.append(plan_o)
+    dec_o = os.path.join(BUILD_DIR, "decode.o")
+    _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS, "-c",
+          os.path.join(CSRC, "decode.hip"), "-o", dec_o], verbose)
+    objs.append(dec_o)
+    if asm:
+        _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS,
+              "--cuda-device-only", "-S", os.path.join(CSRC, "decode.hip"),
+              "-o", os.path.join(BUILD_DIR, "decode-gfx950.s")], verbose)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", action="store_true")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args()
+    print(build(verbose=args.verbose, asm=args.asm))

@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the float64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from workloads import compact_rows
+
+# Tolerance on fp16 outputs: max abs error <= 2e-3 and
+# max abs error / max |reference| <= 1e-2, per case.
+ATOL = 2e-3
+RTOL = 1e-2
+LSE_ATOL = 2e-3
+
+
+def log_case(*parts):
+    sys.stderr.write("[case] " + " ".join(str(p) for p in parts) + "\n")
+    sys.stderr.flush()
+
+
+def check_close(got, ref, atol=ATOL, rtol=RTOL, what="out"):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    assert err <= atol, f"{what}: max abs err {err:.3e} > {atol}"
+    if scale > 0:
+        assert err / scale <= rtol, f"{what}: rel err {err / scale:.3e} > {rtol}"
+    return err, (err / scale if scale > 0 else 0.0)
+
+
+def check_lse(got, ref, atol=LSE_ATOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    inf_r = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf_r), "lse: -inf pattern differs"
+    if (~inf_r).any():
+        err = float(np.max(np.abs(got[~inf_r] - ref[~inf_r])))
+        assert err <= atol, f"lse: max abs err {err:.3e}"
+
+
+def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1):
+    """Plan + decode through the C ABI.  Returns (out fp16 tensor, lse tensor|None, decoder)."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+
+    cfg = wl.cfg
+    if decoder is None:
+        decoder = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=max(len(wl.seq_lens_np), 1),
+                                   max_pages_per_row=wl.block_table_np.shape[1])
+    out = torch.full_like(wl.q, float("nan"))
+    lse_t = torch.full((wl.q.shape[0], cfg.Hq), float("nan"), dtype=torch.float32,
+                       device=wl.q.device) if lse else None
+    for _ in range(repeats):
+        decoder.plan(wl.seq_lens_np, mode, param, block_table_h=wl.block_table_np,
+                     num_pages=wl.k_pool.shape[0])
+        decoder.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, cfg.scale,
+                       out=out, lse=lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t, decoder
+
+
+def oracle_rows(wl, rows=None):
+    """Float64 oracle on the given rows (all rows by default), pages copied
+    from wherever the workload lives."""
+    if rows is None:
+        rows = range(len(wl.seq_lens_np))
+    q, k, v, bt, sl = compact_rows(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, rows)
+    return oracle.attend(q, k, v, bt, sl, wl.cfg.scale)

@@ -1,0 +1,176 @@
+"""C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host planner / policy match the oracle bit for bit.  No device calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_gqa_decode_pkv_amd as pkv
+from workloads import CONFIGS, CALIBRATION_SEED, HELD_OUT_SEEDS, make_lengths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    declared = _declared_symbols()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(pkv.ABI_SYMBOLS) == declared
+
+
+def test_version_and_status_strings():
+    assert pkv.pkv_abi_version() == 1
+    for code in range(6):
+        assert pkv.pkv_status_string(code)
+    assert pkv.pkv_status_string(99) == "unknown status"
+
+
+def test_constants_agree_with_oracle():
+    assert pkv.PKV_MODE_SPLIT == oracle.MODE_SPLIT
+    assert pkv.PKV_MODE_WORKQUEUE == oracle.MODE_WORKQUEUE
+
+
+# --------------------------------------------------------------------------- plan
+
+def _plan_both(lens, Hkv, maxp, mode, param):
+    tasks, offs, slots = pkv.pkv_plan(lens, Hkv, maxp, mode, param)
+    rt, ro = oracle.plan_tasks(lens, Hkv, 16, mode, param)
+    return tasks, offs, slots, rt, ro
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_plan_bit_exact_on_configs(name):
+    cfg = CONFIGS[name]
+    for seed in (CALIBRATION_SEED,) + HELD_OUT_SEEDS:
+        lens = make_lengths(cfg, seed)
+        for mode, params in ((pkv.PKV_MODE_SPLIT, (1, 4, 8, 16, 32, 64, 256)),
+                             (pkv.PKV_MODE_WORKQUEUE, (1, 4, 16, 64, 256))):
+            for p in params:
+                t, o, s, rt, ro = _plan_both(lens, cfg.Hkv, cfg.max_pages_per_row, mode, p)
+                assert np.array_equal(t, rt), (name, seed, mode, p)
+                assert np.array_equal(o, ro)
+                assert s == ro[-1]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_bit_exact_random(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 70))
+    lens = rng.integers(0, 3000, size=B)
+    lens[rng.random(B) < 0.2] = 0
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    maxp = int(-(-lens.max() // 16)) + int(rng.integers(0, 3))
+    for mode in (pkv.PKV_MODE_SPLIT, pkv.PKV_MODE_WORKQUEUE):
+        p = int(rng.integers(1, 300))
+        t, o, s, rt, ro = _plan_both(lens, Hkv, maxp, mode, p)
+        assert np.array_equal(t, rt) and np.array_equal(o, ro) and s == ro[-1]
+
+
+def test_plan_empty_and_zero_rows():
+    t, o, s = pkv.pkv_plan([0, 0, 0], 8, 4, pkv.PKV_MODE_SPLIT, 4)
+    assert t.shape == (0, 4) and o.tolist() == [0, 0, 0, 0] and s == 0
+    t, o, s = pkv.pkv_plan([], 8, 4, pkv.PKV_MODE_SPLIT, 4)
+    assert t.shape == (0, 4) and o.tolist() == [0]
+
+
+def test_plan_errors():
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([100], 1, 2, pkv.PKV_MODE_SPLIT, 1)          # 7 pages > 2
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([-1], 1, 2, pkv.PKV_MODE_SPLIT, 1)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([16], 1, 2, 5, 1)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([16], 1, 2, pkv.PKV_MODE_SPLIT, 0)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([16], 1, 2, pkv.PKV_MODE_SPLIT, 1, page_size=32)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    bt = np.array([[3, -1], [0, 9]], dtype=np.int32)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan([16, 32], 1, 2, pkv.PKV_MODE_SPLIT, 1, block_table=bt, num_pages=8)
+    assert e.value.status == pkv.PKV_ERR_BAD_INDEX          # 9 >= 8
+    # entries past n_b are never checked
+    t, o, s = pkv.pkv_plan([16, 17], 1, 2, pkv.PKV_MODE_SPLIT, 1,
+                           block_table=np.array([[3, -1], [0, 7]], np.int32), num_pages=8)
+    assert t.shape[0] == 2
+
+
+def test_plan_buffer_too_small():
+    lib = pkv._load()
+    lens = np.array([64, 64], dtype=np.int32)
+    tasks = np.zeros((1, 4), dtype=np.int32)
+    offs = np.zeros(3, dtype=np.int32)
+    nt, ns = ctypes.c_int64(), ctypes.c_int64()
+    st = lib.pkv_plan(lens.ctypes.data_as(ctypes.c_void_p), 2, 1, 16, 4, None, 0, 0, 2,
+                      tasks.ctypes.data_as(ctypes.c_void_p), 1,
+                      offs.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nt), ctypes.byref(ns))
+    assert st == pkv.PKV_ERR_BUFFER_TOO_SMALL and nt.value == 4 and ns.value == 4
+
+
+# --------------------------------------------------------------------------- policy
+
+def test_policy_matches_oracle_rule():
+    rng = np.random.default_rng(5)
+    cases = [[32768], [0], [], [100, 0], [16] * 8]
+    for name in CONFIGS:
+        for seed in (CALIBRATION_SEED,) + HELD_OUT_SEEDS:
+            cases.append(make_lengths(CONFIGS[name], seed).tolist())
+    for _ in range(50):
+        cases.append(rng.integers(0, 40000, size=int(rng.integers(1, 65))).tolist())
+    for lens in cases:
+        for cus in (1, 80, 256, 304):
+            for Hkv in (1, 8):
+                got = pkv.pkv_policy(lens, Hkv, cus)
+                want = oracle.policy(lens, Hkv, 16, cus)
+                assert got == tuple(int(x) for x in want), (lens[:4], cus, Hkv)
+
+
+def test_policy_params_and_errors():
+    d = pkv.pkv_policy_defaults()
+    assert d.chunk_min == 4 and d.chunk_max == 256 and d.split_max == 256
+    d.split_max = 8
+    assert pkv.pkv_policy([32768], 8, 256, params=d) == (pkv.PKV_MODE_SPLIT, 8)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_policy([-5], 8, 256)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_policy([5], 8, 0)
+
+
+# --------------------------------------------------------------------------- workspace, decode arg checks
+
+def test_workspace_size():
+    assert pkv.pkv_workspace_size(0, 32, 128) == 256
+    n = pkv.pkv_workspace_size(10, 32, 128)
+    assert n >= 256 + 10 * 32 * 130 * 4 and n % 256 == 0
+
+
+def test_decode_rejects_bad_scalars_before_touching_the_device():
+    lib = pkv._load()
+    common = dict(q=None, k=None, v=None)
+    def call(B=1, Hq=4, Hkv=1, D=64, P=16, scale=0.125):
+        return lib.pkv_decode(None, None, None, 0, None, 1, None, None, 0, None, 0, B, Hq, Hkv, D,
+                              P, scale, None, None, None, 0, None)
+    assert call(D=96) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(P=32) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == pkv.PKV_ERR_UNSUPPORTED      # Hq % Hkv
+    assert call(Hq=48, Hkv=3) == pkv.PKV_ERR_UNSUPPORTED     # G = 16
+    assert call(B=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == pkv.PKV_ERR_INVALID_ARG
+    assert call(B=0) == pkv.PKV_OK                           # nothing to do
+    assert call(B=1) == pkv.PKV_ERR_INVALID_ARG              # null pointers
+    del common

@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every case draws seeded synthetic inputs with the shapes of the five
+workloads (or small ragged edge cases), runs plan + decode + merge on the GPU,
+and compares out and lse element by element with ``oracle.attend``:
+max abs error <= 2e-3 and max abs error / max |ref| <= 1e-2 on fp16 outputs.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import check_close, check_lse, log_case, oracle_rows, run_hip
+from workloads import CALIBRATION_SEED, CONFIGS, HELD_OUT_SEEDS, Config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SEED = HELD_OUT_SEEDS[0]
+
+
+def _parity(wl, mode=None, param=None, rows=None, decoder=None):
+    log_case(wl.cfg.name, "seed", wl.seed, "mode", mode, "param", param,
+             "lens", wl.seq_lens_np.tolist()[:8])
+    out, lse, dec = run_hip(wl, mode, param, decoder=decoder)
+    ref_out, ref_lse = oracle_rows(wl, rows)
+    sel = slice(None) if rows is None else list(rows)
+    got = out.float().cpu().numpy()[sel]
+    check_close(got, ref_out)
+    check_lse(lse.cpu().numpy()[sel], ref_lse)
+    assert dec.error_flags() == 0
+    return got, dec
+
+
+# --------------------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("S", [1, 4])
+@pytest.mark.parametrize("seed", [CALIBRATION_SEED, SEED])
+def test_tiny(S, seed):
+    wl = make_workload("tiny", seed, device="cuda")
+    _parity(wl, 0, S)
+
+
+@pytest.mark.parametrize("S", [8, 16, 32, 64, None])
+def test_b1_split_counts(S):
+    wl = make_workload("b1", SEED, device="cuda")
+    _parity(wl, None if S is None else 0, S)
+
+
+@pytest.mark.parametrize("name", ["b8_bimodal", "b8_zipf", "b8_uniform"])
+def test_b8_policy(name):
+    wl = make_workload(name, SEED, device="cuda")
+    _parity(wl)
+
+
+@pytest.mark.parametrize("mode,param", [(0, 4), (0, 64), (1, 1), (1, 16), (1, 256)])
+def test_b8_bimodal_modes(mode, param):
+    wl = make_workload("b8_bimodal", CALIBRATION_SEED, device="cuda")
+    _parity(wl, mode, param)
+
+
+@pytest.mark.parametrize("seed", HELD_OUT_SEEDS[1:])
+def test_b8_bimodal_held_out_seeds(seed):
+    wl = make_workload("b8_bimodal", seed, device="cuda")
+    _parity(wl)
+
+
+@pytest.fixture(scope="module")
+def b64():
+    import torch
+    wl = make_workload("b64", SEED, device="cuda")
+    yield wl
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", [None, 0, 1])
+def test_b64_sampled_rows(b64, mode):
+    """Full-size B=64 batch (34.4 GB pool), oracle on sampled rows."""
+    rows = [0, 17, 42, 63]
+    param = {None: None, 0: 16, 1: 64}[mode]
+    _parity(b64, mode, param, rows=rows)
+
+
+# --------------------------------------------------------------------------- edge cases
+
+def _small_cfg(G=4, D=128, Hkv=2, maxp=8, pool=64):
+    return Config("small", B=0, Hq=G * Hkv, Hkv=Hkv, D=D, max_pages_per_row=maxp,
+                  pool_pages=pool, lengths=lambda rng: np.zeros(0))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_gqa_ratios_and_head_dims(G, D):
+    cfg = _small_cfg(G=G, D=D)
+    lens = [1, 15, 16, 17, 33, 0, 127, 128]
+    for mode, param in [(0, 1), (0, 3), (1, 1), (1, 2)]:
+        wl = make_workload(cfg, 7 + G + D, device="cuda", seq_lens=lens)
+        _parity(wl, mode, param)
+
+
+def test_all_rows_empty():
+    cfg = _small_cfg()
+    wl = make_workload(cfg, 3, device="cuda", seq_lens=[0, 0, 0])
+    out, lse, dec = run_hip(wl, 0, 4)
+    assert np.all(out.float().cpu().numpy() == 0)
+    assert np.all(np.isneginf(lse.cpu().numpy()))
+    assert dec.error_flags() == 0
+
+
+def test_full_rows_at_max_pages():
+    cfg = _small_cfg(maxp=8)
+    wl = make_workload(cfg, 4, device="cuda", seq_lens=[128, 128, 5])
+    _parity(wl, 1, 3)
+    _parity(wl, 0, 8)
+
+
+def test_poison_does_not_leak():
+    """NaN in unreferenced pages and tail slots gives the same bits as finite garbage."""
+    wl_nan = make_workload("b8_zipf", SEED, device="cuda", fill="nan")
+    wl_rnd = make_workload("b8_zipf", SEED, device="cuda", fill="random")
+    a, _, _ = run_hip(wl_nan, 1, 8)
+    b, _, _ = run_hip(wl_rnd, 1, 8)
+    assert np.all(np.isfinite(a.float().cpu().numpy()))
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
+def test_page_relabelling_bit_identical():
+    import torch
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    a, la, _ = run_hip(wl, 1, 16)
+    perm = torch.randperm(wl.k_pool.shape[0], generator=torch.Generator().manual_seed(1)).cuda()
+    k2 = torch.empty_like(wl.k_pool)
+    v2 = torch.empty_like(wl.v_pool)
+    k2[perm] = wl.k_pool
+    v2[perm] = wl.v_pool
+    bt = wl.block_table.clone()
+    mask = bt >= 0
+    bt[mask] = perm.to(torch.int32)[bt[mask].long()]
+    wl.k_pool, wl.v_pool, wl.block_table = k2, v2, bt
+    wl.block_table_np = bt.cpu().numpy()
+    b, lb, _ = run_hip(wl, 1, 16)
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+    assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy())
+
+
+def test_repeated_launches_deterministic_and_counter_reset():
+    """Many back-to-back steps on one workspace: the self-resetting task counter
+    must hand out every task each time, and results are bit-identical."""
+    wl = make_workload("b8_uniform", SEED, device="cuda")
+    a, la, dec = run_hip(wl, 1, 2)
+    b, lb, _ = run_hip(wl, 1, 2, decoder=dec, repeats=5)
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+    assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy())
+    ref_out, _ = oracle_rows(wl)
+    check_close(b.float().cpu().numpy(), ref_out)
+
+
+def test_split_counts_agree():
+    wl = make_workload("b1", CALIBRATION_SEED, device="cuda")
+    lses = []
+    for S in (1, 2, 8, 64, 256):
+        _, lse, _ = run_hip(wl, 0, S)
+        lses.append(lse.cpu().numpy())
+    for x in lses[1:]:
+        assert np.max(np.abs(x - lses[0])) < 1e-4
+
+
+def test_task_list_readback_bit_exact():
+    import oracle
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    _, _, dec = run_hip(wl, 1, 16)
+    mode, param, T, nslots, B = dec.last
+    rt, ro = oracle.plan_tasks(wl.seq_lens_np, wl.cfg.Hkv, 16, mode, param)
+    assert np.array_equal(dec.tasks_d[:T].cpu().numpy(), rt)
+    assert np.array_equal(dec.offs_d[:B + 1].cpu().numpy(), ro)

@@ -21,7 +21,9 @@ Draw order for a (config, seed) pair:
                        CUDA: ``torch.Generator('cuda').manual_seed(seed)``,
                        q then K then V, ``randn(float32)`` rounded to fp16.
 The CPU and CUDA value streams differ for the same seed; lengths and the block
-table are identical on both.
+table are identical on both.  Finite garbage for unreferenced pages
+(``fill="random"``) comes from a separate generator, so the referenced values
+do not depend on the fill.
 
 Poison: pool pages no row references and the tail slots t >= N_b of each
 row's last page are filled with NaN (``fill="nan"``), and unused block-table
@@ -188,6 +190,7 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
     pshape = (pool, cfg.Hkv, P, cfg.D)
 
     if device == "cpu":
+        fill_rng = np.random.default_rng([seed, 1])
         q = rng.standard_normal((len(lens), cfg.Hq, cfg.D), dtype=np.float32).astype(np.float16)
         pools = []
         for _ in range(2):
@@ -198,7 +201,7 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
             elif fill == "zero":
                 arr = np.zeros(pshape, dtype=np.float16)
             elif fill == "random":
-                arr = rng.standard_normal(pshape, dtype=np.float32).astype(np.float16)
+                arr = fill_rng.standard_normal(pshape, dtype=np.float32).astype(np.float16)
             else:
                 raise ValueError(fill)
             arr[used] = vals
@@ -214,6 +217,8 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
         dev = torch.device(device)
         gen = torch.Generator(device=dev)
         gen.manual_seed(seed)
+        fill_gen = torch.Generator(device=dev)
+        fill_gen.manual_seed(seed + 7919)
         q_t = torch.randn((len(lens), cfg.Hq, cfg.D), generator=gen, device=dev,
                           dtype=torch.float32).half()
         used_t = torch.from_numpy(used.astype(np.int64)).to(dev)
@@ -225,7 +230,7 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
                 arr = torch.zeros(pshape, dtype=torch.float16, device=dev)
             elif fill == "random":
                 arr = torch.empty(pshape, dtype=torch.float16, device=dev)
-                _randn_fill(arr, gen)
+                _randn_fill(arr, fill_gen)
             else:
                 raise ValueError(fill)
             # referenced pages, generated in chunks to bound the fp32 temporary
