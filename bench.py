@@ -135,41 +135,36 @@ def main():
         layers.append((wl.q.clone(), wl.k_pool.clone(), wl.v_pool.clone()))
     outs = [torch.empty_like(wl.q) for _ in range(L)]
     lses = [torch.empty((B, cfg.Hq), dtype=torch.float32, device=dev) for _ in range(L)]
-    dec = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=B,
-                           max_pages_per_row=cfg.max_pages_per_row)
     num_pages = wl.k_pool.shape[0]
     sl_h = wl.seq_lens_np
     bt_h = wl.block_table_np
+    # block table checked once on the host, as a serving loop does on admission
+    pkv.pkv_plan(sl_h, cfg.Hkv, cfg.max_pages_per_row, 0, 1, block_table=bt_h, num_pages=num_pages)
+    decs = []
+    for li, (q, k, v) in enumerate(layers):
+        d = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=B,
+                             max_pages_per_row=cfg.max_pages_per_row)
+        d.set_inputs(q, k, v, wl.block_table, wl.seq_lens, sl_h, cfg.scale, outs[li], lses[li])
+        decs.append(d)
+    stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
-        q, k, v = layers[i % L]
-        out, lse = outs[i % L], lses[i % L]
-        mode, param, T, nslots = dec.plan(sl_h, args.mode, args.param)
-        tasks = dec.tasks_d[:T]
-        offs = dec.offs_d[:B + 1]
-        if ev is not None:
-            ev[0].record()
-        pkv.pkv_decode_splits(q, k, v, wl.block_table, wl.seq_lens, tasks, offs, nslots,
-                              cfg.scale, out, dec.workspace, lse=lse)
-        if ev is not None:
-            ev[1].record()
-        pkv.pkv_merge(offs, nslots, out, dec.workspace, lse=lse)
-        if ev is not None:
-            ev[2].record()
-
-    # validate the block table once (host), as a serving system would on admission
-    pkv.pkv_plan(sl_h, cfg.Hkv, cfg.max_pages_per_row, 0, 1, block_table=bt_h, num_pages=num_pages)
+        decs[i % L].run(args.mode, args.param, stream=stream, events=ev)
 
     print(f"[bench] warmup {args.warmup} steps, {L} layer copies", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, L)):
         step(i)
     torch.cuda.synchronize()
-    if dec.error_flags() != 0:
+    if any(d.error_flags() != 0 for d in decs):
         print("device error flags set", file=sys.stderr)
         sys.exit(1)
 
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+    for e0, e1 in events:     # creates the underlying HIP events
+        e0.record()
+        e1.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -177,15 +172,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
+    dec = decs[0]
 
     wall = t1 - t0
-    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    pair_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
+    dec_ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
     mode, param, T, nslots = dec.last[:4]
     avg_dec_s = float(dec_ms.mean()) * 1e-3
     achieved = kv_bytes / avg_dec_s / 1e9
     ms_per_step = wall / K * 1e3
-    splits = np.diff(dec.offs_d[:B + 1].cpu().numpy())
+    splits = np.diff(dec.plan_arrays()[1])
     extras = {
         "q_out_bytes": B * cfg.Hq * cfg.D * 4,
         "block_table_bytes": int(((sl_h.astype(np.int64) + 15) // 16).sum()) * 4,
@@ -216,7 +211,6 @@ def main():
             "decode_mean": round(float(dec_ms.mean()) * 1e3, 2),
             "decode_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
             "decode_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
-            "decode_plus_merge_mean": round(float(pair_ms.mean()) * 1e3, 2),
         },
         "roofline": {
             "bound": "hbm",

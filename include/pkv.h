@@ -46,6 +46,15 @@ extern "C" {
 
 #define PKV_ABI_VERSION 1
 
+/* Fixed-size head of every workspace: control words (task counter, exit
+ * counter, error word) and the per-(row, KV head) arrival counters of the
+ * fused merge.  pkv_workspace_init zeroes it.  Every launch leaves it zeroed
+ * again, except the sticky error word. */
+#define PKV_WORKSPACE_HEADER_BYTES 65536
+/* Largest B * Hkv the single-launch (fused-merge) decode serves.  Larger
+ * batches fall back to the two-launch form. */
+#define PKV_MAX_FUSED_GROUPS ((PKV_WORKSPACE_HEADER_BYTES - 256) / 4)
+
 /* Status codes. */
 enum pkv_status {
   PKV_OK = 0,
@@ -81,6 +90,10 @@ typedef struct pkv_policy_params {
   int32_t chunk_max;
   int32_t split_max;    /* split-mode cap on S */
   float uniform_ratio;  /* lengths within this max/min ratio count as uniform */
+  int32_t fuse_max_splits; /* step runner: the fused single launch when no row
+                              has more splits than this, else the two-launch
+                              form (the fused merge runs at the tail of a split
+                              group, so long groups favour the separate merge) */
 } pkv_policy_params;
 
 /* ABI version (PKV_ABI_VERSION of the built library). */
@@ -169,21 +182,22 @@ int pkv_plan(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
 
 /*
  * pkv_workspace_size -- device workspace bytes that pkv_decode needs.
- * Layout: a 256-byte control block (task counter, exit counter, error word),
- * then the fp32 partial outputs [num_partial_slots][Hq][head_dim], then the
- * fp32 (max, sum) pairs [num_partial_slots][Hq][2].  The total is rounded up
- * to 256 bytes.
+ * Layout: the PKV_WORKSPACE_HEADER_BYTES header (a 256-byte control block:
+ * task counter, exit counter, error word; then uint32 arrival counters of
+ * the fused merge, one per (row, KV head)), then the fp32 partial outputs
+ * [num_partial_slots][Hq][head_dim], then the fp32 (max, sum) pairs
+ * [num_partial_slots][Hq][2].  The total is rounded up to 256 bytes.
  * Errors: PKV_ERR_INVALID_ARG for NULL bytes or a negative size.
  */
 int pkv_workspace_size(int64_t num_partial_slots, int32_t Hq, int32_t head_dim,
                        size_t* bytes);
 
 /*
- * pkv_workspace_init -- zero the workspace's control block on `stream`.
- * Call it once after allocating a workspace.  It also clears the device
- * error word.  pkv_decode leaves the counters at zero when it completes, so
- * one init serves any number of later decodes on that workspace.
- * Errors: PKV_ERR_INVALID_ARG (NULL or fewer than 256 bytes), PKV_ERR_HIP.
+ * pkv_workspace_init -- zero the workspace header on `stream`.  Call it
+ * once after allocating a workspace.  It also clears the device error word.
+ * Every decode leaves the counters at zero when it completes, so one init
+ * serves any number of later decodes on that workspace.
+ * Errors: PKV_ERR_INVALID_ARG (NULL or smaller than the header), PKV_ERR_HIP.
  */
 int pkv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
@@ -195,14 +209,21 @@ int pkv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stream);
 
 /*
- * pkv_decode -- run one decode step: the persistent decode kernel over the
- * task list, then the merge kernel.  This makes two launches on `stream`.
+ * pkv_decode -- run one decode step in ONE launch: the persistent decode
+ * kernel over the task list, with the split merge fused into it.
  *
  * Source: gist.science explainer, Methodologie, item "Sequentie Splitting".
- * Each split computes a partial online-softmax state and a separate merge
- * combines the states exactly.  Item "Compact Workqueue": one 1-D grid runs
- * the task list.  The fugumt.com abstract reports 2 launches per step for
- * this schedule.  A row with a single split writes its output directly.
+ * Each split computes a partial online-softmax state, and the states are
+ * combined exactly.  Item "Compact Workqueue": one 1-D grid runs the task
+ * list.  The pages run the combination as a separate merge kernel, 2
+ * launches per step (fugumt.com abstract).  That form is
+ * pkv_decode_splits followed by pkv_merge.  Here the workgroup that finishes
+ * the last split of a (row, KV head) merges that group instead.  It finds
+ * out through a device-scope arrival counter, after a release fence by every
+ * split.  The arithmetic is that of pkv_merge.  A row with a single split
+ * writes its output directly.  A row with N_b = 0 gets out = 0 and
+ * lse = -inf.  With B * Hkv > PKV_MAX_FUSED_GROUPS, or no task at all, the
+ * call falls back to the two-launch form.
  *
  * All pointers are device pointers.  Tensors are contiguous, row-major:
  *   q            fp16  [B, Hq, head_dim]
@@ -212,7 +233,8 @@ int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stre
  *   seq_lens     int32 [B]
  *   tasks        int32 [num_tasks][4] and split_offsets int32 [B+1], as
  *                written by pkv_plan for the same seq_lens, Hkv and
- *                page_size
+ *                page_size.  Device memory or device-mapped pinned host
+ *                memory (the runner uses the latter).
  *   out          fp16  [B, Hq, head_dim]
  *   lse          fp32  [B, Hq] natural-log log-sum-exp, or NULL
  *   workspace    >= pkv_workspace_size(num_partial_slots, Hq, head_dim)
@@ -265,13 +287,97 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
  * Here (m_s, l_s, o_s) are the base-2 partial states that pkv_decode_splits
  * left in the workspace.  S_b = 0 (an empty row) writes out = 0 and lse =
  * -inf.  Rows with S_b = 1 are not touched.
- * Pointers are device pointers, laid out as for pkv_decode.
- * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_dim),
+ * Pointers are device pointers, laid out as for pkv_decode.  One
+ * workgroup merges the G = Hq/Hkv heads of one (row, KV head).
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_dim or G),
  * PKV_ERR_BUFFER_TOO_SMALL, PKV_ERR_HIP.
  */
 int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B, int32_t Hq,
-              int32_t head_dim, void* out, float* lse, void* workspace, size_t workspace_bytes,
-              void* stream);
+              int32_t Hkv, int32_t head_dim, void* out, float* lse, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * Step runner -- the whole hot path of one decode step in one call:
+ * policy, host plan, a single async upload of the plan, then the decode
+ * kernel and the merge kernel on the caller's stream.
+ *
+ * Source: gist.science explainer, "2. Calibrated Adaptive Policy" and
+ * Methodologie ("Row-Local Bounds", "Compact Workqueue").  "Evaluatieprotocol"
+ * counts host planning in the synchronized wall time of a step.
+ *
+ * A runner owns host resources only: a ring of pinned plan buffers, each
+ * guarded by a HIP event recorded after the merge kernel, so it never
+ * rewrites a plan that enqueued kernels still read.  The kernels read the
+ * plan in place from pinned host memory (the host-to-device boundary of the
+ * step; 16 bytes per task).  Device memory belongs to the caller.  One
+ * runner serves one thread at a time.
+ */
+typedef struct pkv_runner pkv_runner;
+
+typedef struct pkv_step_args {
+  /* host input */
+  const int32_t* seq_lens_host;  /* int32 [B], the same lengths as seq_lens */
+  int32_t B;
+  int32_t mode;                  /* pkv_mode, or -1 to let pkv_policy choose */
+  int32_t param;                 /* S or c for an explicit mode */
+  int32_t two_launch;            /* 0: pkv_decode (one launch, merge fused);
+                                    1: pkv_decode_splits then pkv_merge;
+                                    -1: choose by the policy's fuse_max_splits */
+  /* device inputs, laid out as for pkv_decode */
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_pages_per_row;
+  const int32_t* seq_lens;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t head_dim;
+  int32_t page_size;
+  float scale;
+  /* device outputs and scratch */
+  void* out;                     /* fp16 [B, Hq, head_dim] */
+  float* lse;                    /* fp32 [B, Hq] or NULL */
+  void* workspace;               /* as for pkv_decode */
+  size_t workspace_bytes;
+  void* stream;                  /* hipStream_t */
+  void* event_before_decode;     /* optional hipEvent_t, recorded on `stream`
+                                    just before the decode kernel */
+  void* event_after_decode;      /* optional hipEvent_t, recorded just after it
+                                    (before the merge kernel in two-launch form) */
+  /* outputs */
+  int32_t chosen_mode;
+  int32_t chosen_param;
+  int32_t chosen_two_launch;     /* the launch form actually used */
+  int32_t max_splits;            /* max over rows of S_b */
+  int64_t num_tasks;
+  int64_t num_partial_slots;
+  size_t workspace_bytes_needed;
+} pkv_step_args;
+
+/* num_cus = 0 queries the current device.  params = NULL selects the
+ * defaults.  ring_depth is the number of pinned staging slots (1..1024).
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_HIP. */
+int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t ring_depth,
+                      pkv_runner** runner);
+
+/* Enqueue one step.  Fills the output fields of *args.  If the workspace is
+ * too small, nothing is enqueued, workspace_bytes_needed holds the size, and
+ * PKV_ERR_BUFFER_TOO_SMALL is returned.  The block table
+ * is not checked here: pkv_plan with a host copy of it does that.  Other
+ * errors are those of pkv_policy, pkv_plan and pkv_decode, or PKV_ERR_HIP. */
+int pkv_runner_step(pkv_runner* runner, pkv_step_args* args);
+
+/* Host view of the plan that the last step's kernels read (valid until that
+ * ring slot is reused): split_offsets [B+1], tasks [num_tasks][4].  For
+ * tests and debugging. */
+int pkv_runner_last_plan(const pkv_runner* runner, const int32_t** split_offsets,
+                         const int32_t** tasks, int64_t* num_tasks, int32_t* B);
+
+/* Wait for the kernels that read the runner's plans, then free its
+ * resources.  NULL is a no-op. */
+int pkv_runner_destroy(pkv_runner* runner);
 
 #ifdef __cplusplus
 }

@@ -204,7 +204,7 @@ def split_merge(q, k_pool, v_pool, block_table, seq_lens, scale, tasks, split_of
 # policy
 # ---------------------------------------------------------------------------
 
-def policy(seq_lens, Hkv, page_size, num_cus, tasks_per_cu=4.0, chunk_min=4, chunk_max=256,
+def policy(seq_lens, Hkv, page_size, num_cus, tasks_per_cu=0.75, chunk_min=4, chunk_max=256,
            split_max=256, uniform_ratio=1.25):
     """Pick (mode, param) from the batch size and the length histogram.
 

@@ -35,12 +35,14 @@ PKV_DEVERR_ROW = 4
 PKV_DEVERR_SLOT = 8
 
 PAGE_SIZE = 16
+WORKSPACE_HEADER_BYTES = 65536      # PKV_WORKSPACE_HEADER_BYTES
 
 # Every symbol include/pkv.h declares.
 ABI_SYMBOLS = (
     "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_policy_defaults",
     "pkv_policy", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
     "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_splits", "pkv_merge",
+    "pkv_runner_create", "pkv_runner_step", "pkv_runner_destroy", "pkv_runner_last_plan",
 )
 
 
@@ -56,7 +58,27 @@ class PkvError(RuntimeError):
 class pkv_policy_params(ctypes.Structure):
     _fields_ = [("tasks_per_cu", ctypes.c_float), ("chunk_min", ctypes.c_int32),
                 ("chunk_max", ctypes.c_int32), ("split_max", ctypes.c_int32),
-                ("uniform_ratio", ctypes.c_float)]
+                ("uniform_ratio", ctypes.c_float), ("fuse_max_splits", ctypes.c_int32)]
+
+
+class pkv_step_args(ctypes.Structure):
+    """Mirror of pkv_step_args in include/pkv.h (same field order and types)."""
+    _fields_ = [
+        ("seq_lens_host", ctypes.c_void_p), ("B", ctypes.c_int32), ("mode", ctypes.c_int32),
+        ("param", ctypes.c_int32), ("two_launch", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+        ("max_pages_per_row", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+        ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+        ("event_before_decode", ctypes.c_void_p), ("event_after_decode", ctypes.c_void_p),
+        ("chosen_mode", ctypes.c_int32), ("chosen_param", ctypes.c_int32),
+        ("chosen_two_launch", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+        ("num_tasks", ctypes.c_int64), ("num_partial_slots", ctypes.c_int64),
+        ("workspace_bytes_needed", ctypes.c_size_t),
+    ]
 
 
 _lib = None
@@ -87,7 +109,14 @@ def _load():
         "pkv_workspace_error_flags": ([_vp, ctypes.POINTER(ctypes.c_uint32), _vp], ctypes.c_int),
         "pkv_decode": ([_vp, _vp, _vp, i64, _vp, i32, _vp, _vp, i64, _vp, i64, i32, i32, i32, i32,
                         i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
-        "pkv_merge": ([_vp, i64, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "pkv_merge": ([_vp, i64, i32, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+                      ctypes.c_int),
+        "pkv_runner_create": ([i32, ctypes.POINTER(pkv_policy_params), i32, ctypes.POINTER(_vp)],
+                              ctypes.c_int),
+        "pkv_runner_step": ([_vp, ctypes.POINTER(pkv_step_args)], ctypes.c_int),
+        "pkv_runner_destroy": ([_vp], ctypes.c_int),
+        "pkv_runner_last_plan": ([_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64p, _i32p],
+                                 ctypes.c_int),
     }
     sig["pkv_decode_splits"] = sig["pkv_decode"]
     for name, (args, res) in sig.items():
@@ -265,7 +294,8 @@ def pkv_decode_splits(q, k_pool, v_pool, block_table, seq_lens, tasks, split_off
     _check(_load().pkv_decode_splits(*args), "pkv_decode_splits")
 
 
-def pkv_merge(split_offsets, num_partial_slots: int, out, workspace, lse=None, stream=None):
+def pkv_merge(split_offsets, num_partial_slots: int, Hkv: int, out, workspace, lse=None,
+              stream=None):
     """Enqueue the merge kernel only; see pkv_merge in include/pkv.h."""
     import torch
     B, Hq, D = out.shape
@@ -274,27 +304,59 @@ def pkv_merge(split_offsets, num_partial_slots: int, out, workspace, lse=None, s
     if lse is not None and tuple(lse.shape) != (B, Hq):
         raise ValueError("lse must be [B, Hq]")
     _check(_load().pkv_merge(
-        _dev(split_offsets, torch.int32, "split_offsets"), num_partial_slots, B, Hq, D,
+        _dev(split_offsets, torch.int32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D,
         _dev(out, torch.float16, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
         "pkv_merge")
 
 
-# --------------------------------------------------------------------------- convenience
+# --------------------------------------------------------------------------- runner
+
+def pkv_runner_create(num_cus: int = 0, params: Optional[pkv_policy_params] = None,
+                      ring_depth: int = 8) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    pp = ctypes.byref(params) if params is not None else None
+    _check(_load().pkv_runner_create(num_cus, pp, ring_depth, ctypes.byref(h)), "pkv_runner_create")
+    return h
+
+
+def pkv_runner_step(runner, args: pkv_step_args) -> int:
+    """Run one step (see pkv_runner_step in include/pkv.h); returns the status
+    (PKV_OK or PKV_ERR_BUFFER_TOO_SMALL), raising on any other error."""
+    st = _load().pkv_runner_step(runner, ctypes.byref(args))
+    if st not in (PKV_OK, PKV_ERR_BUFFER_TOO_SMALL):
+        raise PkvError(st, "pkv_runner_step")
+    return st
+
+
+def pkv_runner_destroy(runner):
+    _check(_load().pkv_runner_destroy(runner), "pkv_runner_destroy")
+
+
+def pkv_runner_last_plan(runner):
+    """Copies of the plan the last step's kernels read: (tasks [T,4], split_offsets [B+1])."""
+    offs, tasks = ctypes.c_void_p(), ctypes.c_void_p()
+    T, B = ctypes.c_int64(), ctypes.c_int32()
+    _check(_load().pkv_runner_last_plan(runner, ctypes.byref(offs), ctypes.byref(tasks),
+                                        ctypes.byref(T), ctypes.byref(B)), "pkv_runner_last_plan")
+    o = np.ctypeslib.as_array(ctypes.cast(offs, _i32p), shape=(B.value + 1,)).copy()
+    t = np.ctypeslib.as_array(ctypes.cast(tasks, _i32p), shape=(max(T.value, 1) * 4,))
+    return t[:4 * T.value].reshape(T.value, 4).copy(), o
+
 
 class PagedDecoder:
-    """One decode step = policy -> plan (host C++) -> H2D copy of the task list
-    -> decode + merge kernels, all enqueued on the current stream.
+    """Decode steps through the native runner: one library call per step runs
+    policy -> host plan -> async plan upload -> decode kernel -> merge kernel on
+    the current stream.
 
-    Owns pinned host staging for the plan, device copies of it, and the
-    workspace.  These grow on demand.  The pinned staging is reused only after
-    the copy that read it has completed (an event per ring slot), so steps can
-    be enqueued back to back without host synchronisation.
+    The decoder owns the workspace (a torch allocation, grown on demand) and a
+    runner, whose pinned plan ring the kernels read in place.  The argument
+    block is built once.  A step only rewrites the fields that change.
     """
 
     def __init__(self, Hq: int, Hkv: int, head_dim: int, max_batch: int, max_pages_per_row: int,
-                 device=None, num_cus: Optional[int] = None, ring: int = 4,
+                 device=None, num_cus: Optional[int] = None, ring: int = 8,
                  policy_params: Optional[pkv_policy_params] = None):
         import torch
         self.Hq, self.Hkv, self.D = Hq, Hkv, head_dim
@@ -303,72 +365,99 @@ class PagedDecoder:
         if num_cus is None:
             num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
         self.num_cus = num_cus
-        self.params = policy_params
-        self._ring = []
-        for _ in range(ring):
-            self._ring.append(dict(tasks_h=None, offs_h=torch.empty(max_batch + 1, dtype=torch.int32,
-                                                                   pin_memory=True),
-                                   event=None))
-        self._slot = 0
-        self.tasks_d = torch.empty((0, 4), dtype=torch.int32, device=self.device)
-        self.offs_d = torch.empty(max_batch + 1, dtype=torch.int32, device=self.device)
-        self.workspace = torch.zeros(256, dtype=torch.uint8, device=self.device)
+        self.runner = pkv_runner_create(num_cus, policy_params, ring)
+        self.workspace = torch.zeros(WORKSPACE_HEADER_BYTES, dtype=torch.uint8, device=self.device)
         pkv_workspace_init(self.workspace)
+        self._seq_host = None
+        a = pkv_step_args()
+        a.Hq, a.Hkv, a.head_dim, a.page_size = Hq, Hkv, head_dim, PAGE_SIZE
+        a.max_pages_per_row = max_pages_per_row
+        self.args = a
+        self._bind_buffers()
         self.last = None
 
-    def _ensure_ws(self, slots):
+    def _bind_buffers(self):
+        a = self.args
+        a.workspace = self.workspace.data_ptr()
+        a.workspace_bytes = self.workspace.numel()
+
+    def __del__(self):
+        try:
+            if getattr(self, "runner", None):
+                pkv_runner_destroy(self.runner)
+                self.runner = None
+        except Exception:
+            pass
+
+    def set_inputs(self, q, k_pool, v_pool, block_table, seq_lens, seq_lens_h, scale: float,
+                   out, lse=None):
+        """Bind the tensors of the next steps (checked once here)."""
         import torch
-        need = pkv_workspace_size(slots, self.Hq, self.D)
-        if self.workspace.numel() < need:
+        B, Hq, D = q.shape
+        if (Hq, D) != (self.Hq, self.D) or k_pool.shape[1:] != (self.Hkv, PAGE_SIZE, D):
+            raise ValueError("q / k_pool shape does not match the decoder")
+        if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
+            raise ValueError("shape mismatch between k_pool, v_pool, q and out")
+        if tuple(block_table.shape) != (B, self.max_pages) or tuple(seq_lens.shape) != (B,):
+            raise ValueError("block_table must be [B, max_pages_per_row] and seq_lens [B]")
+        if lse is not None and tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+        a = self.args
+        a.q = _dev(q, torch.float16, "q").value
+        a.k_pool = _dev(k_pool, torch.float16, "k_pool").value
+        a.v_pool = _dev(v_pool, torch.float16, "v_pool").value
+        a.num_pages = k_pool.shape[0]
+        a.block_table = _dev(block_table, torch.int32, "block_table").value
+        a.seq_lens = _dev(seq_lens, torch.int32, "seq_lens").value
+        a.out = _dev(out, torch.float16, "out").value
+        a.lse = _dev(lse, torch.float32, "lse").value if lse is not None else None
+        a.scale = float(scale)
+        self._seq_host = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
+        a.seq_lens_host = self._seq_host.ctypes.data
+        a.B = B
+        self._tensors = (q, k_pool, v_pool, block_table, seq_lens, out, lse)
+
+    def run(self, mode: Optional[int] = None, param: Optional[int] = None, stream=None,
+            events=None, two_launch: Optional[bool] = None):
+        """Enqueue one step on the bound inputs.  ``events`` = (before, after)
+        torch.cuda.Event pair recorded around the decode kernel, or None.
+        ``two_launch``: True = separate merge kernel, False = fused single
+        launch, None = the policy's choice (fuse_max_splits)."""
+        import torch
+        a = self.args
+        a.two_launch = -1 if two_launch is None else (1 if two_launch else 0)
+        a.mode = -1 if mode is None else mode
+        a.param = 0 if param is None else param
+        a.stream = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
+        if events is not None:
+            a.event_before_decode = events[0].cuda_event
+            a.event_after_decode = events[1].cuda_event
+        else:
+            a.event_before_decode = None
+            a.event_after_decode = None
+        while pkv_runner_step(self.runner, a) == PKV_ERR_BUFFER_TOO_SMALL:
             torch.cuda.current_stream().synchronize()
-            self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.device)
-            pkv_workspace_init(self.workspace)
-
-    def plan(self, seq_lens_h: np.ndarray, mode: Optional[int] = None, param: Optional[int] = None,
-             block_table_h: Optional[np.ndarray] = None, num_pages: int = 0):
-        """Host planning + async upload.  Returns (mode, param, T, slots)."""
-        import torch
-        if len(seq_lens_h) + 1 > self._ring[0]["offs_h"].numel():
-            raise ValueError("batch larger than max_batch")
-        if mode is None:
-            mode, param = pkv_policy(seq_lens_h, self.Hkv, self.num_cus, self.params)
-        slot = self._ring[self._slot]
-        self._slot = (self._slot + 1) % len(self._ring)
-        if slot["event"] is not None:
-            slot["event"].synchronize()
-        tasks_np, offs_np, nslots = pkv_plan(
-            seq_lens_h, self.Hkv, self.max_pages, mode, param, block_table_h, num_pages,
-            tasks_out=slot["tasks_h"].numpy() if slot["tasks_h"] is not None else None,
-            offsets_out=slot["offs_h"].numpy())
-        T = tasks_np.shape[0]
-        if slot["tasks_h"] is None or slot["tasks_h"].shape[0] < T:
-            slot["tasks_h"] = torch.empty((max(T, 1), 4), dtype=torch.int32, pin_memory=True)
-            slot["tasks_h"][:T].numpy()[:] = tasks_np
-        if self.tasks_d.shape[0] < T:
-            self.tasks_d = torch.empty((max(T, 1), 4), dtype=torch.int32, device=self.device)
-        B = offs_np.size - 1
-        self._ensure_ws(nslots)
-        self.tasks_d[:T].copy_(slot["tasks_h"][:T], non_blocking=True)
-        self.offs_d[:B + 1].copy_(slot["offs_h"][:B + 1], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        slot["event"] = ev
-        self.last = (mode, param, T, nslots, B)
-        return mode, param, T, nslots
-
-    def decode(self, q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None, lse=None):
-        import torch
-        mode, param, T, nslots, B = self.last
-        if out is None:
-            out = torch.empty_like(q)
-        pkv_decode(q, k_pool, v_pool, block_table, seq_lens, self.tasks_d[:T], self.offs_d[:B + 1],
-                   nslots, scale, out, self.workspace, lse=lse)
-        return out
+            if a.workspace_bytes_needed > a.workspace_bytes:
+                self.workspace = torch.zeros(a.workspace_bytes_needed * 5 // 4 + 256,
+                                             dtype=torch.uint8, device=self.device)
+                pkv_workspace_init(self.workspace)
+            self._bind_buffers()
+        self.last = (a.chosen_mode, a.chosen_param, a.num_tasks, a.num_partial_slots, a.B,
+                     a.chosen_two_launch)
+        return self.last
 
     def step(self, q, k_pool, v_pool, block_table, seq_lens, seq_lens_h, scale: float, out=None,
              lse=None, mode=None, param=None):
-        self.plan(seq_lens_h, mode, param)
-        return self.decode(q, k_pool, v_pool, block_table, seq_lens, scale, out=out, lse=lse)
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        self.set_inputs(q, k_pool, v_pool, block_table, seq_lens, seq_lens_h, scale, out, lse)
+        self.run(mode, param)
+        return out
+
+    def plan_arrays(self):
+        """The plan the last step's kernels read: (tasks [T,4], split_offsets [B+1])."""
+        return pkv_runner_last_plan(self.runner)
 
     def error_flags(self) -> int:
         return pkv_workspace_error_flags(self.workspace)

@@ -22,8 +22,13 @@ LIB = os.path.join(HERE, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-# Packed fp32 VALU forms are switched off for every device compile.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are switched off for every device compile.  The
+# atomic optimizer is off too: the decode kernel issues one counter atomic
+# per task from one lane and consumes it a whole task later, and the
+# optimizer's broadcast of the result would force an immediate wait on every
+# load in flight.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def _hipcc() -> str:
@@ -53,6 +58,11 @@ def build(verbose: bool = False, asm: bool = False) -> str:
     _run([hipcc, "-x", "c++", *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o],
          verbose)
     objs.append(plan_o)
+    run_o = os.path.join(BUILD_DIR, "runner.o")
+    rocm_inc = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc))), "include")
+    _run([hipcc, "-x", "c++", *common, "-D__HIP_PLATFORM_AMD__", "-I", rocm_inc, "-c",
+          os.path.join(CSRC, "runner.cpp"), "-o", run_o], verbose)
+    objs.append(run_o)
     dec_o = os.path.join(BUILD_DIR, "decode.o")
     _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS, "-c",
           os.path.join(CSRC, "decode.hip"), "-o", dec_o], verbose)

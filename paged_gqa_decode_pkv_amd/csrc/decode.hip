@@ -45,12 +45,14 @@
 #include <cstdint>
 
 #include "pkv.h"
+#include "internal.h"
 
 namespace pkv {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned uint2x __attribute__((ext_vector_type(2)));
 
 template <int N>
 using halfN = _Float16 __attribute__((ext_vector_type(N)));
@@ -78,6 +80,8 @@ struct DecodeArgs {
   _Float16* out;
   float* lse;
   uint32_t* ctrl;     // [0] task counter, [1] exit counter, [2] error word
+  uint32_t* arrive;   // [B*Hkv] arrival counters of the fused merge
+  int32_t fuse;       // 1: the last split of a (row, KV head) merges it
   float* part_o;      // [slots][Hq][D]
   float2* part_ml;    // [slots][Hq] (max in log2 units, sum)
 };
@@ -97,222 +101,575 @@ struct PageRegs {
   halfN<VW> v[4];
 };
 
+// Buffer resource for raw buffer loads (gfx9 dword3).  Loads at offsets
+// >= num_records return zero without touching memory.  This gives the
+// streaming loop unconditional loads: a page outside the wave's range, or one
+// whose block-table entry is out of bounds, is loaded with num_records = 0.
+constexpr int kRsrcDword3 = 0x00020000;
+
+// Cache policy of the partial states: system-scope (sc0 sc1) stores write
+// through the per-XCD L2s, and loads with the same bits bypass them.  Split
+// states then reach other workgroups, on any XCD, without a fence that would
+// write back or invalidate a whole L2.
+constexpr int kCoherent = 17;   // sc0 | sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcDword3);
+}
+
 // K operand of the score MFMA: token row `col`, 8 halves at d-chunk 4*kk+grp
-// (d = 32*kk + 8*grp .. +8).  V: token rows 4*grp + j, VW halves starting at
-// d = VW*col.  Each load instruction reads whole 64-byte (K) or row-wide (V)
-// runs of the contiguous page tile.
+// (byte offset koff + 64*kk with koff = 2*(col*D + 8*grp)).  V: token rows
+// 4*grp + j, VW halves at d = VW*col (byte offset voff + 2*D*j with
+// voff = 2*(4*grp*D + VW*col)).  Each K instruction reads 16 runs of 64
+// contiguous bytes, and each V instruction reads 4 whole 2*D-byte rows of
+// the contiguous page tile.
 template <int D>
-__device__ __forceinline__ void load_page(PageRegs<D>& r, const _Float16* __restrict__ kt,
-                                          const _Float16* __restrict__ vt, int col, int grp) {
+__device__ __forceinline__ void load_page(PageRegs<D>& r, __amdgpu_buffer_rsrc_t kr,
+                                          __amdgpu_buffer_rsrc_t vr, int koff, int voff) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    r.k[kk] = *reinterpret_cast<const half8*>(kt + col * D + 8 * (4 * kk + grp));
+    r.k[kk] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r.v[j] = *reinterpret_cast<const halfN<VW>*>(vt + (4 * grp + j) * D + VW * col);
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (VW == 8)
+      r.v[j] = __builtin_bit_cast(halfN<VW>,
+                                  __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
+    else
+      r.v[j] = __builtin_bit_cast(halfN<VW>,
+                                  __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, 0));
+  }
+}
+
+// Online-softmax state of one wave for the G heads of its task, and the
+// per-page update.  Scores are kept in base-2 units (scale*log2(e) folded in).
+//
+// Lazy maximum: the reference m only moves when some score exceeds it by
+// more than kLazy (base 2).  Any reference value gives the same normalised
+// result, since 2^-m cancels between numerator and denominator, and keeping
+// p <= 2^kLazy stays far inside fp16 and fp32 range.  In the common case a
+// page costs no cross-lane traffic and no rescale of the accumulators.
+constexpr float kLazy = 8.0f;
+
+template <int D>
+struct WaveState {
+  static constexpr int VW = D / 16;
+  float m;              // reference max (base 2), same in all 4 lane groups
+  float l;              // this lane's share of sum p (tokens 4*grp+j of each page)
+  floatx4 acc[VW];      // O^T block e: lane holds O[head col][VW*(4*grp+j)+e]
+};
+
+template <int D>
+__device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D>& pg,
+                                             const half8* __restrict__ qf_lds, int nvalid,
+                                             float scale_log2, int lane) {
+  constexpr int KK = D / 32;
+  constexpr int VW = D / 16;
+  const int grp = lane >> 4;
+  // S^T = K . Q^T: lane holds the raw scores of tokens 4*grp+j for head col.
+  // The q operand is re-read from LDS for each page (saves 16 VGPRs).
+  floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pg.k[kk], qf_lds[kk * 64 + lane], sacc, 0, 0, 0);
+  float sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc[j] = sacc[j] * scale_log2;
+  if (nvalid < kPage) {   // last page of the row: mask the tail with selects
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool live = 4 * grp + j < nvalid;
+      sc[j] = live ? sc[j] : -INFINITY;
+      if (!live) pg.v[j] = halfN<VW>{};
+    }
+  }
+  const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazy) != 0) {
+    // a score escaped the window: exact max over the 16 tokens, rescale
+    float mg = fmaxf(mx, __shfl_xor(mx, 16));
+    mg = fmaxf(mg, __shfl_xor(mg, 32));
+    const float m_new = fmaxf(st.m, mg);
+    const float alpha = fast_exp2(st.m - m_new);   // 0 on the first page (m = -inf)
+    st.l *= alpha;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) st.acc[e] *= alpha;
+    st.m = m_new;
+  }
+  half4 pb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pb[j] = static_cast<_Float16>(fast_exp2(sc[j] - st.m));
+  st.l += (static_cast<float>(pb[0]) + static_cast<float>(pb[1])) +
+          (static_cast<float>(pb[2]) + static_cast<float>(pb[3]));
+  // O^T += V^T . P^T, one 16x16x16 MFMA per 16 output columns
+#pragma unroll
+  for (int e = 0; e < VW; ++e) {
+    const half4 av = {pg.v[0][e], pg.v[1][e], pg.v[2][e], pg.v[3][e]};
+    st.acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, st.acc[e], 0, 0, 0);
+  }
+}
+
+struct MergeArgs {
+  const int32_t* split_offsets;
+  int64_t num_slots;
+  int32_t B, Hq, Hkv, G;
+  const float* part_o;
+  const float2* part_ml;
+  _Float16* out;
+  float* lse;
+  uint32_t* ctrl;
+};
+
+// "Sequentie Splitting": the exact combination of the split states.  For
+// query head h of row b, with base-2 states (m_s, l_s, o_s):
+//   M = max_s m_s,  w_s = 2^(m_s - M),
+//   out = sum_s w_s o_s / sum_s w_s l_s,  lse = (M + log2 sum_s w_s l_s) ln 2.
+// One workgroup merges the G heads of one (row, KV head), whose partial
+// outputs are contiguous (G*D floats per slot), over slots o0 .. o0+S-1.
+//   pass 1: M per head.  Thread t strides over (slot, head) pairs with head
+//           t % G, then a wave reduction and an LDS reduction over waves.
+//   pass 2: wave w sums slots w, w+4, ...  Lane owns float4 columns lane,
+//           lane+64, ... of the group.  The 4 wave sums are added in LDS.
+// `lds` holds kMergeLdsFloats floats.  All threads of the workgroup call it.
+template <int D>
+constexpr int merge_lds_floats() {
+  return kWaves * kMaxG * 2 + kWaves * (kMaxG * D / 4) * 4;
 }
 
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2) pkv_decode_kernel(DecodeArgs a) {
+__device__ void merge_group(const MergeArgs& a, int b, int g, int o0, int S, float* lds) {
+  constexpr int kCols = kMaxG * D / 4;              // float4 columns, largest group
+  constexpr int kPerLane = (kCols + 63) / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.G;
+  const int64_t head0 = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G;
+  float (*s_Mw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(lds);
+  float (*s_L)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(lds + kWaves * kMaxG);
+  floatx4 (*s_O)[kCols] = reinterpret_cast<floatx4 (*)[kCols]>(lds + 2 * kWaves * kMaxG);
+
+  // Coherent (L2-bypassing) loads: the states may come from other XCDs.
+  const __amdgpu_buffer_rsrc_t ml_rsrc = make_rsrc(
+      a.part_ml + static_cast<int64_t>(o0) * a.Hq, static_cast<uint32_t>(S) * a.Hq * 8u);
+  const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+      a.part_o + static_cast<int64_t>(o0) * a.Hq * D, static_cast<uint32_t>(S) * a.Hq * D * 4u);
+  auto load_ml = [&](int sl, int h) -> float2 {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+        ml_rsrc, 8 * (sl * a.Hq + g * G + h), 0, kCoherent));
+  };
+
+  // pass 1: maximum of m over the splits, per head
+  {
+    float v = -INFINITY;
+    for (int i = tid; i < S * G; i += kThreads) {
+      const int sl = i / G;
+      const int h = i - sl * G;   // == tid % G, since kThreads % G == 0
+      v = fmaxf(v, load_ml(sl, h).x);
+    }
+    for (int off = 32; off >= G; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane < G) s_Mw[wave][lane] = v;
+  }
+  __syncthreads();
+
+  // pass 2: weighted sums
+  const int cols = G * D / 4;
+  float Mh[kPerLane];
+  floatx4 O[kPerLane];
+  float L[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    const int c = lane + 64 * j;
+    const int h = (c < cols) ? (4 * c) / D : 0;
+    Mh[j] = fmaxf(fmaxf(s_Mw[0][h], s_Mw[1][h]), fmaxf(s_Mw[2][h], s_Mw[3][h]));
+    O[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    L[j] = 0.f;
+  }
+  // Column indices are clamped so every load is unconditional (a
+  // conditional load would make the loop wait on each slot in turn);
+  // clamped columns are dropped when the sums are stored.
+  int cj[kPerLane], hj[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    cj[j] = (lane + 64 * j < cols) ? lane + 64 * j : lane;
+    hj[j] = (4 * cj[j]) / D;
+  }
+#pragma unroll 4
+  for (int sl = wave; sl < S; sl += kWaves) {
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const float2 ml = load_ml(sl, hj[j]);
+      const floatx4 o = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+          o_rsrc, 4 * ((sl * a.Hq + g * G) * D + 4 * cj[j]), 0, kCoherent));
+      const float w = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - Mh[j]);
+      O[j] += w * o;
+      L[j] += w * ml.y;   // used by the lane whose column starts head h
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    const int c = lane + 64 * j;
+    if (c < cols) {
+      s_O[wave][c] = O[j];
+      if ((4 * c) % D == 0) s_L[wave][(4 * c) / D] = L[j];
+    }
+  }
+  __syncthreads();
+
+  for (int c = tid; c < cols; c += kThreads) {
+    const int h = (4 * c) / D;
+    const floatx4 o = s_O[0][c] + s_O[1][c] + s_O[2][c] + s_O[3][c];
+    const float Lh = (s_L[0][h] + s_L[1][h]) + (s_L[2][h] + s_L[3][h]);
+    const float inv = 1.f / Lh;
+    _Float16* dst = a.out + head0 * D + 4 * c;
+    dst[0] = static_cast<_Float16>(o[0] * inv);
+    dst[1] = static_cast<_Float16>(o[1] * inv);
+    dst[2] = static_cast<_Float16>(o[2] * inv);
+    dst[3] = static_cast<_Float16>(o[3] * inv);
+    if ((4 * c) % D == 0 && a.lse) {
+      const float M = fmaxf(fmaxf(s_Mw[0][h], s_Mw[1][h]), fmaxf(s_Mw[2][h], s_Mw[3][h]));
+      a.lse[head0 + h] = (M + __log2f(Lh)) * kLn2;
+    }
+  }
+}
+
+// Output of an empty row (N_b = 0): out = 0, lse = -inf, for the G heads of
+// KV head g.
+template <int D>
+__device__ __forceinline__ void write_empty_group(const MergeArgs& a, int b, int g) {
+  const int64_t head0 = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * a.G;
+  for (int i = threadIdx.x; i < a.G * D; i += kThreads)
+    a.out[head0 * D + i] = static_cast<_Float16>(0.f);
+  if (static_cast<int>(threadIdx.x) < a.G && a.lse) a.lse[head0 + threadIdx.x] = -INFINITY;
+}
+
+// Batches up to kRowStage rows get their lengths and split offsets staged in
+// LDS once per workgroup.  Larger batches read them with scalar loads.
+constexpr int kRowStage = 1024;
+constexpr int kRing = 4;   // page tiles in flight per wave (one "round")
+
+// Everything the workgroup needs to know about one task.  All fields are
+// wave-uniform and live in SGPRs.
+struct Meta {
+  int t;          // task index (>= num_tasks: no task)
+  int b, g;
+  int N;          // row length in tokens
+  int p0, p1;     // page range [p0, p1) of the row
+  int Sb;         // splits of the row
+  int o0;         // first partial-state slot of the row
+  int64_t slot;   // partial-state slot
+  int rounds;     // >= 1 rounds of kRing positions per wave
+  bool ok;        // a real task whose checks passed
+};
+
+// Task record and row-local bounds ("Row-Local Bounds").  A failed check is
+// flagged in the error word and leaves ok = false (all pages disabled).
+// The read-only inputs arrive as restrict pointers, so uniform loads from
+// them are scalar (SMEM) loads, whose waits never cover vector page loads.
+template <bool kStaged>
+__device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __restrict__ tasks,
+                                          const int32_t* __restrict__ seq_lens,
+                                          const int32_t* __restrict__ offs, const int* s_len,
+                                          const int* s_off, int t) {
+  Meta m;
+  m.t = t;
+  m.b = m.g = m.N = m.p0 = m.p1 = m.Sb = m.o0 = 0;
+  m.slot = 0;
+  m.rounds = 1;
+  m.ok = false;
+  if (t >= a.num_tasks) return m;
+  const int4 rec = tasks[t];
+  const int b = __builtin_amdgcn_readfirstlane(rec.x);
+  const int g = __builtin_amdgcn_readfirstlane(rec.y);
+  const int s = __builtin_amdgcn_readfirstlane(rec.z);
+  const int c = __builtin_amdgcn_readfirstlane(rec.w);
+  if (!(b >= 0 && b < a.B && g >= 0 && g < a.Hkv && s >= 0 && c >= 1)) {
+    if (threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_TASK);
+    return m;
+  }
+  // Staging is a compile-time choice.  A runtime select between an LDS and
+  // a global pointer would become a flat load, whose wait also drains every
+  // page load in flight.
+  int N, o0, o1;
+  if constexpr (kStaged) {
+    N = s_len[b];
+    o0 = s_off[b];
+    o1 = s_off[b + 1];
+  } else {
+    N = seq_lens[b];
+    o0 = offs[b];
+    o1 = offs[b + 1];
+  }
+  N = __builtin_amdgcn_readfirstlane(N);
+  o0 = __builtin_amdgcn_readfirstlane(o0);
+  o1 = __builtin_amdgcn_readfirstlane(o1);
+  const int npages = (N + kPage - 1) / kPage;
+  if (N < 0 || npages > a.max_pages) {
+    if (threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_ROW);
+    return m;
+  }
+  const int64_t q0 = static_cast<int64_t>(s) * c;
+  const int64_t q1 = q0 + c;
+  const int p0 = static_cast<int>(q0 < npages ? q0 : npages);
+  const int p1 = static_cast<int>(q1 < npages ? q1 : npages);
+  const int64_t slot = static_cast<int64_t>(o0) + s;
+  if (p0 >= p1 || s >= o1 - o0 || o0 < 0 || slot >= a.num_slots) {
+    if (threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_SLOT);
+    return m;
+  }
+  m.b = b;
+  m.g = g;
+  m.N = N;
+  m.p0 = p0;
+  m.p1 = p1;
+  m.Sb = o1 - o0;
+  m.o0 = o0;
+  m.slot = slot;
+  const int per_wave = (p1 - p0 + kWaves - 1) / kWaves;
+  m.rounds = (per_wave + kRing - 1) / kRing;
+  m.ok = true;
+  return m;
+}
+
+// Block-table entries of round j of task m for this wave: position 4j+r is
+// page p0 + wave + 16j + 4r.  Positions past the range read a clamped,
+// in-row entry that issue() never uses (it re-checks page < p1).  No select
+// on the loaded values, so the four scalar loads issue back to back.
+struct Round {
+  int e[kRing];
+};
+
+__device__ __forceinline__ Round load_round(const DecodeArgs& a, const int32_t* __restrict__ bt,
+                                            const Meta& m, int wave, int j) {
+  Round r;
+  const int32_t* row = bt + static_cast<int64_t>(m.b) * a.max_pages;
+  const int last = m.ok ? m.p1 - 1 : 0;
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    const int page = m.p0 + wave + kWaves * (kRing * j + i);
+    r.e[i] = row[page < last ? page : last];
+  }
+  return r;
+}
+
+template <int D, bool kStaged>
+__global__ void __launch_bounds__(kThreads, 2)
+pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
+                  const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
+                  const int32_t* __restrict__ offs_in) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   constexpr int LDS_STRIDE = D + 4;
+  constexpr uint32_t kTileBytes = static_cast<uint32_t>(kPage * D * 2);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  __shared__ int s_task[2];
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ float s_o[kWaves][kMaxG][LDS_STRIDE];
+  __shared__ int s_len[kStaged ? kRowStage : 1];
+  __shared__ int s_off[kStaged ? kRowStage + 1 : 1];
+  __shared__ int s_next[2];
+  __shared__ half8 s_q[2][KK * 64];                 // q operand of a task, per lane
+  __shared__ float s_m[2][kWaves][16];
+  __shared__ float s_l[2][kWaves][16];
+  __shared__ __attribute__((aligned(16))) float s_o[2][kWaves][kMaxG][LDS_STRIDE];
+  __shared__ int s_last;
+  static_assert(kWaves * kMaxG * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
 
-  uint32_t next_task = 0;
-  if (threadIdx.x == 0) s_task[0] = static_cast<int>(atomicAdd(a.ctrl, 1u));
-
-  const int G = a.G;
-  const int64_t tile_elems = static_cast<int64_t>(kPage) * D;
-
-  for (int it = 0;; ++it) {
-    __syncthreads();
-    const int t = s_task[it & 1];
-    if (t >= a.num_tasks) break;
-    if (threadIdx.x == 0) next_task = atomicAdd(a.ctrl, 1u);
-
-    // ---- task record and row-local bounds ("Row-Local Bounds")
-    const int4 rec = *reinterpret_cast<const int4*>(a.tasks + 4 * static_cast<int64_t>(t));
-    const int b = rec.x, g = rec.y, s = rec.z, c = rec.w;
-    bool ok = (b >= 0 && b < a.B && g >= 0 && g < a.Hkv && s >= 0 && c >= 1);
-    int N = 0, p0 = 0, p1 = 0, Sb = 0;
-    int64_t slot = 0;
-    if (ok) {
-      N = a.seq_lens[b];
-      const int npages = (N + kPage - 1) / kPage;
-      if (N < 0 || npages > a.max_pages) {
-        if (threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_ROW);
-        ok = false;
-      } else {
-        const int64_t q0 = static_cast<int64_t>(s) * c;
-        p0 = static_cast<int>(q0 < npages ? q0 : npages);
-        const int64_t q1 = q0 + c;
-        p1 = static_cast<int>(q1 < npages ? q1 : npages);
-        const int o0 = a.split_offsets[b], o1 = a.split_offsets[b + 1];
-        Sb = o1 - o0;
-        slot = static_cast<int64_t>(o0) + s;
-        if (p0 >= p1 || s >= Sb || o0 < 0 || slot >= a.num_slots) {
-          if (threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_SLOT);
-          ok = false;
-        }
-      }
-    } else if (threadIdx.x == 0) {
-      flag_error(a.ctrl, PKV_DEVERR_TASK);
-    }
-    if (!ok) {
-      if (threadIdx.x == 0) s_task[(it + 1) & 1] = static_cast<int>(next_task);
-      continue;
-    }
-
-    // ---- q operand: B of the score MFMA, column = head within the group
-    half8 qf[KK];
-    {
-      const bool live = col < G;
-      const _Float16* qp =
-          a.q + (static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G + (live ? col : 0)) * D;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        half8 x = *reinterpret_cast<const half8*>(qp + 8 * (4 * kk + grp));
-        qf[kk] = live ? x : half8{};
-      }
-    }
-
-    // ---- per-wave online softmax over pages p0 + wave, p0 + wave + 4, ...
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    floatx4 acc[VW];
-#pragma unroll
-    for (int e = 0; e < VW; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_pages;
-    const _Float16* kbase = a.k + static_cast<int64_t>(g) * tile_elems;
-    const _Float16* vbase = a.v + static_cast<int64_t>(g) * tile_elems;
-    const int64_t page_stride = static_cast<int64_t>(a.Hkv) * tile_elems;
-
-    int p = p0 + wave;
-    PageRegs<D> cur;
-    bool have = false;
-    auto fetch = [&](int pg, PageRegs<D>& r) -> bool {
-      int phys = bt_row[pg];
-      phys = __builtin_amdgcn_readfirstlane(phys);
-      if (phys < 0 || phys >= a.num_pages) {
-        if (lane == 0) flag_error(a.ctrl, PKV_DEVERR_PAGE);
-        return false;
-      }
-      const int64_t off = static_cast<int64_t>(phys) * page_stride;
-      load_page<D>(r, kbase + off, vbase + off, col, grp);
-      return true;
-    };
-    if (p < p1) have = fetch(p, cur);
-
-    while (p < p1) {
-      const int pn = p + kWaves;
-      PageRegs<D> nxt;
-      bool have_n = false;
-      if (pn < p1) have_n = fetch(pn, nxt);
-
-      if (have) {
-        const int nvalid = N - p * kPage;   // >= 1; >= 16 means a full page
-        // scores S^T: lane holds tokens 4*grp + j, head col
-        floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.k[kk], qf[kk], sacc, 0, 0, 0);
-        float sc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x = sacc[j] * a.scale_log2;
-          sc[j] = (4 * grp + j < nvalid) ? x : -INFINITY;
-        }
-        if (nvalid < kPage) {
-          // zero V rows past the end so 0 * NaN cannot reach the accumulators
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (4 * grp + j >= nvalid) cur.v[j] = halfN<VW>{};
-        }
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any(m_new > m_run)) {
-          const float alpha = fast_exp2(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int e = 0; e < VW; ++e) acc[e] *= alpha;
-          m_run = m_new;
-        }
-        half4 pb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pb[j] = static_cast<_Float16>(fast_exp2(sc[j] - m_run));
-        l_run += (static_cast<float>(pb[0]) + static_cast<float>(pb[1])) +
-                 (static_cast<float>(pb[2]) + static_cast<float>(pb[3]));
-#pragma unroll
-        for (int e = 0; e < VW; ++e) {
-          half4 av = {cur.v[0][e], cur.v[1][e], cur.v[2][e], cur.v[3][e]};
-          acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, acc[e], 0, 0, 0);
-        }
-      }
-      cur = nxt;
-      have = have_n;
-      p = pn;
-    }
-
-    // ---- combine the 4 waves' states in LDS
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (col < G) {
-      if (grp == 0) {
-        s_m[wave][col] = m_run;
-        s_l[wave][col] = l_run;
-      }
-      // acc[e][j] is O[head col][d = VW*(4*grp + j) + e]
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < VW; ++e) s_o[wave][col][VW * (4 * grp + j) + e] = acc[e][j];
-    }
-    if (threadIdx.x == 0) s_task[(it + 1) & 1] = static_cast<int>(next_task);
-    __syncthreads();
-
-    const bool direct = (Sb == 1);
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-      const int h = idx / D;
-      const int d = idx - h * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_m[w][h];
-        const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        L += wt * s_l[w][h];
-        O += wt * s_o[w][h][d];
-      }
-      const int64_t hq = static_cast<int64_t>(g) * G + h;
-      if (direct) {
-        a.out[(static_cast<int64_t>(b) * a.Hq + hq) * D + d] = static_cast<_Float16>(O / L);
-        if (d == 0 && a.lse) a.lse[static_cast<int64_t>(b) * a.Hq + hq] = (M + __log2f(L)) * kLn2;
-      } else {
-        a.part_o[(slot * a.Hq + hq) * D + d] = O;
-        if (d == 0) a.part_ml[slot * a.Hq + hq] = make_float2(M, L);
-      }
+  const MergeArgs ma{a.split_offsets, a.num_slots, a.B, a.Hq, a.Hkv, a.G,
+                     a.part_o, a.part_ml, a.out, a.lse, a.ctrl};
+  if constexpr (kStaged) {
+    for (int i = tid; i < a.B; i += kThreads) s_len[i] = seq_lens_in[i];
+    for (int i = tid; i <= a.B; i += kThreads) s_off[i] = offs_in[i];
+  }
+  __syncthreads();
+  if (a.fuse) {
+    // rows without tasks (N_b = 0): out = 0, lse = -inf
+    for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+      const int sb = kStaged ? s_off[b + 1] - s_off[b] : offs_in[b + 1] - offs_in[b];
+      if (sb == 0)
+        for (int g = 0; g < a.Hkv; ++g) write_empty_group<D>(ma, b, g);
     }
   }
 
+  const int G = a.G;
+  const int64_t tile_elems = static_cast<int64_t>(kPage) * D;
+  const int64_t stride_bytes = static_cast<int64_t>(a.Hkv) * tile_elems * 2;
+  const int koff = 2 * (col * D + 8 * grp);
+  const int voff = 2 * (4 * grp * D + VW * col);
+  const char* kpool = reinterpret_cast<const char*>(a.k);
+  const char* vpool = reinterpret_cast<const char*>(a.v);
+
+  // Load the page at position `pos` of task m (entry e) into `r`.  A
+  // position past the range, an invalid task or an out-of-pool entry loads
+  // nothing (num_records = 0) and returns false.
+  auto issue = [&](const Meta& m, int pos, int e, PageRegs<D>& r) -> bool {
+    const int page = m.p0 + wave + kWaves * pos;
+    const bool want = m.ok && page < m.p1;
+    const bool inr = e >= 0 && static_cast<int64_t>(e) < a.num_pages;
+    if (want && !inr && lane == 0) flag_error(a.ctrl, PKV_DEVERR_PAGE);
+    const bool live = want && inr;
+    const int64_t off = static_cast<int64_t>(m.g) * tile_elems * 2 +
+                        (live ? static_cast<int64_t>(e) * stride_bytes : 0);
+    const uint32_t bytes = live ? kTileBytes : 0u;
+    load_page<D>(r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff, voff);
+    return live;
+  };
+  // q of task m (B operand of the score MFMA, column = head within the
+  // group).  Raw loads; columns >= G are zeroed when stored to LDS, so the
+  // loads can stay in flight until then.
+  auto load_q = [&](const Meta& m, half8 (&qf)[KK]) {
+    const bool live = m.ok && col < G;
+    const _Float16* qp = a.q + (static_cast<int64_t>(m.b) * a.Hq +
+                                static_cast<int64_t>(m.g) * G + (live ? col : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qp + 8 * (4 * kk + grp));
+  };
+  auto store_q = [&](const Meta& m, const half8 (&qf)[KK], half8* dst) {
+    const bool live = m.ok && col < G;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) dst[kk * 64 + lane] = live ? qf[kk] : half8{};
+  };
+
+  // ---- prologue: task 0 = blockIdx.x, task 1 = blockIdx.x + gridDim.x
+  Meta cur = load_meta<kStaged>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, blockIdx.x);
+  int t_nxt = blockIdx.x + gridDim.x;
+  PageRegs<D> ring[kRing];
+  bool valid[kRing];
+  {
+    const Round r0 = load_round(a, bt_in, cur, wave, 0);
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
+    if (wave == 0) {
+      half8 qf[KK];
+      load_q(cur, qf);
+      store_q(cur, qf, s_q[0]);
+    }
+  }
+  __syncthreads();
+
+  for (int it = 0; cur.t < a.num_tasks; ++it) {
+    const int par = it & 1;
+    // next task's metadata, its first round of table entries and its q;
+    // the index of the task after it (counter values start at 2*gridDim.x)
+    const Meta nxt = load_meta<kStaged>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, t_nxt);
+    const Round nr0 = load_round(a, bt_in, nxt, wave, 0);
+    // Wave 0: the index after next and the next task's q, both to LDS.
+    // Their loads queue behind this task's first round, which the wave has
+    // to wait for next anyway, so the wait costs nothing extra.
+    if (wave == 0) {
+      const bool fetch = t_nxt < a.num_tasks;
+      uint32_t raw_nn = 0;
+      if (fetch && lane == 0) raw_nn = atomicAdd(a.ctrl, 1u);
+      half8 qn[KK];
+      load_q(nxt, qn);
+      store_q(nxt, qn, s_q[par ^ 1]);
+      if (lane == 0)
+        s_next[par] = fetch ? static_cast<int>(2u * gridDim.x + raw_nn) : a.num_tasks;
+    }
+
+    WaveState<D> st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) st.acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int j = 0; j < cur.rounds; ++j) {
+      const bool last = (j + 1 == cur.rounds);
+      const Round fr = last ? nr0 : load_round(a, bt_in, cur, wave, j + 1);
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        if (valid[r]) {
+          const int page = cur.p0 + wave + kWaves * (kRing * j + r);
+          process_page<D>(st, ring[r], s_q[par], cur.N - page * kPage, a.scale_log2, lane);
+        }
+        // refill the slot with the position one round ahead
+        if (last)
+          valid[r] = issue(nxt, r, fr.e[r], ring[r]);
+        else
+          valid[r] = issue(cur, kRing * (j + 1) + r, fr.e[r], ring[r]);
+      }
+    }
+
+    // ---- this wave's state to LDS
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    if (col < G) {
+      if (grp == 0) {
+        s_m[par][wave][col] = st.m;
+        s_l[par][wave][col] = st.l;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < VW; ++e) s_o[par][wave][col][VW * (4 * grp + j) + e] = st.acc[e][j];
+    }
+    __syncthreads();
+
+    // ---- combine the 4 waves' states; write the output or the partial
+    if (cur.ok) {
+      const bool direct = (cur.Sb == 1);
+      for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[par][w][h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = s_m[par][w][h];
+          const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+          L += wt * s_l[par][w][h];
+          O += wt * s_o[par][w][h][d];
+        }
+        const int64_t hq = static_cast<int64_t>(cur.g) * G + h;
+        if (direct) {
+          a.out[(static_cast<int64_t>(cur.b) * a.Hq + hq) * D + d] = static_cast<_Float16>(O / L);
+          if (d == 0 && a.lse)
+            a.lse[static_cast<int64_t>(cur.b) * a.Hq + hq] = (M + __log2f(L)) * kLn2;
+        } else {
+          // write-through (system-scope) stores, read back by the merge
+          const __amdgpu_buffer_rsrc_t po = make_rsrc(
+              a.part_o + cur.slot * a.Hq * D, static_cast<uint32_t>(a.Hq) * D * 4u);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, O), po,
+                                                4 * (static_cast<int>(hq) * D + d), 0, kCoherent);
+          if (d == 0) {
+            const __amdgpu_buffer_rsrc_t pm = make_rsrc(
+                a.part_ml + cur.slot * a.Hq, static_cast<uint32_t>(a.Hq) * 8u);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(uint2x, make_float2(M, L)), pm, 8 * static_cast<int>(hq), 0,
+                kCoherent);
+          }
+        }
+      }
+      if (a.fuse && !direct) {
+        // Fused merge.  Each thread waits until its write-through stores are
+        // acknowledged, the workgroup then counts this split in, and the
+        // last split of the (row, KV head) merges the group with coherent
+        // loads.  No L2 write-back or invalidate is needed.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+          uint32_t* cnt = a.arrive + static_cast<int64_t>(cur.b) * a.Hkv + cur.g;
+          s_last = (atomicAdd(cnt, 1u) + 1u == static_cast<uint32_t>(cur.Sb)) ? 1 : 0;
+        }
+        __syncthreads();
+        if (s_last) {
+          merge_group<D>(ma, cur.b, cur.g, cur.o0, cur.Sb, &s_o[par][0][0][0]);
+          if (tid == 0) atomicExch(a.arrive + static_cast<int64_t>(cur.b) * a.Hkv + cur.g, 0u);
+        }
+      }
+    }
+    t_nxt = __builtin_amdgcn_readfirstlane(s_next[par]);
+    cur = nxt;
+  }
+
   // Last workgroup out resets the counters for the next launch.
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const uint32_t prev = atomicAdd(a.ctrl + 1, 1u);
     if (prev == gridDim.x - 1) {
       atomicExch(a.ctrl, 0u);
@@ -321,68 +678,32 @@ __global__ void __launch_bounds__(kThreads, 2) pkv_decode_kernel(DecodeArgs a) {
   }
 }
 
-struct MergeArgs {
-  const int32_t* split_offsets;
-  int64_t num_slots;
-  int32_t B, Hq;
-  const float* part_o;
-  const float2* part_ml;
-  _Float16* out;
-  float* lse;
-  uint32_t* ctrl;
-};
-
-// "Sequentie Splitting": the separate merge that combines split states
-// exactly.  M = max m_s, w_s = 2^(m_s - M), out = sum w_s o_s / sum w_s l_s.
+// Kernel 2 of the two-launch form: one workgroup per (row, KV head).
 template <int D>
-__global__ void __launch_bounds__(64) pkv_merge_kernel(MergeArgs a) {
-  constexpr int PER = D / 64;
-  const int b = blockIdx.x / a.Hq;
-  const int h = blockIdx.x - b * a.Hq;
-  const int o0 = a.split_offsets[b];
-  const int S = a.split_offsets[b + 1] - o0;
+__global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[merge_lds_floats<D>()];
+  const int b = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x - b * a.Hkv;
+  const int o0 = __builtin_amdgcn_readfirstlane(a.split_offsets[b]);
+  const int S = __builtin_amdgcn_readfirstlane(a.split_offsets[b + 1]) - o0;
   if (S == 1) return;   // written directly by the decode kernel
-  const int64_t row = static_cast<int64_t>(b) * a.Hq + h;
   if (S <= 0 || o0 < 0 || static_cast<int64_t>(o0) + S > a.num_slots) {
     if (S != 0 && threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_SLOT);
-    // empty row: out = 0, lse = -inf
-#pragma unroll
-    for (int i = 0; i < PER; ++i) a.out[row * D + threadIdx.x * PER + i] = static_cast<_Float16>(0.f);
-    if (threadIdx.x == 0 && a.lse) a.lse[row] = -INFINITY;
+    write_empty_group<D>(a, b, g);
     return;
   }
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[(static_cast<int64_t>(o0) + s) * a.Hq + h].x);
-  float L = 0.f;
-  float O[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) O[i] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const int64_t sl = (static_cast<int64_t>(o0) + s) * a.Hq + h;
-    const float2 ml = a.part_ml[sl];
-    const float w = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - M);
-    L += w * ml.y;
-    const float* po = a.part_o + sl * D + threadIdx.x * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) O[i] += w * po[i];
-  }
-  const float inv = 1.f / L;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) a.out[row * D + threadIdx.x * PER + i] = static_cast<_Float16>(O[i] * inv);
-  if (threadIdx.x == 0 && a.lse) a.lse[row] = (M + __log2f(L)) * kLn2;
+  merge_group<D>(a, b, g, o0, S, lds);
 }
 
 // ---------------------------------------------------------------------------
 // host glue
-
-thread_local int g_last_hip_error = 0;
 
 int num_cus_of_current_device(int* cus) {
   static int cache[64] = {0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
-    g_last_hip_error = static_cast<int>(e);
+    set_hip_error(static_cast<int>(e));
     return PKV_ERR_HIP;
   }
   if (dev >= 0 && dev < 64 && cache[dev] > 0) {
@@ -392,7 +713,7 @@ int num_cus_of_current_device(int* cus) {
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess || n <= 0) {
-    g_last_hip_error = static_cast<int>(e);
+    set_hip_error(static_cast<int>(e));
     return PKV_ERR_HIP;
   }
   if (dev >= 0 && dev < 64) cache[dev] = n;
@@ -403,18 +724,24 @@ int num_cus_of_current_device(int* cus) {
 template <int D>
 int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream) {
   if (da.num_tasks > 0) {
-    hipLaunchKernelGGL(pkv_decode_kernel<D>, dim3(grid), dim3(kThreads), 0, stream, da);
+    const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
+    if (da.B <= kRowStage)
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, da,
+                         tasks, da.block_table, da.seq_lens, da.split_offsets);
+    else
+      hipLaunchKernelGGL((pkv_decode_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, da,
+                         tasks, da.block_table, da.seq_lens, da.split_offsets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
-      g_last_hip_error = static_cast<int>(e);
+      set_hip_error(static_cast<int>(e));
       return PKV_ERR_HIP;
     }
   }
   if (ma.B > 0) {
-    hipLaunchKernelGGL(pkv_merge_kernel<D>, dim3(ma.B * ma.Hq), dim3(64), 0, stream, ma);
+    hipLaunchKernelGGL(pkv_merge_kernel<D>, dim3(ma.B * ma.Hkv), dim3(kThreads), 0, stream, ma);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
-      g_last_hip_error = static_cast<int>(e);
+      set_hip_error(static_cast<int>(e));
       return PKV_ERR_HIP;
     }
   }
@@ -425,13 +752,12 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
 
 extern "C" {
 
-int pkv_last_hip_error(void) { return pkv::g_last_hip_error; }
-
 int pkv_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-  if (!workspace || workspace_bytes < 256) return PKV_ERR_INVALID_ARG;
-  hipError_t e = hipMemsetAsync(workspace, 0, 256, static_cast<hipStream_t>(stream));
+  if (!workspace || workspace_bytes < PKV_WORKSPACE_HEADER_BYTES) return PKV_ERR_INVALID_ARG;
+  hipError_t e = hipMemsetAsync(workspace, 0, PKV_WORKSPACE_HEADER_BYTES,
+                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
-    pkv::g_last_hip_error = static_cast<int>(e);
+    pkv::set_hip_error(static_cast<int>(e));
     return PKV_ERR_HIP;
   }
   return PKV_OK;
@@ -445,7 +771,7 @@ int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stre
     e = hipMemcpy(flags, static_cast<const uint32_t*>(workspace) + 2, sizeof(uint32_t),
                   hipMemcpyDeviceToHost);
   if (e != hipSuccess) {
-    pkv::g_last_hip_error = static_cast<int>(e);
+    pkv::set_hip_error(static_cast<int>(e));
     return PKV_ERR_HIP;
   }
   return PKV_OK;
@@ -467,7 +793,7 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128) || Hq % Hkv != 0)
     return PKV_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
-  if (need_decode && G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * Hq > INT32_MAX) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (!split_offsets || !out || !workspace) return PKV_ERR_INVALID_ARG;
@@ -485,9 +811,10 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   if (workspace_bytes < need) return PKV_ERR_BUFFER_TOO_SMALL;
 
   char* ws = static_cast<char*>(workspace);
-  float* part_o = reinterpret_cast<float*>(ws + 256);
-  float2* part_ml = reinterpret_cast<float2*>(
-      ws + 256 + static_cast<size_t>(num_partial_slots) * Hq * head_dim * sizeof(float));
+  float* part_o = reinterpret_cast<float*>(ws + PKV_WORKSPACE_HEADER_BYTES);
+  float2* part_ml = reinterpret_cast<float2*>(ws + PKV_WORKSPACE_HEADER_BYTES +
+                                              static_cast<size_t>(num_partial_slots) * Hq *
+                                                  head_dim * sizeof(float));
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
 
   da->q = static_cast<const _Float16*>(q);
@@ -509,6 +836,8 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   da->out = static_cast<_Float16*>(out);
   da->lse = lse;
   da->ctrl = ctrl;
+  da->arrive = ctrl + 64;
+  da->fuse = 0;
   da->part_o = part_o;
   da->part_ml = part_ml;
 
@@ -516,6 +845,8 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   ma->num_slots = num_partial_slots;
   ma->B = B;
   ma->Hq = Hq;
+  ma->Hkv = Hkv;
+  ma->G = G;
   ma->part_o = part_o;
   ma->part_ml = part_ml;
   ma->out = static_cast<_Float16*>(out);
@@ -529,13 +860,20 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
         const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,
         int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
         int32_t page_size, float scale, void* out, float* lse, void* workspace,
-        size_t workspace_bytes, void* stream, bool do_decode, bool do_merge) {
+        size_t workspace_bytes, void* stream, bool do_decode, bool do_merge, bool fused) {
   pkv::DecodeArgs da{};
   pkv::MergeArgs ma{};
   int st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
                    num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size,
                    scale, out, lse, workspace, workspace_bytes, do_decode, &da, &ma);
   if (st != PKV_OK || B == 0) return st;
+  // Fused single launch when the arrival counters fit and there is work for
+  // the decode kernel; otherwise the two-launch form.
+  if (fused && do_decode && num_tasks > 0 &&
+      static_cast<int64_t>(B) * Hkv <= PKV_MAX_FUSED_GROUPS) {
+    da.fuse = 1;
+    do_merge = false;
+  }
   int grid = 1;
   if (do_decode) {
     int cus = 0;
@@ -563,7 +901,7 @@ int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t nu
                void* stream) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
              num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, scale,
-             out, lse, workspace, workspace_bytes, stream, true, true);
+             out, lse, workspace, workspace_bytes, stream, true, true, true);
 }
 
 int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
@@ -575,15 +913,15 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
                       size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
              num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, scale,
-             out, lse, workspace, workspace_bytes, stream, true, false);
+             out, lse, workspace, workspace_bytes, stream, true, false, false);
 }
 
 int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B, int32_t Hq,
-              int32_t head_dim, void* out, float* lse, void* workspace, size_t workspace_bytes,
-              void* stream) {
+              int32_t Hkv, int32_t head_dim, void* out, float* lse, void* workspace,
+              size_t workspace_bytes, void* stream) {
   return run(nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, 0, split_offsets,
-             num_partial_slots, B, Hq, 1, head_dim, pkv::kPage, 1.0f, out, lse, workspace,
-             workspace_bytes, stream, false, true);
+             num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, 1.0f, out, lse, workspace,
+             workspace_bytes, stream, false, true, false);
 }
 
 }  // extern "C"

@@ -7,6 +7,7 @@
 // "Compact Workqueue", and "2. Calibrated Adaptive Policy".
 
 #include "pkv.h"
+#include "internal.h"
 
 #include <cstdint>
 #include <cstring>
@@ -17,11 +18,19 @@ constexpr int32_t kPageSize = 16;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+thread_local int g_last_hip_error = 0;
+
 }  // namespace
+
+namespace pkv {
+void set_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace pkv
 
 extern "C" {
 
 int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+int pkv_last_hip_error(void) { return g_last_hip_error; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -37,11 +46,12 @@ const char* pkv_status_string(int status) {
 
 int pkv_policy_defaults(pkv_policy_params* p) {
   if (!p) return PKV_ERR_INVALID_ARG;
-  p->tasks_per_cu = 4.0f;
+  p->tasks_per_cu = 0.75f;
   p->chunk_min = 4;
   p->chunk_max = 256;
   p->split_max = 256;
   p->uniform_ratio = 1.25f;
+  p->fuse_max_splits = 16;
   return PKV_OK;
 }
 
@@ -60,7 +70,7 @@ int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_siz
     pkv_policy_defaults(&p);
   }
   if (!(p.tasks_per_cu > 0.0f) || p.chunk_min < 1 || p.chunk_max < p.chunk_min ||
-      p.split_max < 1 || !(p.uniform_ratio >= 1.0f))
+      p.split_max < 1 || !(p.uniform_ratio >= 1.0f) || p.fuse_max_splits < 0)
     return PKV_ERR_INVALID_ARG;
 
   int64_t active = 0, total = 0, nmin = INT64_MAX, nmax = 0;
@@ -161,7 +171,7 @@ int pkv_workspace_size(int64_t num_partial_slots, int32_t Hq, int32_t head_dim,
                        size_t* bytes) {
   if (!bytes || num_partial_slots < 0 || Hq < 0 || head_dim < 0) return PKV_ERR_INVALID_ARG;
   const uint64_t per_slot = static_cast<uint64_t>(Hq) * (static_cast<uint64_t>(head_dim) + 2) * 4;
-  uint64_t total = 256 + static_cast<uint64_t>(num_partial_slots) * per_slot;
+  uint64_t total = PKV_WORKSPACE_HEADER_BYTES + static_cast<uint64_t>(num_partial_slots) * per_slot;
   total = (total + 255) & ~static_cast<uint64_t>(255);
   *bytes = static_cast<size_t>(total);
   return PKV_OK;

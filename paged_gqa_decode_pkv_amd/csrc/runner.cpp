@@ -1,0 +1,229 @@
+// Native step runner: one call runs the whole hot path of a decode step.
+// It chooses the policy, plans on the host, uploads the plan in one async
+// copy, and enqueues the decode and merge kernels.
+//
+// Source: PersistentKV (arXiv 2606.26666), gist.science explainer,
+// "Technische Samenvatting" > "2. Calibrated Adaptive Policy" and
+// Methodologie ("Row-Local Bounds", "Compact Workqueue").  Host planning is
+// part of the step, and the "Evaluatieprotocol" wall timing includes it.
+//
+// The runner owns host resources only: a ring of pinned plan buffers, each
+// guarded by a HIP event, so a slot is rewritten only after the kernels that
+// read it have completed.  The kernels read the plan in place from pinned
+// host memory (16 bytes per task, read once).  A small DMA copy would cost
+// more on the device timeline than the whole read.  Device memory
+// (workspace) belongs to the caller.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "pkv.h"
+#include "internal.h"
+
+namespace {
+
+struct Slot {
+  int32_t* host = nullptr;   // pinned: split_offsets (padded) then tasks
+  int32_t* dev = nullptr;    // the same memory as seen by the device
+  size_t bytes = 0;
+  hipEvent_t done = nullptr; // recorded after the kernels that read it
+  bool armed = false;
+  int32_t B = 0;
+  int64_t T = 0;
+};
+
+inline size_t pad4(int64_t n) { return static_cast<size_t>((n + 3) & ~int64_t(3)); }
+
+}  // namespace
+
+struct pkv_runner {
+  int32_t num_cus = 0;
+  pkv_policy_params params{};
+  std::vector<Slot> ring;
+  size_t next = 0;
+  Slot* last = nullptr;
+};
+
+extern "C" {
+
+int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t ring_depth,
+                      pkv_runner** runner) {
+  if (!runner || ring_depth < 1 || ring_depth > 1024 || num_cus < 0) return PKV_ERR_INVALID_ARG;
+  *runner = nullptr;
+  if (num_cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || num_cus <= 0) {
+      pkv::set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
+  }
+  pkv_runner* r = new (std::nothrow) pkv_runner();
+  if (!r) return PKV_ERR_INVALID_ARG;
+  r->num_cus = num_cus;
+  if (params) {
+    r->params = *params;
+  } else {
+    pkv_policy_defaults(&r->params);
+  }
+  r->ring.resize(static_cast<size_t>(ring_depth));
+  for (Slot& s : r->ring) {
+    hipError_t e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pkv::set_hip_error(static_cast<int>(e));
+      pkv_runner_destroy(r);
+      return PKV_ERR_HIP;
+    }
+  }
+  *runner = r;
+  return PKV_OK;
+}
+
+int pkv_runner_destroy(pkv_runner* r) {
+  if (!r) return PKV_OK;
+  int st = PKV_OK;
+  for (Slot& s : r->ring) {
+    if (s.done) {
+      if (s.armed) hipEventSynchronize(s.done);
+      hipEventDestroy(s.done);
+    }
+    if (s.host && hipHostFree(s.host) != hipSuccess) st = PKV_ERR_HIP;
+  }
+  delete r;
+  return st;
+}
+
+int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
+  if (!r || !a) return PKV_ERR_INVALID_ARG;
+  if (a->B < 0 || (a->B > 0 && !a->seq_lens_host)) return PKV_ERR_INVALID_ARG;
+
+  // policy ("2. Calibrated Adaptive Policy")
+  int32_t mode = a->mode, param = a->param;
+  if (mode < 0) {
+    int st = pkv_policy(a->seq_lens_host, a->B, a->Hkv, a->page_size, r->num_cus, &r->params,
+                        &mode, &param);
+    if (st != PKV_OK) return st;
+  }
+  a->chosen_mode = mode;
+  a->chosen_param = param;
+
+  // plan sizes and buffer checks
+  int64_t T = 0, slots = 0;
+  int st = pkv_plan(a->seq_lens_host, a->B, a->Hkv, a->page_size, a->max_pages_per_row, nullptr,
+                    0, mode, param, nullptr, 0, nullptr, &T, &slots);
+  if (st != PKV_OK) return st;
+  a->num_tasks = T;
+  a->num_partial_slots = slots;
+  const size_t off_words = pad4(static_cast<int64_t>(a->B) + 1);
+  const size_t plan_bytes = (off_words + 4 * static_cast<size_t>(T)) * sizeof(int32_t);
+  size_t ws_bytes = 0;
+  pkv_workspace_size(slots, a->Hq, a->head_dim, &ws_bytes);
+  a->workspace_bytes_needed = ws_bytes;
+  if (!a->workspace) return PKV_ERR_INVALID_ARG;
+  if (a->workspace_bytes < ws_bytes) return PKV_ERR_BUFFER_TOO_SMALL;
+
+  // a plan slot whose previous readers have finished
+  Slot& s = r->ring[r->next];
+  r->next = (r->next + 1) % r->ring.size();
+  hipStream_t stream = static_cast<hipStream_t>(a->stream);
+  hipError_t e = hipSuccess;
+  if (s.armed) {
+    e = hipEventSynchronize(s.done);
+    s.armed = false;
+    if (e != hipSuccess) {
+      pkv::set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
+  }
+  if (s.bytes < plan_bytes) {
+    if (s.host) hipHostFree(s.host);
+    s.host = s.dev = nullptr;
+    s.bytes = 0;
+    size_t want = plan_bytes < 4096 ? 4096 : plan_bytes + plan_bytes / 4;
+    e = hipHostMalloc(reinterpret_cast<void**>(&s.host), want, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s.dev), s.host, 0);
+    if (e != hipSuccess) {
+      if (s.host) hipHostFree(s.host);
+      s.host = s.dev = nullptr;
+      pkv::set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
+    s.bytes = want;
+  }
+  int32_t* offs_h = s.host;
+  int32_t* tasks_h = s.host + off_words;
+  st = pkv_plan(a->seq_lens_host, a->B, a->Hkv, a->page_size, a->max_pages_per_row, nullptr, 0,
+                mode, param, tasks_h, T, offs_h, &T, &slots);
+  if (st != PKV_OK) return st;
+  for (size_t i = static_cast<size_t>(a->B) + 1; i < off_words; ++i) offs_h[i] = 0;
+  int32_t max_splits = 0;
+  for (int32_t b = 0; b < a->B; ++b)
+    if (offs_h[b + 1] - offs_h[b] > max_splits) max_splits = offs_h[b + 1] - offs_h[b];
+  a->max_splits = max_splits;
+  const bool two = a->two_launch < 0 ? (max_splits > r->params.fuse_max_splits)
+                                     : (a->two_launch != 0);
+  a->chosen_two_launch = two ? 1 : 0;
+  s.B = a->B;
+  s.T = T;
+  r->last = &s;
+  const int32_t* offs_d = s.dev;
+  const int32_t* tasks_d = s.dev + off_words;
+
+  // the decode kernel (merge fused in), or decode then merge kernel
+  if (a->event_before_decode) {
+    e = hipEventRecord(static_cast<hipEvent_t>(a->event_before_decode), stream);
+    if (e != hipSuccess) {
+      pkv::set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
+  }
+  if (two) {
+    st = pkv_decode_splits(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
+                           a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B,
+                           a->Hq, a->Hkv, a->head_dim, a->page_size, a->scale, a->out, a->lse,
+                           a->workspace, a->workspace_bytes, a->stream);
+  } else {
+    st = pkv_decode(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
+                    a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B, a->Hq,
+                    a->Hkv, a->head_dim, a->page_size, a->scale, a->out, a->lse, a->workspace,
+                    a->workspace_bytes, a->stream);
+  }
+  if (st != PKV_OK) return st;
+  if (a->event_after_decode) {
+    e = hipEventRecord(static_cast<hipEvent_t>(a->event_after_decode), stream);
+    if (e != hipSuccess) {
+      pkv::set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
+  }
+  if (two)
+    st = pkv_merge(offs_d, slots, a->B, a->Hq, a->Hkv, a->head_dim, a->out, a->lse,
+                   a->workspace, a->workspace_bytes, a->stream);
+  // the slot is free once everything enqueued so far has run
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) {
+    pkv::set_hip_error(static_cast<int>(e));
+    return PKV_ERR_HIP;
+  }
+  s.armed = true;
+  return st;
+}
+
+int pkv_runner_last_plan(const pkv_runner* r, const int32_t** split_offsets,
+                         const int32_t** tasks, int64_t* num_tasks, int32_t* B) {
+  if (!r || !split_offsets || !tasks || !num_tasks || !B) return PKV_ERR_INVALID_ARG;
+  if (!r->last) return PKV_ERR_INVALID_ARG;
+  const Slot& s = *r->last;
+  *split_offsets = s.host;
+  *tasks = s.host + pad4(static_cast<int64_t>(s.B) + 1);
+  *num_tasks = s.T;
+  *B = s.B;
+  return PKV_OK;
+}
+
+}  // extern "C"

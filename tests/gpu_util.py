@@ -44,8 +44,9 @@ def check_lse(got, ref, atol=LSE_ATOL):
         assert err <= atol, f"lse: max abs err {err:.3e}"
 
 
-def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1):
-    """Plan + decode through the C ABI.  Returns (out fp16 tensor, lse tensor|None, decoder)."""
+def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1, two_launch=None):
+    """Plan + decode through the C ABI (fused single launch, or the two-launch
+    decode + merge form).  Returns (out fp16 tensor, lse tensor|None, decoder)."""
     import torch
     import paged_gqa_decode_pkv_amd as pkv
 
@@ -56,11 +57,13 @@ def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1):
     out = torch.full_like(wl.q, float("nan"))
     lse_t = torch.full((wl.q.shape[0], cfg.Hq), float("nan"), dtype=torch.float32,
                        device=wl.q.device) if lse else None
+    # host-side block-table check (what a serving loop does on admission)
+    pkv.pkv_plan(wl.seq_lens_np, cfg.Hkv, wl.block_table_np.shape[1], 0, 1,
+                 block_table=wl.block_table_np, num_pages=wl.k_pool.shape[0])
+    decoder.set_inputs(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, wl.seq_lens_np,
+                       cfg.scale, out, lse_t)
     for _ in range(repeats):
-        decoder.plan(wl.seq_lens_np, mode, param, block_table_h=wl.block_table_np,
-                     num_pages=wl.k_pool.shape[0])
-        decoder.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, cfg.scale,
-                       out=out, lse=lse_t)
+        decoder.run(mode, param, two_launch=two_launch)
     torch.cuda.synchronize()
     return out, lse_t, decoder
 

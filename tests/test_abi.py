@@ -154,9 +154,12 @@ def test_policy_params_and_errors():
 # --------------------------------------------------------------------------- workspace, decode arg checks
 
 def test_workspace_size():
-    assert pkv.pkv_workspace_size(0, 32, 128) == 256
+    hdr = pkv.WORKSPACE_HEADER_BYTES
+    assert pkv.pkv_workspace_size(0, 32, 128) == hdr
     n = pkv.pkv_workspace_size(10, 32, 128)
-    assert n >= 256 + 10 * 32 * 130 * 4 and n % 256 == 0
+    assert n >= hdr + 10 * 32 * 130 * 4 and n % 256 == 0
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    assert re.search(r"#define PKV_WORKSPACE_HEADER_BYTES %d\b" % hdr, text)
 
 
 def test_decode_rejects_bad_scalars_before_touching_the_device():
@@ -174,3 +177,34 @@ def test_decode_rejects_bad_scalars_before_touching_the_device():
     assert call(B=0) == pkv.PKV_OK                           # nothing to do
     assert call(B=1) == pkv.PKV_ERR_INVALID_ARG              # null pointers
     del common
+
+
+def test_step_args_layout_matches_c(tmp_path):
+    """The ctypes mirror of pkv_step_args has the C field offsets and size."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in pkv.pkv_step_args._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "pkv.h"', 'int main(void) {',
+           '  printf("%zu\\n", sizeof(pkv_step_args));']
+    src += [f'  printf("%zu\\n", offsetof(pkv_step_args, {f}));' for f in fields]
+    src += ['  return 0;', '}']
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(pkv.pkv_step_args)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(pkv.pkv_step_args, f).offset == off, f
+
+
+def test_runner_rejects_bad_args_without_device():
+    lib = pkv._load()
+    h = ctypes.c_void_p()
+    assert lib.pkv_runner_create(0, None, 0, ctypes.byref(h)) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_runner_step(None, None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_runner_destroy(None) == pkv.PKV_OK

@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 SEED = HELD_OUT_SEEDS[0]
 
 
-def _parity(wl, mode=None, param=None, rows=None, decoder=None):
+def _parity(wl, mode=None, param=None, rows=None, decoder=None, two_launch=False):
     log_case(wl.cfg.name, "seed", wl.seed, "mode", mode, "param", param,
-             "lens", wl.seq_lens_np.tolist()[:8])
-    out, lse, dec = run_hip(wl, mode, param, decoder=decoder)
+             "two_launch", two_launch, "lens", wl.seq_lens_np.tolist()[:8])
+    out, lse, dec = run_hip(wl, mode, param, decoder=decoder, two_launch=two_launch)
     ref_out, ref_lse = oracle_rows(wl, rows)
     sel = slice(None) if rows is None else list(rows)
     got = out.float().cpu().numpy()[sel]
@@ -31,23 +31,29 @@ def _parity(wl, mode=None, param=None, rows=None, decoder=None):
 
 # --------------------------------------------------------------------------- the five workloads
 
+TWO = [False, True]
+
+
+@pytest.mark.parametrize("two_launch", TWO)
 @pytest.mark.parametrize("S", [1, 4])
 @pytest.mark.parametrize("seed", [CALIBRATION_SEED, SEED])
-def test_tiny(S, seed):
+def test_tiny(S, seed, two_launch):
     wl = make_workload("tiny", seed, device="cuda")
-    _parity(wl, 0, S)
+    _parity(wl, 0, S, two_launch=two_launch)
 
 
+@pytest.mark.parametrize("two_launch", TWO)
 @pytest.mark.parametrize("S", [8, 16, 32, 64, None])
-def test_b1_split_counts(S):
+def test_b1_split_counts(S, two_launch):
     wl = make_workload("b1", SEED, device="cuda")
-    _parity(wl, None if S is None else 0, S)
+    _parity(wl, None if S is None else 0, S, two_launch=two_launch)
 
 
+@pytest.mark.parametrize("two_launch", TWO)
 @pytest.mark.parametrize("name", ["b8_bimodal", "b8_zipf", "b8_uniform"])
-def test_b8_policy(name):
+def test_b8_policy(name, two_launch):
     wl = make_workload(name, SEED, device="cuda")
-    _parity(wl)
+    _parity(wl, two_launch=two_launch)
 
 
 @pytest.mark.parametrize("mode,param", [(0, 4), (0, 64), (1, 1), (1, 16), (1, 256)])
@@ -71,12 +77,13 @@ def b64():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("two_launch", TWO)
 @pytest.mark.parametrize("mode", [None, 0, 1])
-def test_b64_sampled_rows(b64, mode):
+def test_b64_sampled_rows(b64, mode, two_launch):
     """Full-size B=64 batch (34.4 GB pool), oracle on sampled rows."""
     rows = [0, 17, 42, 63]
     param = {None: None, 0: 16, 1: 64}[mode]
-    _parity(b64, mode, param, rows=rows)
+    _parity(b64, mode, param, rows=rows, two_launch=two_launch)
 
 
 # --------------------------------------------------------------------------- edge cases
@@ -86,23 +93,34 @@ def _small_cfg(G=4, D=128, Hkv=2, maxp=8, pool=64):
                   pool_pages=pool, lengths=lambda rng: np.zeros(0))
 
 
+@pytest.mark.parametrize("two_launch", TWO)
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("D", [64, 128])
-def test_ragged_gqa_ratios_and_head_dims(G, D):
+def test_ragged_gqa_ratios_and_head_dims(G, D, two_launch):
     cfg = _small_cfg(G=G, D=D)
     lens = [1, 15, 16, 17, 33, 0, 127, 128]
     for mode, param in [(0, 1), (0, 3), (1, 1), (1, 2)]:
         wl = make_workload(cfg, 7 + G + D, device="cuda", seq_lens=lens)
-        _parity(wl, mode, param)
+        _parity(wl, mode, param, two_launch=two_launch)
 
 
-def test_all_rows_empty():
+@pytest.mark.parametrize("two_launch", TWO)
+def test_all_rows_empty(two_launch):
     cfg = _small_cfg()
     wl = make_workload(cfg, 3, device="cuda", seq_lens=[0, 0, 0])
-    out, lse, dec = run_hip(wl, 0, 4)
+    out, lse, dec = run_hip(wl, 0, 4, two_launch=two_launch)
     assert np.all(out.float().cpu().numpy() == 0)
     assert np.all(np.isneginf(lse.cpu().numpy()))
     assert dec.error_flags() == 0
+
+
+def test_fused_and_two_launch_agree():
+    """Same arithmetic in both schedules: bit-identical outputs."""
+    wl = make_workload("b8_bimodal", CALIBRATION_SEED, device="cuda")
+    a, la, _ = run_hip(wl, 1, 8)
+    b, lb, _ = run_hip(wl, 1, 8, two_launch=True)
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+    assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy())
 
 
 def test_full_rows_at_max_pages():
@@ -142,11 +160,14 @@ def test_page_relabelling_bit_identical():
 
 
 def test_repeated_launches_deterministic_and_counter_reset():
-    """Many back-to-back steps on one workspace: the self-resetting task counter
-    must hand out every task each time, and results are bit-identical."""
+    """Many back-to-back steps on one workspace: the self-resetting task and
+    arrival counters must work every time, and results are bit-identical."""
     wl = make_workload("b8_uniform", SEED, device="cuda")
     a, la, dec = run_hip(wl, 1, 2)
     b, lb, _ = run_hip(wl, 1, 2, decoder=dec, repeats=5)
+    c, lc, _ = run_hip(wl, 0, 16, decoder=dec, repeats=3)
+    d, ld, _ = run_hip(wl, 1, 2, decoder=dec, repeats=2)
+    assert np.array_equal(a.cpu().numpy(), d.cpu().numpy())
     assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
     assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy())
     ref_out, _ = oracle_rows(wl)
@@ -167,7 +188,8 @@ def test_task_list_readback_bit_exact():
     import oracle
     wl = make_workload("b8_bimodal", SEED, device="cuda")
     _, _, dec = run_hip(wl, 1, 16)
-    mode, param, T, nslots, B = dec.last
+    mode, param, T, nslots, B, two = dec.last
     rt, ro = oracle.plan_tasks(wl.seq_lens_np, wl.cfg.Hkv, 16, mode, param)
-    assert np.array_equal(dec.tasks_d[:T].cpu().numpy(), rt)
-    assert np.array_equal(dec.offs_d[:B + 1].cpu().numpy(), ro)
+    tasks, offs = dec.plan_arrays()       # the memory the kernels read
+    assert np.array_equal(tasks, rt)
+    assert np.array_equal(offs, ro)
