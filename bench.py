@@ -43,15 +43,18 @@ def _kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kv_bytes_per_launch):
+def _traffic(config):
     """Measured HBM bytes per decode launch from the committed rocprofv3 PMC
-    runs, if they were taken on the current kernel source; else None."""
+    runs, if they were taken on the current kernel source and on this same
+    workload and schedule; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != _kernel_source_hash():
+        return None
+    if rec.get("config") != config:
         return None
     return rec.get("bytes_per_launch")
 
@@ -105,6 +108,11 @@ def main():
                     help="KV copies rotated over (default: enough for >= 2 GiB between reuses)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the HIP event pair around the decode kernel on every n-th "
+                         "timed step (each pair adds a few microseconds of queue time)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (scales PMC byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,6 +129,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}), flush=True)
+        return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda")
     print(f"[bench] drawing {cfg.name} seed {args.seed}", file=sys.stderr, flush=True)
@@ -151,6 +169,8 @@ def main():
     def step(i, ev=None):
         decs[i % L].run(args.mode, args.param, stream=stream, events=ev)
 
+    every = max(1, args.event_every)
+
     print(f"[bench] warmup {args.warmup} steps, {L} layer copies", file=sys.stderr, flush=True)
     for i in range(max(args.warmup, L)):
         step(i)
@@ -161,14 +181,14 @@ def main():
 
     K = args.steps
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(K)]
+              for _ in range((K + every - 1) // every)]
     for e0, e1 in events:     # creates the underlying HIP events
         e0.record()
         e1.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, events[i])
+        step(i, events[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
@@ -177,6 +197,7 @@ def main():
     wall = t1 - t0
     dec_ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
     mode, param, T, nslots = dec.last[:4]
+    two_launch = bool(dec.last[5])
     avg_dec_s = float(dec_ms.mean()) * 1e-3
     achieved = kv_bytes / avg_dec_s / 1e9
     ms_per_step = wall / K * 1e3
@@ -203,8 +224,10 @@ def main():
             "workload": cfg.name, "seed": args.seed, "B": B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
             "head_dim": cfg.D, "page_size": 16, "seq_lens": sl_h.tolist(),
             "kv_bytes_per_step": kv_bytes, "mode": ["split", "workqueue"][mode], "param": param,
-            "tasks": T, "layers_rotated": L, "launches_per_step": 2,
-            "step": "policy + plan (host C++) + task-list H2D + decode kernel + merge kernel",
+            "tasks": T, "layers_rotated": L, "launches_per_step": 2 if two_launch else 1,
+            "merge": "separate merge kernel" if two_launch else "fused into the decode kernel",
+            "step": "policy + plan (host C++, read in place by the kernel from pinned memory) "
+                    "+ decode kernel (+ merge kernel in the two-launch form)",
         },
         "kv_gbps_step": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "gpu_us": {
@@ -218,8 +241,11 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": _traffic(kv_bytes),
-            "kernel": "pkv_decode_kernel<128>",
+            "traffic": _traffic({"workload": cfg.name, "seed": args.seed,
+                                 "mode": ["split", "workqueue"][mode], "param": param,
+                                 "merge": "two-launch" if two_launch else "fused"}),
+            "kernel": "pkv_decode_kernel<128, true>",
+            "event_timed_steps": len(events),
             "algorithmic_bytes_per_launch": kv_bytes,
             "extras_bytes_per_launch": extras,
         },
