@@ -227,110 +227,100 @@ struct MergeArgs {
 //   out = sum_s w_s o_s / sum_s w_s l_s,  lse = (M + log2 sum_s w_s l_s) ln 2.
 // One workgroup merges the G heads of one (row, KV head), whose partial
 // outputs are contiguous (G*D floats per slot), over slots o0 .. o0+S-1.
-//   pass 1: M per head.  Thread t strides over (slot, head) pairs with head
-//           t % G, then a wave reduction and an LDS reduction over waves.
-//   pass 2: wave w sums slots w, w+4, ...  Lane owns float4 columns lane,
-//           lane+64, ... of the group.  The 4 wave sums are added in LDS.
-// `lds` holds kMergeLdsFloats floats.  All threads of the workgroup call it.
-template <int D>
-constexpr int merge_lds_floats() {
-  return kWaves * kMaxG * 2 + kWaves * (kMaxG * D / 4) * 4;
-}
+// Thread t owns float4 column t % C of the group (C = G*D/4) and the slots
+// r, r+R, r+2R, ... with r = t / C and R = 256 / C.  It folds its slots into
+// a running (max, sum, vector) state kB slots at a time, so kB loads per
+// thread are in flight together; the R states of a column are then combined
+// in LDS.  The result is the same maximum and the same sums as the two-pass
+// form, up to the order of the additions.
+// Slots in flight per thread in the merge.  Every merge (fused or not) uses
+// the same value, so both forms add the states in the same order.
+constexpr int kMergeBatch = 8;
 
 template <int D>
+constexpr int merge_lds_floats() {
+  return kThreads * 6;
+}
+
+template <int D, int kB>
 __device__ void merge_group(const MergeArgs& a, int b, int g, int o0, int S, float* lds) {
-  constexpr int kCols = kMaxG * D / 4;              // float4 columns, largest group
-  constexpr int kPerLane = (kCols + 63) / 64;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G;
+  const int cols = G * (D / 4);          // <= kThreads, since G <= kMaxG
+  const int R = kThreads / cols;
+  const int r = tid / cols;
+  const int c = tid - r * cols;
+  const int h = (4 * c) / D;
   const int64_t head0 = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G;
-  float (*s_Mw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(lds);
-  float (*s_L)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(lds + kWaves * kMaxG);
-  floatx4 (*s_O)[kCols] = reinterpret_cast<floatx4 (*)[kCols]>(lds + 2 * kWaves * kMaxG);
+  float* s_M = lds;
+  float* s_L = lds + kThreads;
+  floatx4* s_O = reinterpret_cast<floatx4*>(lds + 2 * kThreads);
 
   // Coherent (L2-bypassing) loads: the states may come from other XCDs.
   const __amdgpu_buffer_rsrc_t ml_rsrc = make_rsrc(
       a.part_ml + static_cast<int64_t>(o0) * a.Hq, static_cast<uint32_t>(S) * a.Hq * 8u);
   const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
       a.part_o + static_cast<int64_t>(o0) * a.Hq * D, static_cast<uint32_t>(S) * a.Hq * D * 4u);
-  auto load_ml = [&](int sl, int h) -> float2 {
-    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-        ml_rsrc, 8 * (sl * a.Hq + g * G + h), 0, kCoherent));
-  };
+  const int ml_off = 8 * (g * G + h);
+  const int o_off = 4 * (g * G * D + 4 * c);
 
-  // pass 1: maximum of m over the splits, per head
-  {
-    float v = -INFINITY;
-    for (int i = tid; i < S * G; i += kThreads) {
-      const int sl = i / G;
-      const int h = i - sl * G;   // == tid % G, since kThreads % G == 0
-      v = fmaxf(v, load_ml(sl, h).x);
+  float M = -INFINITY, L = 0.f;
+  floatx4 O = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (r < R) {
+    for (int base = r; base < S; base += R * kB) {
+      float2 ml[kB];
+      floatx4 o[kB];
+      // Slot indices are clamped so every load is unconditional; clamped
+      // slots get weight 0 below.
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int sl = min(base + R * k, S - 1);
+        ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+            ml_rsrc, 8 * sl * a.Hq + ml_off, 0, kCoherent));
+        o[k] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+            o_rsrc, 4 * sl * a.Hq * D + o_off, 0, kCoherent));
+      }
+      __builtin_amdgcn_sched_barrier(0);   // all 2*kB loads issue before the first wait
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (base + R * k < S) Mn = fmaxf(Mn, ml[k].x);
+      const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+      O *= f;
+      L *= f;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const bool live = base + R * k < S && ml[k].x != -INFINITY;
+        const float w = live ? fast_exp2(ml[k].x - Mn) : 0.f;
+        O += w * o[k];
+        L += w * ml[k].y;
+      }
+      M = Mn;
     }
-    for (int off = 32; off >= G; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if (lane < G) s_Mw[wave][lane] = v;
   }
+  s_M[tid] = M;
+  s_L[tid] = L;
+  s_O[tid] = O;
   __syncthreads();
 
-  // pass 2: weighted sums
-  const int cols = G * D / 4;
-  float Mh[kPerLane];
-  floatx4 O[kPerLane];
-  float L[kPerLane];
-#pragma unroll
-  for (int j = 0; j < kPerLane; ++j) {
-    const int c = lane + 64 * j;
-    const int h = (c < cols) ? (4 * c) / D : 0;
-    Mh[j] = fmaxf(fmaxf(s_Mw[0][h], s_Mw[1][h]), fmaxf(s_Mw[2][h], s_Mw[3][h]));
-    O[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    L[j] = 0.f;
-  }
-  // Column indices are clamped so every load is unconditional (a
-  // conditional load would make the loop wait on each slot in turn);
-  // clamped columns are dropped when the sums are stored.
-  int cj[kPerLane], hj[kPerLane];
-#pragma unroll
-  for (int j = 0; j < kPerLane; ++j) {
-    cj[j] = (lane + 64 * j < cols) ? lane + 64 * j : lane;
-    hj[j] = (4 * cj[j]) / D;
-  }
-#pragma unroll 4
-  for (int sl = wave; sl < S; sl += kWaves) {
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-      const float2 ml = load_ml(sl, hj[j]);
-      const floatx4 o = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-          o_rsrc, 4 * ((sl * a.Hq + g * G) * D + 4 * cj[j]), 0, kCoherent));
-      const float w = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - Mh[j]);
-      O[j] += w * o;
-      L[j] += w * ml.y;   // used by the lane whose column starts head h
+  if (tid < cols) {
+    float Mt = -INFINITY;
+    for (int j = 0; j < R; ++j) Mt = fmaxf(Mt, s_M[tid + j * cols]);
+    float Lt = 0.f;
+    floatx4 Ot = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < R; ++j) {
+      const float mj = s_M[tid + j * cols];
+      const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mt);
+      Lt += w * s_L[tid + j * cols];
+      Ot += w * s_O[tid + j * cols];
     }
-  }
-#pragma unroll
-  for (int j = 0; j < kPerLane; ++j) {
-    const int c = lane + 64 * j;
-    if (c < cols) {
-      s_O[wave][c] = O[j];
-      if ((4 * c) % D == 0) s_L[wave][(4 * c) / D] = L[j];
-    }
-  }
-  __syncthreads();
-
-  for (int c = tid; c < cols; c += kThreads) {
-    const int h = (4 * c) / D;
-    const floatx4 o = s_O[0][c] + s_O[1][c] + s_O[2][c] + s_O[3][c];
-    const float Lh = (s_L[0][h] + s_L[1][h]) + (s_L[2][h] + s_L[3][h]);
-    const float inv = 1.f / Lh;
+    const float inv = 1.f / Lt;
     _Float16* dst = a.out + head0 * D + 4 * c;
-    dst[0] = static_cast<_Float16>(o[0] * inv);
-    dst[1] = static_cast<_Float16>(o[1] * inv);
-    dst[2] = static_cast<_Float16>(o[2] * inv);
-    dst[3] = static_cast<_Float16>(o[3] * inv);
-    if ((4 * c) % D == 0 && a.lse) {
-      const float M = fmaxf(fmaxf(s_Mw[0][h], s_Mw[1][h]), fmaxf(s_Mw[2][h], s_Mw[3][h]));
-      a.lse[head0 + h] = (M + __log2f(Lh)) * kLn2;
-    }
+    dst[0] = static_cast<_Float16>(Ot[0] * inv);
+    dst[1] = static_cast<_Float16>(Ot[1] * inv);
+    dst[2] = static_cast<_Float16>(Ot[2] * inv);
+    dst[3] = static_cast<_Float16>(Ot[3] * inv);
+    if ((4 * c) % D == 0 && a.lse) a.lse[head0 + h] = (Mt + __log2f(Lt)) * kLn2;
   }
 }
 
@@ -348,6 +338,9 @@ __device__ __forceinline__ void write_empty_group(const MergeArgs& a, int b, int
 // LDS once per workgroup.  Larger batches read them with scalar loads.
 constexpr int kRowStage = 1024;
 constexpr int kRing = 4;   // page tiles in flight per wave (one "round")
+// Split tasks of a workgroup whose arrival is deferred: they are counted in
+// together when the workgroup runs out of tasks or holds kMaxDone of them.
+constexpr int kMaxDone = 64;
 
 // Everything the workgroup needs to know about one task.  All fields are
 // wave-uniform and live in SGPRs.
@@ -367,11 +360,16 @@ struct Meta {
 // flagged in the error word and leaves ok = false (all pages disabled).
 // The read-only inputs arrive as restrict pointers, so uniform loads from
 // them are scalar (SMEM) loads, whose waits never cover vector page loads.
+// The record of task t (a scalar load), or zeros past the end of the list.
+__device__ __forceinline__ int4 load_record(const DecodeArgs& a, const int4* __restrict__ tasks,
+                                            int t) {
+  return t < a.num_tasks ? tasks[t] : int4{0, 0, 0, 0};
+}
+
 template <bool kStaged>
-__device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __restrict__ tasks,
-                                          const int32_t* __restrict__ seq_lens,
-                                          const int32_t* __restrict__ offs, const int* s_len,
-                                          const int* s_off, int t) {
+__device__ __forceinline__ Meta decode_meta(const DecodeArgs& a, const int32_t* __restrict__ seq_lens,
+                                            const int32_t* __restrict__ offs, const int* s_len,
+                                            const int* s_off, int t, int4 rec) {
   Meta m;
   m.t = t;
   m.b = m.g = m.N = m.p0 = m.p1 = m.Sb = m.o0 = 0;
@@ -379,7 +377,6 @@ __device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __res
   m.rounds = 1;
   m.ok = false;
   if (t >= a.num_tasks) return m;
-  const int4 rec = tasks[t];
   const int b = __builtin_amdgcn_readfirstlane(rec.x);
   const int g = __builtin_amdgcn_readfirstlane(rec.y);
   const int s = __builtin_amdgcn_readfirstlane(rec.z);
@@ -432,6 +429,40 @@ __device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __res
   return m;
 }
 
+template <bool kStaged>
+__device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __restrict__ tasks,
+                                          const int32_t* __restrict__ seq_lens,
+                                          const int32_t* __restrict__ offs, const int* s_len,
+                                          const int* s_off, int t) {
+  return decode_meta<kStaged>(a, seq_lens, offs, s_len, s_off, t, load_record(a, tasks, t));
+}
+
+// Count in n deferred split tasks (row, KV head, first slot, splits) of this
+// workgroup: one wait for all of its write-through partial stores, one
+// arrival per task (in parallel), then the workgroup merges, one after
+// another, the groups whose last split it holds.  All threads call it.
+template <int D, int kB>
+__device__ __forceinline__ void flush_done(const DecodeArgs& a, const MergeArgs& ma, int n,
+                                        const int4* s_done, int* s_lastf, float* scratch) {
+  const int tid = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid < n) {
+    const int4 d = s_done[tid];
+    uint32_t* cnt = a.arrive + static_cast<int64_t>(d.x) * a.Hkv + d.y;
+    s_lastf[tid] = (atomicAdd(cnt, 1u) + 1u == static_cast<uint32_t>(d.w)) ? 1 : 0;
+  }
+  __syncthreads();
+  for (int i = 0; i < n; ++i) {
+    if (s_lastf[i]) {
+      const int4 d = s_done[i];
+      merge_group<D, kB>(ma, d.x, d.y, d.z, d.w, scratch);
+      if (tid == 0) atomicExch(a.arrive + static_cast<int64_t>(d.x) * a.Hkv + d.y, 0u);
+      __syncthreads();   // the scratch is reused by the next merge
+    }
+  }
+}
+
 // Block-table entries of round j of task m for this wave: position 4j+r is
 // page p0 + wave + 16j + 4r.  Positions past the range read a clamped,
 // in-row entry that issue() never uses (it re-checks page < p1).  No select
@@ -476,14 +507,33 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ float s_m[2][kWaves][16];
   __shared__ float s_l[2][kWaves][16];
   __shared__ __attribute__((aligned(16))) float s_o[2][kWaves][kMaxG][LDS_STRIDE];
-  __shared__ int s_last;
+  __shared__ int4 s_done[kMaxDone];   // (row, KV head, first slot, splits)
+  __shared__ int s_lastf[kMaxDone];
   static_assert(kWaves * kMaxG * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
 
   const MergeArgs ma{a.split_offsets, a.num_slots, a.B, a.Hq, a.Hkv, a.G,
                      a.part_o, a.part_ml, a.out, a.lse, a.ctrl};
+  // Staging loads first (vector), then the first task record (scalar), then
+  // the LDS stores: the two load latencies overlap instead of adding up.
+  int4 rec0;
   if constexpr (kStaged) {
-    for (int i = tid; i < a.B; i += kThreads) s_len[i] = seq_lens_in[i];
-    for (int i = tid; i <= a.B; i += kThreads) s_off[i] = offs_in[i];
+    constexpr int kPer = (kRowStage + kThreads) / kThreads;   // covers B+1 <= kRowStage+1
+    int lv[kPer], ov[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      lv[k] = i < a.B ? seq_lens_in[i] : 0;
+      ov[k] = i <= a.B ? offs_in[i] : 0;
+    }
+    rec0 = load_record(a, tasks_in, blockIdx.x);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < a.B) s_len[i] = lv[k];
+      if (i <= a.B) s_off[i] = ov[k];
+    }
+  } else {
+    rec0 = load_record(a, tasks_in, blockIdx.x);
   }
   __syncthreads();
   if (a.fuse) {
@@ -535,7 +585,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   };
 
   // ---- prologue: task 0 = blockIdx.x, task 1 = blockIdx.x + gridDim.x
-  Meta cur = load_meta<kStaged>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, blockIdx.x);
+  Meta cur = decode_meta<kStaged>(a, seq_lens_in, offs_in, s_len, s_off, blockIdx.x, rec0);
   int t_nxt = blockIdx.x + gridDim.x;
   PageRegs<D> ring[kRing];
   bool valid[kRing];
@@ -551,6 +601,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   }
   __syncthreads();
 
+  int n_done = 0;   // entries of s_done (workgroup-uniform)
   for (int it = 0; cur.t < a.num_tasks; ++it) {
     const int par = it & 1;
     // next task's metadata, its first round of table entries and its q;
@@ -647,26 +698,21 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
         }
       }
       if (a.fuse && !direct) {
-        // Fused merge.  Each thread waits until its write-through stores are
-        // acknowledged, the workgroup then counts this split in, and the
-        // last split of the (row, KV head) merges the group with coherent
-        // loads.  No L2 write-back or invalidate is needed.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) {
-          uint32_t* cnt = a.arrive + static_cast<int64_t>(cur.b) * a.Hkv + cur.g;
-          s_last = (atomicAdd(cnt, 1u) + 1u == static_cast<uint32_t>(cur.Sb)) ? 1 : 0;
-        }
-        __syncthreads();
-        if (s_last) {
-          merge_group<D>(ma, cur.b, cur.g, cur.o0, cur.Sb, &s_o[par][0][0][0]);
-          if (tid == 0) atomicExch(a.arrive + static_cast<int64_t>(cur.b) * a.Hkv + cur.g, 0u);
+        // Fused merge, deferred: the split is counted in later, so waiting
+        // for its stores does not also wait for the page loads of the tasks
+        // behind it.
+        if (tid == 0) s_done[n_done] = int4{cur.b, cur.g, cur.o0, cur.Sb};
+        if (++n_done == kMaxDone) {
+          flush_done<D, kMergeBatch>(a, ma, n_done, s_done, s_lastf, &s_o[par][0][0][0]);
+          n_done = 0;
         }
       }
     }
     t_nxt = __builtin_amdgcn_readfirstlane(s_next[par]);
     cur = nxt;
   }
+
+  if (n_done > 0) flush_done<D, kMergeBatch>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0][0]);
 
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
@@ -692,7 +738,7 @@ __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
     write_empty_group<D>(a, b, g);
     return;
   }
-  merge_group<D>(a, b, g, o0, S, lds);
+  merge_group<D, kMergeBatch>(a, b, g, o0, S, lds);
 }
 
 // ---------------------------------------------------------------------------
