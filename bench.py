@@ -226,7 +226,8 @@ def main():
             "kv_bytes_per_step": kv_bytes, "mode": ["split", "workqueue"][mode], "param": param,
             "tasks": T, "layers_rotated": L, "launches_per_step": 2 if two_launch else 1,
             "merge": "separate merge kernel" if two_launch else "fused into the decode kernel",
-            "step": "policy + plan (host C++, read in place by the kernel from pinned memory) "
+            "step": "policy + plan (host C++; a changed plan is read from pinned memory, a repeated "
+                    "one from the runner's device copy) "
                     "+ decode kernel (+ merge kernel in the two-launch form)",
         },
         "kv_gbps_step": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),

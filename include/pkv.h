@@ -298,19 +298,25 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
 
 /*
  * Step runner -- the whole hot path of one decode step in one call:
- * policy, host plan, a single async upload of the plan, then the decode
- * kernel and the merge kernel on the caller's stream.
+ * policy, host plan, then the decode kernel and the merge kernel on the
+ * caller's stream.
  *
  * Source: gist.science explainer, "2. Calibrated Adaptive Policy" and
  * Methodologie ("Row-Local Bounds", "Compact Workqueue").  "Evaluatieprotocol"
  * counts host planning in the synchronized wall time of a step.
  *
- * A runner owns host resources only: a ring of pinned plan buffers, each
- * guarded by a HIP event recorded after the merge kernel, so it never
- * rewrites a plan that enqueued kernels still read.  The kernels read the
- * plan in place from pinned host memory (the host-to-device boundary of the
- * step; 16 bytes per task).  Device memory belongs to the caller.  One
- * runner serves one thread at a time.
+ * A runner owns a ring of pinned plan buffers, each guarded by a HIP event
+ * recorded after the merge kernel, so it never rewrites a plan that
+ * enqueued kernels still read, plus one device buffer and a side stream
+ * (default priority) for a device copy of the last distinct plan.  When a
+ * step's plan differs from the previous distinct plan, its kernels read it
+ * in place from pinned host memory (16 bytes per task) and the plan is
+ * uploaded on the side stream; a later step with the same plan reads the
+ * device copy (the caller's stream waits for the upload).  Other device
+ * memory belongs to the caller.  One runner serves one thread at a time and
+ * the device that was current when it was created (on another device it
+ * always reads the pinned plan).  A stream passed to a step must stay valid
+ * until pkv_runner_destroy returns.
  */
 typedef struct pkv_runner pkv_runner;
 
@@ -375,8 +381,8 @@ int pkv_runner_step(pkv_runner* runner, pkv_step_args* args);
 int pkv_runner_last_plan(const pkv_runner* runner, const int32_t** split_offsets,
                          const int32_t** tasks, int64_t* num_tasks, int32_t* B);
 
-/* Wait for the kernels that read the runner's plans, then free its
- * resources.  NULL is a no-op. */
+/* Wait for the kernels and uploads that use the runner's plans, then free
+ * its resources.  NULL is a no-op. */
 int pkv_runner_destroy(pkv_runner* runner);
 
 #ifdef __cplusplus

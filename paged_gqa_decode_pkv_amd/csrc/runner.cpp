@@ -7,12 +7,15 @@
 // Methodologie ("Row-Local Bounds", "Compact Workqueue").  Host planning is
 // part of the step, and the "Evaluatieprotocol" wall timing includes it.
 //
-// The runner owns host resources only: a ring of pinned plan buffers, each
-// guarded by a HIP event, so a slot is rewritten only after the kernels that
-// read it have completed.  The kernels read the plan in place from pinned
-// host memory (16 bytes per task, read once).  A small DMA copy would cost
-// more on the device timeline than the whole read.  Device memory
-// (workspace) belongs to the caller.
+// The runner owns a ring of pinned plan buffers, each guarded by a HIP event,
+// so a slot is rewritten only after the kernels that read it have completed.
+// A step whose plan differs from the previous one is read by its kernels in
+// place from pinned host memory (16 bytes per task); the plan is also copied
+// to a runner-owned device buffer on a side stream.  Later steps with the
+// same plan (the steady state of decoding, where a row's task records only
+// change when it crosses a chunk boundary) read that device copy, which
+// removes a host-memory round trip from the start of every workgroup.  The
+// remaining device memory (workspace) belongs to the caller.
 
 #include <hip/hip_runtime_api.h>
 
@@ -46,7 +49,70 @@ struct pkv_runner {
   std::vector<Slot> ring;
   size_t next = 0;
   Slot* last = nullptr;
+  // device copy of the last distinct plan
+  int device = -1;                 // device of `dplan`
+  hipStream_t side = nullptr;      // stream of the uploads
+  int32_t* dplan = nullptr;
+  size_t dplan_bytes = 0;          // capacity
+  std::vector<int32_t> shadow;     // what dplan holds (or will hold)
+  bool shadow_valid = false;
+  Slot* upload_src = nullptr;      // slot the pending upload reads
+  hipEvent_t uploaded = nullptr;   // recorded on `side` after the upload
+  uint64_t upload_seq = 0;         // uploads started so far
+  uint64_t waited_seq = 0;         // upload that `waited_stream` has waited for
+  hipStream_t waited_stream = nullptr;
+  hipStream_t reader_stream = nullptr;  // stream of the last kernels that read dplan
+  bool have_reader = false;
+  hipEvent_t readers_done = nullptr;    // recorded on reader_stream before an upload
 };
+
+namespace {
+
+int hip_fail(hipError_t e) {
+  pkv::set_hip_error(static_cast<int>(e));
+  return PKV_ERR_HIP;
+}
+
+// Start copying the plan in `s` (words int32) to the device buffer on the
+// side stream, after every kernel enqueued so far on the stream that last
+// read the old copy.
+int upload_plan(pkv_runner* r, Slot& s, size_t words) {
+  const size_t bytes = words * sizeof(int32_t);
+  hipError_t e = hipSuccess;
+  r->shadow_valid = false;
+  if (r->have_reader) {
+    e = hipEventRecord(r->readers_done, r->reader_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(r->side, r->readers_done, 0);
+    if (e != hipSuccess) return hip_fail(e);
+    r->have_reader = false;
+  }
+  if (r->dplan_bytes < bytes) {
+    if (r->dplan) {
+      e = hipStreamSynchronize(r->side);
+      if (e != hipSuccess) return hip_fail(e);
+      hipFree(r->dplan);
+      r->dplan = nullptr;
+      r->dplan_bytes = 0;
+    }
+    const size_t want = bytes < 4096 ? 4096 : bytes + bytes / 4;
+    e = hipMalloc(reinterpret_cast<void**>(&r->dplan), want);
+    if (e != hipSuccess) {
+      r->dplan = nullptr;
+      return hip_fail(e);
+    }
+    r->dplan_bytes = want;
+  }
+  e = hipMemcpyAsync(r->dplan, s.host, bytes, hipMemcpyHostToDevice, r->side);
+  if (e == hipSuccess) e = hipEventRecord(r->uploaded, r->side);
+  if (e != hipSuccess) return hip_fail(e);
+  r->shadow.assign(s.host, s.host + words);
+  r->shadow_valid = true;
+  r->upload_src = &s;
+  ++r->upload_seq;
+  return PKV_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -72,6 +138,17 @@ int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t 
     pkv_policy_defaults(&r->params);
   }
   r->ring.resize(static_cast<size_t>(ring_depth));
+  {
+    hipError_t e = hipGetDevice(&r->device);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r->uploaded, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r->readers_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pkv::set_hip_error(static_cast<int>(e));
+      pkv_runner_destroy(r);
+      return PKV_ERR_HIP;
+    }
+  }
   for (Slot& s : r->ring) {
     hipError_t e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -87,6 +164,17 @@ int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t 
 int pkv_runner_destroy(pkv_runner* r) {
   if (!r) return PKV_OK;
   int st = PKV_OK;
+  if (r->readers_done) {
+    if (r->have_reader && hipEventRecord(r->readers_done, r->reader_stream) == hipSuccess)
+      hipEventSynchronize(r->readers_done);
+    hipEventDestroy(r->readers_done);
+  }
+  if (r->side) {
+    hipStreamSynchronize(r->side);
+    hipStreamDestroy(r->side);
+  }
+  if (r->uploaded) hipEventDestroy(r->uploaded);
+  if (r->dplan && hipFree(r->dplan) != hipSuccess) st = PKV_ERR_HIP;
   for (Slot& s : r->ring) {
     if (s.done) {
       if (s.armed) hipEventSynchronize(s.done);
@@ -140,6 +228,12 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
       return PKV_ERR_HIP;
     }
   }
+  if (r->upload_src == &s) {
+    // the pending upload reads this slot
+    e = hipEventSynchronize(r->uploaded);
+    r->upload_src = nullptr;
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (s.bytes < plan_bytes) {
     if (s.host) hipHostFree(s.host);
     s.host = s.dev = nullptr;
@@ -173,6 +267,27 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   r->last = &s;
   const int32_t* offs_d = s.dev;
   const int32_t* tasks_d = s.dev + off_words;
+
+  // The device copy serves this step if it holds the same plan; otherwise
+  // the kernels read the pinned slot and the new plan is uploaded for the
+  // steps after this one.
+  const size_t words = off_words + 4 * static_cast<size_t>(T);
+  int dev = -1;
+  bool use_dev = false;
+  if (hipGetDevice(&dev) == hipSuccess && dev == r->device) {
+    if (r->shadow_valid && r->shadow.size() == words &&
+        std::memcmp(r->shadow.data(), s.host, words * sizeof(int32_t)) == 0) {
+      if (r->waited_seq != r->upload_seq || r->waited_stream != stream) {
+        e = hipStreamWaitEvent(stream, r->uploaded, 0);
+        if (e != hipSuccess) return hip_fail(e);
+        r->waited_seq = r->upload_seq;
+        r->waited_stream = stream;
+      }
+      use_dev = true;
+      offs_d = r->dplan;
+      tasks_d = r->dplan + off_words;
+    }
+  }
 
   // the decode kernel (merge fused in), or decode then merge kernel
   if (a->event_before_decode) {
@@ -211,6 +326,12 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
     return PKV_ERR_HIP;
   }
   s.armed = true;
+  if (use_dev) {
+    r->reader_stream = stream;
+    r->have_reader = true;
+  } else if (st == PKV_OK && dev == r->device) {
+    st = upload_plan(r, s, words);
+  }
   return st;
 }
 

@@ -174,6 +174,30 @@ def test_repeated_launches_deterministic_and_counter_reset():
     check_close(b.float().cpu().numpy(), ref_out)
 
 
+def test_plan_device_copy_reuse_and_switch():
+    """One runner over steps whose plans repeat and change.  A repeated plan is
+    read from the runner's device copy, a changed one from pinned host memory
+    while its copy is uploaded; both give the bits of a fresh runner."""
+    import torch
+    wls = [make_workload("b8_bimodal", s, device="cuda") for s in HELD_OUT_SEEDS[:2]]
+    steps = [(0, 1, 16), (0, 1, 16), (0, 1, 16), (0, 0, 8), (0, 1, 16), (1, 1, 16), (1, 1, 16),
+             (0, 0, 8), (0, 0, 8), (1, 1, 64), (0, 1, 64), (0, 1, 64)]
+    fresh = {}
+    for w, mode, param in sorted(set(steps)):
+        out, lse, _ = run_hip(wls[w], mode, param)
+        fresh[(w, mode, param)] = (out.cpu().numpy(), lse.cpu().numpy())
+    dec = None
+    for w, mode, param in steps:
+        log_case("plan copy step", "seed", wls[w].seed, "mode", mode, "param", param)
+        out, lse, dec = run_hip(wls[w], mode, param, decoder=dec)
+        assert np.array_equal(out.cpu().numpy(), fresh[(w, mode, param)][0])
+        assert np.array_equal(lse.cpu().numpy(), fresh[(w, mode, param)][1])
+        assert dec.error_flags() == 0
+    torch.cuda.synchronize()
+    ref_out, _ = oracle_rows(wls[0])
+    check_close(fresh[(0, 1, 16)][0].astype(np.float64), ref_out)
+
+
 def test_split_counts_agree():
     wl = make_workload("b1", CALIBRATION_SEED, device="cuda")
     lses = []
