@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* Fixed-size head of every workspace: control words (task counter, exit
  * counter, error word) and the per-(row, KV head) arrival counters of the
@@ -82,18 +82,27 @@ enum pkv_device_error {
   PKV_DEVERR_SLOT = 8u         /* split_offsets points outside the partial-state slots */
 };
 
-/* Policy constants.  The pages print no thresholds.  These are this
- * library's own calibration; see pkv_policy. */
+/* Policy constants: the candidate sets and the cost model (see pkv_policy).
+ * The pages print no thresholds.  The defaults are this library's own fit on
+ * the calibration seed (see pkv_policy_defaults). */
 typedef struct pkv_policy_params {
-  float tasks_per_cu;   /* target task count T* = tasks_per_cu * num_cus */
-  int32_t chunk_min;    /* workqueue chunk bounds, in pages */
-  int32_t chunk_max;
-  int32_t split_max;    /* split-mode cap on S */
-  float uniform_ratio;  /* lengths within this max/min ratio count as uniform */
-  int32_t fuse_max_splits; /* step runner: the fused single launch when no row
-                              has more splits than this, else the two-launch
-                              form (the fused merge runs at the tail of a split
-                              group, so long groups favour the separate merge) */
+  int32_t split_max;        /* split candidates S = 1, 2, 4, ... <= split_max */
+  int32_t chunk_min;        /* workqueue candidates c = chunk_min, 2 chunk_min, ... */
+  int32_t chunk_max;        /*   ... <= chunk_max, in pages */
+  int32_t fuse_max_splits;  /* step runner: the fused single launch when no row
+                               has more splits than this, else the two-launch
+                               form (the fused merge runs at the tail of a
+                               split group, so long groups favour the separate
+                               merge kernel) */
+  /* cost model of one step (microseconds, GB/s) */
+  double t0_us;             /* fixed time of a step */
+  double t_round_us;        /* per round of tasks, ceil(T / W) */
+  double alpha;             /* dynamic-queue imbalance, in largest tasks */
+  double cu_gbps;           /* streaming rate of one CU */
+  double hbm_gbps;          /* streaming rate of the chip */
+  double t_two_us;          /* extra fixed time of the two-launch form */
+  double t_two_split_us;    /* two-launch: per split of the deepest row */
+  double t_fused_split_us;  /* fused merge: per split of the deepest row */
 } pkv_policy_params;
 
 /* ABI version (PKV_ABI_VERSION of the built library). */
@@ -105,38 +114,65 @@ const char* pkv_status_string(int status);
 /* hipError_t of the last PKV_ERR_HIP returned on this thread (0 if none). */
 int pkv_last_hip_error(void);
 
-/* Fill *params with the default policy constants.  Returns PKV_ERR_INVALID_ARG
- * if params is NULL. */
+/* Fill *params with the default policy constants: split_max 256, chunks
+ * 4..256, fuse_max_splits 16, and the cost model fitted on seed 20260622 of
+ * the calibration traces on one MI355X (256 CUs): every candidate schedule of
+ * eight trace families (B = 1 fixed and bucketed, 4, 8 bimodal / Zipf /
+ * uniform, 32, 64) timed on the GPU, least squares on log time.  Returns
+ * PKV_ERR_INVALID_ARG if params is NULL. */
 int pkv_policy_defaults(pkv_policy_params* params);
 
 /*
  * pkv_policy -- choose the scheduling mode and its parameter for one step.
  * Host only and deterministic.  The device is not touched.
  *
- * Source: gist.science explainer, "2. Calibrated Adaptive Policy".  A single
- * long row uses sequence splitting to open enough parallel work.  A batch of
+ * Source: gist.science explainer, "2. Calibrated Adaptive Policy": a single
+ * long row uses sequence splitting to open enough parallel work; a batch of
  * 8 or more long rows uses the compact workqueue, which amortises the
- * split+merge overhead.  The fugumt.com (v2) abstract calls the calibrated
+ * split+merge overhead; the thresholds are calibrated on one seed and judged
+ * on held-out seeds ("Resultaten").  The fugumt.com (v2) abstract calls the
  * policy "roofline-style".  The branches that hand work to another library
  * are outside this library.
  *
- * Rule, with n_b = ceil(N_b / page_size), active rows having n_b > 0, and
- * T* = tasks_per_cu * num_cus:
- *   - no active row: (SPLIT, 1).
- *   - one active row, or max n_b <= uniform_ratio * min n_b over active rows:
- *     SPLIT with S = the smallest power of two >= T* / (B_active * Hkv),
- *     capped at split_max.
- *   - otherwise: WORKQUEUE with c = the largest power of two
- *     <= Hkv * sum n_b / T*, clamped to [chunk_min, chunk_max].
+ * The policy predicts the time of every candidate plan with a roofline-style
+ * model and returns the fastest.  Candidates, in this order (ties keep the
+ * earlier one): SPLIT with S = 1, 2, 4, ... <= split_max, then WORKQUEUE with
+ * c = chunk_min, 2 chunk_min, ... <= chunk_max.  For a candidate, with
+ * n_b = ceil(N_b / page_size), c_b the chunk of row b (SPLIT: ceil(n_b/S);
+ * WORKQUEUE: c) and S_b = ceil(n_b / c_b) over rows with n_b > 0:
+ *   T = Hkv sum S_b tasks, P = Hkv sum n_b page tiles,
+ *   pmax = max min(c_b, n_b), maxS = max S_b,
+ *   W = min(T, 2 num_cus) workgroups (the decode grid), A = min(W, num_cus),
+ *   rho = min(cu_gbps, hbm_gbps / A)                 per-CU rate,
+ *   load = ceil(T / A) pmax              if T <= W   (every task static)
+ *        = P / A + alpha pmax            otherwise   (dynamic queue),
+ *   tile = 2 * page_size * head_dim * 2 bytes (K and V of one page of one
+ *          KV head),
+ *   t = t0_us + t_round_us ceil(T / W) + load tile / (rho 1e3)
+ *       + (maxS > fuse_max_splits ? t_two_us + t_two_split_us maxS
+ *                                 : t_fused_split_us maxS).
+ * All in double precision, in this order of operations (pkv_policy_predict
+ * returns t).  No active row gives (SPLIT, 1).
  *
  * seq_lens: host int32 [B].  params: NULL selects the defaults.
  * Outputs *mode (pkv_mode) and *param.
  * Errors: PKV_ERR_INVALID_ARG for a NULL pointer, B < 0, Hkv < 1,
- * page_size < 1, num_cus < 1 or a negative length.
+ * head_dim < 1, page_size < 1, num_cus < 1, a negative length or parameters
+ * outside their domain (split_max < 1, chunk_min < 1, chunk_max < chunk_min,
+ * fuse_max_splits < 0, a rate <= 0, a negative time or alpha).
  */
-int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
-               int32_t num_cus, const pkv_policy_params* params, int32_t* mode,
-               int32_t* param);
+int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
+               int32_t page_size, int32_t num_cus, const pkv_policy_params* params,
+               int32_t* mode, int32_t* param);
+
+/* The model time t (microseconds) of one candidate (mode, param) of
+ * pkv_policy, for tools and tests.  two_launch < 0 applies the
+ * fuse_max_splits rule; 0 / 1 force the fused / two-launch term.  Same
+ * arguments and errors as pkv_policy, plus PKV_ERR_INVALID_ARG for an unknown
+ * mode or param < 1. */
+int pkv_policy_predict(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
+                       int32_t page_size, int32_t num_cus, const pkv_policy_params* params,
+                       int32_t mode, int32_t param, int32_t two_launch, double* us);
 
 /*
  * pkv_plan -- build the compact task list and the per-row split offsets.

@@ -16,7 +16,10 @@ What it computes is fixed by the PersistentKV pages (arXiv 2606.26666):
     compact list of non-empty (row, KV head, split) tasks (same section, items
     "Sequentie Splitting", "Row-Local Bounds", "Compact Workqueue").
   * A host policy choosing split or workqueue scheduling from the batch size
-    and lengths (same page, "2. Calibrated Adaptive Policy").
+    and lengths, calibrated on one seed and judged on held-out seeds (same
+    page, "2. Calibrated Adaptive Policy" and "Resultaten"); the v2 abstract
+    calls it roofline-style.  Here: a roofline-style time model of each
+    candidate plan (``predict_us``), fastest candidate wins.
 
 Readings taken where the pages are silent (each also listed in the design doc):
   scale = 1/sqrt(d); query head h reads KV head floor(h/G); token t of a row
@@ -25,17 +28,21 @@ Readings taken where the pages are silent (each also listed in the design doc):
 
 Pins: every function here is checked against something other than itself in
 ``tests/test_oracle_pins.py`` (brute force, closed forms, a library special
-case, invariances) -- except ``policy``, whose thresholds are this project's
-own calibration choice: parity unpinned for the policy constants (its
-structural properties are still tested).
+case, invariances) -- except the policy's constants, which are this
+project's own fit to MI355X measurements: parity unpinned for ``policy`` and
+``predict_us`` (``plan_shape`` is pinned against the task list, and the
+policy's structural properties are tested).
 """
 from .ref import (  # noqa: F401
     MODE_SPLIT,
     MODE_WORKQUEUE,
+    POLICY_DEFAULTS,
     attend,
     merge_states,
     partial_state,
+    plan_shape,
     plan_tasks,
     policy,
+    predict_us,
     split_merge,
 )

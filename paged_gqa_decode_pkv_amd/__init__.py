@@ -40,7 +40,7 @@ WORKSPACE_HEADER_BYTES = 65536      # PKV_WORKSPACE_HEADER_BYTES
 # Every symbol include/pkv.h declares.
 ABI_SYMBOLS = (
     "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_policy_defaults",
-    "pkv_policy", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
+    "pkv_policy", "pkv_policy_predict", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
     "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_splits", "pkv_merge",
     "pkv_runner_create", "pkv_runner_step", "pkv_runner_destroy", "pkv_runner_last_plan",
 )
@@ -56,9 +56,16 @@ class PkvError(RuntimeError):
 
 
 class pkv_policy_params(ctypes.Structure):
-    _fields_ = [("tasks_per_cu", ctypes.c_float), ("chunk_min", ctypes.c_int32),
-                ("chunk_max", ctypes.c_int32), ("split_max", ctypes.c_int32),
-                ("uniform_ratio", ctypes.c_float), ("fuse_max_splits", ctypes.c_int32)]
+    """Mirror of pkv_policy_params in include/pkv.h."""
+    _fields_ = [("split_max", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
+                ("chunk_max", ctypes.c_int32), ("fuse_max_splits", ctypes.c_int32),
+                ("t0_us", ctypes.c_double), ("t_round_us", ctypes.c_double),
+                ("alpha", ctypes.c_double), ("cu_gbps", ctypes.c_double),
+                ("hbm_gbps", ctypes.c_double), ("t_two_us", ctypes.c_double),
+                ("t_two_split_us", ctypes.c_double), ("t_fused_split_us", ctypes.c_double)]
+
+    MODEL = ("t0_us", "t_round_us", "alpha", "cu_gbps", "hbm_gbps", "t_two_us",
+             "t_two_split_us", "t_fused_split_us")
 
 
 class pkv_step_args(ctypes.Structure):
@@ -100,8 +107,11 @@ def _load():
         "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "pkv_last_hip_error": ([], ctypes.c_int),
         "pkv_policy_defaults": ([ctypes.POINTER(pkv_policy_params)], ctypes.c_int),
-        "pkv_policy": ([_vp, i32, i32, i32, i32, ctypes.POINTER(pkv_policy_params), _i32p, _i32p],
+        "pkv_policy": ([_vp, i32, i32, i32, i32, i32, ctypes.POINTER(pkv_policy_params), _i32p,
+                        _i32p],
                        ctypes.c_int),
+        "pkv_policy_predict": ([_vp, i32, i32, i32, i32, i32, ctypes.POINTER(pkv_policy_params),
+                                i32, i32, i32, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "pkv_plan": ([_vp, i32, i32, i32, i32, _vp, i64, i32, i32, _vp, i64, _vp, _i64p, _i64p],
                      ctypes.c_int),
         "pkv_workspace_size": ([i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
@@ -163,14 +173,27 @@ def pkv_policy_defaults() -> pkv_policy_params:
 
 
 def pkv_policy(seq_lens, Hkv: int, num_cus: int, params: Optional[pkv_policy_params] = None,
-               page_size: int = PAGE_SIZE) -> Tuple[int, int]:
+               page_size: int = PAGE_SIZE, head_dim: int = 128) -> Tuple[int, int]:
     """(mode, param) for this batch; see pkv_policy in include/pkv.h."""
     sl = _host_i32(seq_lens)
     mode, param = ctypes.c_int32(), ctypes.c_int32()
     pp = ctypes.byref(params) if params is not None else None
-    _check(_load().pkv_policy(_ptr(sl), sl.size, Hkv, page_size, num_cus, pp, ctypes.byref(mode),
-                              ctypes.byref(param)), "pkv_policy")
+    _check(_load().pkv_policy(_ptr(sl), sl.size, Hkv, head_dim, page_size, num_cus, pp,
+                              ctypes.byref(mode), ctypes.byref(param)), "pkv_policy")
     return mode.value, param.value
+
+
+def pkv_policy_predict(seq_lens, Hkv: int, num_cus: int, mode: int, param: int,
+                       two_launch: int = -1, params: Optional[pkv_policy_params] = None,
+                       page_size: int = PAGE_SIZE, head_dim: int = 128) -> float:
+    """Model time (us) of one candidate; see pkv_policy_predict in include/pkv.h."""
+    sl = _host_i32(seq_lens)
+    us = ctypes.c_double()
+    pp = ctypes.byref(params) if params is not None else None
+    _check(_load().pkv_policy_predict(_ptr(sl), sl.size, Hkv, head_dim, page_size, num_cus, pp,
+                                      mode, param, two_launch, ctypes.byref(us)),
+           "pkv_policy_predict")
+    return us.value
 
 
 def pkv_plan(seq_lens, Hkv: int, max_pages_per_row: int, mode: int, param: int,

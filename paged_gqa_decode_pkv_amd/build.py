@@ -55,8 +55,11 @@ def build(verbose: bool = False, asm: bool = False) -> str:
     common = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall"]
     objs = []
     plan_o = os.path.join(BUILD_DIR, "plan.o")
-    _run([hipcc, "-x", "c++", *common, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o],
-         verbose)
+    # The policy's cost model must round every product and sum on its own
+    # (its decisions are compared bit for bit with the reference): no FMA
+    # contraction in the host planner.
+    _run([hipcc, "-x", "c++", *common, "-ffp-contract=off", "-c",
+          os.path.join(CSRC, "plan.cpp"), "-o", plan_o], verbose)
     objs.append(plan_o)
     run_o = os.path.join(BUILD_DIR, "runner.o")
     rocm_inc = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc))), "include")

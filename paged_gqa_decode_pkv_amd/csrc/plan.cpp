@@ -46,66 +46,154 @@ const char* pkv_status_string(int status) {
 
 int pkv_policy_defaults(pkv_policy_params* p) {
   if (!p) return PKV_ERR_INVALID_ARG;
-  p->tasks_per_cu = 0.75f;
+  p->split_max = 256;
   p->chunk_min = 4;
   p->chunk_max = 256;
-  p->split_max = 256;
-  p->uniform_ratio = 1.25f;
   p->fuse_max_splits = 16;
+  // Fitted on the calibration seed (paged_gqa_decode_pkv_amd/calibration/
+  // mi355x_fit.json, written by policy_fit.py from calibrate.py's runs).
+  p->t0_us = 10.01;
+  p->t_round_us = 5.849;
+  p->alpha = 1.056;
+  p->cu_gbps = 45.71;
+  p->hbm_gbps = 8113.0;
+  p->t_two_us = 5.69;
+  p->t_two_split_us = 0.01229;
+  p->t_fused_split_us = 0.2748;
   return PKV_OK;
 }
 
-// "2. Calibrated Adaptive Policy": split for one long row, workqueue for a
-// ragged batch.  The thresholds are this library's own.
-int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
-               int32_t num_cus, const pkv_policy_params* params, int32_t* mode,
-               int32_t* param) {
-  if (!mode || !param || B < 0 || (B > 0 && !seq_lens) || Hkv < 1 || page_size < 1 ||
-      num_cus < 1)
+}  // extern "C"
+
+namespace {
+
+// What the cost model needs to know about a candidate plan.
+struct PlanShape {
+  int64_t T = 0;      // tasks
+  int64_t P = 0;      // page tiles (page x KV head) in all
+  int64_t pmax = 0;   // pages of the largest task
+  int64_t maxS = 0;   // splits of the deepest row
+};
+
+PlanShape plan_shape(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
+                     int32_t mode, int64_t param) {
+  PlanShape f;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = ceil_div(seq_lens[b], page_size);
+    if (n == 0) continue;
+    const int64_t c = mode == PKV_MODE_SPLIT ? ceil_div(n, param) : param;
+    const int64_t S = ceil_div(n, c);
+    f.T += Hkv * S;
+    f.P += Hkv * n;
+    const int64_t largest = c < n ? c : n;
+    if (largest > f.pmax) f.pmax = largest;
+    if (S > f.maxS) f.maxS = S;
+  }
+  return f;
+}
+
+// The model of pkv_policy (include/pkv.h), in the documented order of
+// operations.  This file is compiled without floating-point contraction, so
+// every product and sum is rounded on its own.
+double model_us(const pkv_policy_params& p, const PlanShape& f, int32_t num_cus,
+                int32_t head_dim, int32_t page_size, bool two) {
+  if (f.T == 0) return p.t0_us;
+  const int64_t W = f.T < 2 * static_cast<int64_t>(num_cus) ? f.T : 2 * static_cast<int64_t>(num_cus);
+  const int64_t A = W < num_cus ? W : num_cus;
+  const double share = p.hbm_gbps / static_cast<double>(A);
+  const double rho = share < p.cu_gbps ? share : p.cu_gbps;
+  double load;
+  if (f.T <= W) {
+    load = static_cast<double>(ceil_div(f.T, A) * f.pmax);
+  } else {
+    load = static_cast<double>(f.P) / static_cast<double>(A) +
+           p.alpha * static_cast<double>(f.pmax);
+  }
+  const double tile = 2.0 * page_size * head_dim * 2.0;
+  double t = p.t0_us + p.t_round_us * static_cast<double>(ceil_div(f.T, W)) +
+             load * tile / (rho * 1e3);
+  if (two) {
+    t = t + p.t_two_us + p.t_two_split_us * static_cast<double>(f.maxS);
+  } else {
+    t = t + p.t_fused_split_us * static_cast<double>(f.maxS);
+  }
+  return t;
+}
+
+int check_policy_args(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
+                      int32_t page_size, int32_t num_cus, const pkv_policy_params& p) {
+  if (B < 0 || (B > 0 && !seq_lens) || Hkv < 1 || head_dim < 1 || page_size < 1 || num_cus < 1)
     return PKV_ERR_INVALID_ARG;
+  if (p.split_max < 1 || p.chunk_min < 1 || p.chunk_max < p.chunk_min || p.fuse_max_splits < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!(p.cu_gbps > 0.0) || !(p.hbm_gbps > 0.0) || !(p.t0_us >= 0.0) ||
+      !(p.t_round_us >= 0.0) || !(p.alpha >= 0.0) || !(p.t_two_us >= 0.0) ||
+      !(p.t_two_split_us >= 0.0) || !(p.t_fused_split_us >= 0.0))
+    return PKV_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < B; ++b)
+    if (seq_lens[b] < 0) return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_policy_predict(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
+                       int32_t page_size, int32_t num_cus, const pkv_policy_params* params,
+                       int32_t mode, int32_t param, int32_t two_launch, double* us) {
   pkv_policy_params p;
   if (params) {
     p = *params;
   } else {
     pkv_policy_defaults(&p);
   }
-  if (!(p.tasks_per_cu > 0.0f) || p.chunk_min < 1 || p.chunk_max < p.chunk_min ||
-      p.split_max < 1 || !(p.uniform_ratio >= 1.0f) || p.fuse_max_splits < 0)
+  if (!us || (mode != PKV_MODE_SPLIT && mode != PKV_MODE_WORKQUEUE) || param < 1)
     return PKV_ERR_INVALID_ARG;
+  const int st = check_policy_args(seq_lens, B, Hkv, head_dim, page_size, num_cus, p);
+  if (st != PKV_OK) return st;
+  const PlanShape f = plan_shape(seq_lens, B, Hkv, page_size, mode, param);
+  const bool two = two_launch < 0 ? f.maxS > p.fuse_max_splits : two_launch != 0;
+  *us = model_us(p, f, num_cus, head_dim, page_size, two);
+  return PKV_OK;
+}
 
-  int64_t active = 0, total = 0, nmin = INT64_MAX, nmax = 0;
-  for (int32_t b = 0; b < B; ++b) {
-    if (seq_lens[b] < 0) return PKV_ERR_INVALID_ARG;
-    const int64_t n = ceil_div(seq_lens[b], page_size);
-    if (n == 0) continue;
-    ++active;
-    total += n;
-    if (n < nmin) nmin = n;
-    if (n > nmax) nmax = n;
+// "2. Calibrated Adaptive Policy": the fastest candidate under the fitted
+// roofline-style model (include/pkv.h documents the model).
+int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
+               int32_t page_size, int32_t num_cus, const pkv_policy_params* params,
+               int32_t* mode, int32_t* param) {
+  if (!mode || !param) return PKV_ERR_INVALID_ARG;
+  pkv_policy_params p;
+  if (params) {
+    p = *params;
+  } else {
+    pkv_policy_defaults(&p);
   }
+  const int st = check_policy_args(seq_lens, B, Hkv, head_dim, page_size, num_cus, p);
+  if (st != PKV_OK) return st;
+  int64_t active = 0;
+  for (int32_t b = 0; b < B; ++b)
+    if (seq_lens[b] > 0) ++active;
   if (active == 0) {
     *mode = PKV_MODE_SPLIT;
     *param = 1;
     return PKV_OK;
   }
-  const double target = static_cast<double>(p.tasks_per_cu) * num_cus;
-  if (active == 1 ||
-      static_cast<double>(nmax) <= static_cast<double>(p.uniform_ratio) * nmin) {
-    const double want = target / static_cast<double>(active * Hkv);
-    int64_t S = 1;
-    while (S < want && S < p.split_max) S *= 2;
-    if (S > p.split_max) S = p.split_max;
-    *mode = PKV_MODE_SPLIT;
-    *param = static_cast<int32_t>(S);
-    return PKV_OK;
-  }
-  const double per = static_cast<double>(Hkv) * static_cast<double>(total) / target;
-  int64_t c = 1;
-  while (static_cast<double>(c * 2) <= per) c *= 2;
-  if (c < p.chunk_min) c = p.chunk_min;
-  if (c > p.chunk_max) c = p.chunk_max;
-  *mode = PKV_MODE_WORKQUEUE;
-  *param = static_cast<int32_t>(c);
+  bool have = false;
+  double best = 0.0;
+  auto consider = [&](int32_t m, int64_t v) {
+    const PlanShape f = plan_shape(seq_lens, B, Hkv, page_size, m, v);
+    const double t = model_us(p, f, num_cus, head_dim, page_size, f.maxS > p.fuse_max_splits);
+    if (!have || t < best) {
+      have = true;
+      best = t;
+      *mode = m;
+      *param = static_cast<int32_t>(v);
+    }
+  };
+  for (int64_t S = 1; S <= p.split_max; S *= 2) consider(PKV_MODE_SPLIT, S);
+  for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) consider(PKV_MODE_WORKQUEUE, c);
   return PKV_OK;
 }
 

@@ -41,6 +41,15 @@ struct Slot {
 
 inline size_t pad4(int64_t n) { return static_cast<size_t>((n + 3) & ~int64_t(3)); }
 
+// Capacity for a plan buffer that must hold `bytes`: at least 64 KiB (about
+// 4000 tasks), else the next power of two, so that growing plans reallocate
+// (and, for pinned memory, re-pin) only a few times.
+inline size_t grown_size(size_t bytes) {
+  size_t n = size_t(1) << 16;
+  while (n < bytes) n <<= 1;
+  return n;
+}
+
 }  // namespace
 
 struct pkv_runner {
@@ -94,7 +103,7 @@ int upload_plan(pkv_runner* r, Slot& s, size_t words) {
       r->dplan = nullptr;
       r->dplan_bytes = 0;
     }
-    const size_t want = bytes < 4096 ? 4096 : bytes + bytes / 4;
+    const size_t want = grown_size(bytes);
     e = hipMalloc(reinterpret_cast<void**>(&r->dplan), want);
     if (e != hipSuccess) {
       r->dplan = nullptr;
@@ -149,13 +158,29 @@ int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t 
       return PKV_ERR_HIP;
     }
   }
+  // Buffers of the initial capacity up front, so that the first steps do
+  // not pin memory.
   for (Slot& s : r->ring) {
     hipError_t e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipHostMalloc(reinterpret_cast<void**>(&s.host), grown_size(0), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s.dev), s.host, 0);
     if (e != hipSuccess) {
       pkv::set_hip_error(static_cast<int>(e));
       pkv_runner_destroy(r);
       return PKV_ERR_HIP;
     }
+    s.bytes = grown_size(0);
+  }
+  {
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&r->dplan), grown_size(0));
+    if (e != hipSuccess) {
+      r->dplan = nullptr;
+      pkv::set_hip_error(static_cast<int>(e));
+      pkv_runner_destroy(r);
+      return PKV_ERR_HIP;
+    }
+    r->dplan_bytes = grown_size(0);
   }
   *runner = r;
   return PKV_OK;
@@ -193,8 +218,8 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   // policy ("2. Calibrated Adaptive Policy")
   int32_t mode = a->mode, param = a->param;
   if (mode < 0) {
-    int st = pkv_policy(a->seq_lens_host, a->B, a->Hkv, a->page_size, r->num_cus, &r->params,
-                        &mode, &param);
+    int st = pkv_policy(a->seq_lens_host, a->B, a->Hkv, a->head_dim, a->page_size, r->num_cus,
+                        &r->params, &mode, &param);
     if (st != PKV_OK) return st;
   }
   a->chosen_mode = mode;
@@ -238,7 +263,7 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
     if (s.host) hipHostFree(s.host);
     s.host = s.dev = nullptr;
     s.bytes = 0;
-    size_t want = plan_bytes < 4096 ? 4096 : plan_bytes + plan_bytes / 4;
+    const size_t want = grown_size(plan_bytes);
     e = hipHostMalloc(reinterpret_cast<void**>(&s.host), want, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s.dev), s.host, 0);
     if (e != hipSuccess) {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert pkv.pkv_abi_version() == 1
+    assert pkv.pkv_abi_version() == 2
     for code in range(6):
         assert pkv.pkv_status_string(code)
     assert pkv.pkv_status_string(99) == "unknown status"
@@ -124,31 +124,106 @@ def test_plan_buffer_too_small():
 
 # --------------------------------------------------------------------------- policy
 
-def test_policy_matches_oracle_rule():
+def _policy_cases():
     rng = np.random.default_rng(5)
-    cases = [[32768], [0], [], [100, 0], [16] * 8]
+    cases = [[32768], [0], [], [100, 0], [16] * 8, [1] * 300, [65536, 1]]
     for name in CONFIGS:
         for seed in (CALIBRATION_SEED,) + HELD_OUT_SEEDS:
             cases.append(make_lengths(CONFIGS[name], seed).tolist())
-    for _ in range(50):
-        cases.append(rng.integers(0, 40000, size=int(rng.integers(1, 65))).tolist())
-    for lens in cases:
+    for _ in range(60):
+        hi = int(rng.choice([300, 5000, 40000, 70000]))
+        cases.append(rng.integers(0, hi, size=int(rng.integers(1, 65))).tolist())
+    return cases
+
+
+def test_policy_matches_oracle():
+    """The library's cost-model policy takes the oracle's decision, bit for bit,
+    over the workload configs, their seeds and random batches."""
+    for lens in _policy_cases():
         for cus in (1, 80, 256, 304):
             for Hkv in (1, 8):
-                got = pkv.pkv_policy(lens, Hkv, cus)
-                want = oracle.policy(lens, Hkv, 16, cus)
-                assert got == tuple(int(x) for x in want), (lens[:4], cus, Hkv)
+                for D in (64, 128):
+                    got = pkv.pkv_policy(lens, Hkv, cus, head_dim=D)
+                    want = oracle.policy(lens, Hkv, 16, cus, head_dim=D)
+                    assert got == tuple(int(x) for x in want), (lens[:4], cus, Hkv, D)
+
+
+def test_policy_predict_matches_oracle_bit_for_bit():
+    """The model times themselves agree exactly (same float64 operations, no
+    contraction), for every candidate and both launch forms."""
+    rng = np.random.default_rng(6)
+    for lens in _policy_cases()[::3]:
+        for cus in (80, 256):
+            for mode, param in [(0, 1), (0, 8), (0, 256), (1, 4), (1, 64), (1, 256),
+                                (0, int(rng.integers(1, 500))), (1, int(rng.integers(1, 500)))]:
+                for two in (-1, 0, 1):
+                    got = pkv.pkv_policy_predict(lens, 8, cus, mode, param, two)
+                    shape = oracle.plan_shape(lens, 8, 16, mode, param)
+                    t2 = shape[3] > oracle.POLICY_DEFAULTS["fuse_max_splits"] if two < 0 else bool(two)
+                    want = oracle.predict_us(shape, cus, 128, 16, t2, oracle.POLICY_DEFAULTS)
+                    assert got == want, (lens[:4], cus, mode, param, two, got, want)
+
+
+def test_policy_defaults_are_the_committed_fit():
+    """pkv_policy_defaults and the oracle's defaults hold the constants that
+    policy_fit.py fitted on the calibration seed."""
+    import json
+    fit = json.load(open(os.path.join(ROOT, "paged_gqa_decode_pkv_amd", "calibration",
+                                      "mi355x_fit.json")))
+    d = pkv.pkv_policy_defaults()
+    for name, v in fit["params"].items():
+        assert getattr(d, name) == v, name
+        assert oracle.POLICY_DEFAULTS[name] == v, name
+    assert (d.split_max, d.chunk_min, d.chunk_max, d.fuse_max_splits) == (256, 4, 256, 16)
+    for k in ("split_max", "chunk_min", "chunk_max", "fuse_max_splits"):
+        assert oracle.POLICY_DEFAULTS[k] == getattr(d, k)
 
 
 def test_policy_params_and_errors():
     d = pkv.pkv_policy_defaults()
-    assert d.chunk_min == 4 and d.chunk_max == 256 and d.split_max == 256
     d.split_max = 8
-    assert pkv.pkv_policy([32768], 8, 256, params=d) == (pkv.PKV_MODE_SPLIT, 8)
+    d.chunk_max = 2          # below chunk_min: invalid
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_policy([32768], 8, 256, params=d)
+    d = pkv.pkv_policy_defaults()
+    d.chunk_min, d.chunk_max = 1024, 1024
+    d.split_max = 8
+    # one long row: only S <= 8 or c = 1024 are candidates
+    m, p = pkv.pkv_policy([32768], 8, 256, params=d)
+    assert (m, p) in [(pkv.PKV_MODE_SPLIT, 8), (pkv.PKV_MODE_WORKQUEUE, 1024)]
+    assert (m, p) == oracle.policy([32768], 8, 16, 256, split_max=8, chunk_min=1024,
+                                   chunk_max=1024)
     with pytest.raises(pkv.PkvError):
         pkv.pkv_policy([-5], 8, 256)
     with pytest.raises(pkv.PkvError):
         pkv.pkv_policy([5], 8, 0)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_policy([5], 8, 256, head_dim=0)
+    for field, bad in (("cu_gbps", 0.0), ("hbm_gbps", -1.0), ("alpha", -0.5), ("t0_us", -1.0),
+                       ("split_max", 0), ("fuse_max_splits", -1)):
+        d = pkv.pkv_policy_defaults()
+        setattr(d, field, bad)
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_policy([5000], 8, 256, params=d)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_policy_predict([5000], 8, 256, 7, 4)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_policy_predict([5000], 8, 256, 1, 0)
+
+
+def test_policy_fit_features_match_the_planner():
+    """The calibration tool's closed-form plan features equal the planner's."""
+    from paged_gqa_decode_pkv_amd import policy_fit
+    rng = np.random.default_rng(8)
+    for _ in range(30):
+        lens = rng.integers(0, 20000, size=int(rng.integers(1, 20)))
+        for mode, param in [(0, 1), (0, 7), (0, 64), (1, 4), (1, 33), (1, 256)]:
+            T, P, pmax, maxS = policy_fit.plan_features(lens, 8, mode, param)
+            tasks, offs, _ = pkv.pkv_plan(lens, 8, 2048, mode, param)
+            n = -(-lens // 16)
+            pages = [min((s + 1) * c, n[b]) - s * c for b, g, s, c in tasks]
+            assert T == len(tasks) and P == sum(pages) and pmax == max(pages, default=0)
+            assert maxS == (int(np.max(np.diff(offs))) if len(offs) > 1 else 0)
 
 
 # --------------------------------------------------------------------------- workspace, decode arg checks

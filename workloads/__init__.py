@@ -88,6 +88,22 @@ def _uniform64(rng: np.random.Generator) -> np.ndarray:
     return rng.integers(4096, 65537, size=64)
 
 
+def _bucketed1(rng: np.random.Generator) -> np.ndarray:
+    # one long-context row whose length falls in a power-of-two bucket
+    bucket = int(rng.choice([8192, 16384, 32768, 65536]))
+    return np.array([rng.integers(bucket // 2 + 1, bucket + 1)])
+
+
+def _bimodal4(rng: np.random.Generator) -> np.ndarray:
+    short = rng.integers(256, 1025, size=2)
+    long_ = rng.integers(12288, 16385, size=2)
+    return rng.permutation(np.concatenate([short, long_]))
+
+
+def _uniform32(rng: np.random.Generator) -> np.ndarray:
+    return rng.integers(1024, 32769, size=32)
+
+
 CONFIGS: Dict[str, Config] = {
     c.name: c
     for c in [
@@ -109,6 +125,16 @@ CONFIGS: Dict[str, Config] = {
         Config("b64", B=64, Hq=32, Hkv=8, D=128, max_pages_per_row=4096,
                pool_pages=2 * 64 * 4096, lengths=_uniform64,
                description="B=64, N~U[4096,65536], 34.4 GB K+V pool"),
+        # traces of the policy calibration protocol
+        Config("b1_bucketed", B=1, Hq=32, Hkv=8, D=128, max_pages_per_row=4096,
+               pool_pages=8192, lengths=_bucketed1,
+               description="B=1, bucket in {8K,16K,32K,64K}, N~U(bucket/2, bucket]"),
+        Config("b4_bimodal", B=4, Hq=32, Hkv=8, D=128, max_pages_per_row=1024,
+               pool_pages=2 * 4 * 1024, lengths=_bimodal4,
+               description="B=4, 2 rows U[256,1024] + 2 rows U[12288,16384], shuffled"),
+        Config("b32_uniform", B=32, Hq=32, Hkv=8, D=128, max_pages_per_row=2048,
+               pool_pages=2 * 32 * 2048, lengths=_uniform32,
+               description="B=32, N~U[1024,32768] (B*Hkv = one task per CU unsplit)"),
     ]
 }
 
