@@ -333,6 +333,67 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
               size_t workspace_bytes, void* stream);
 
 /*
+ * Device-side planning -- one decode step whose plan is built on the device
+ * from the row lengths in device memory: no host copy of the lengths, no
+ * host planning, nothing the host must wait for.  (The pages plan on the
+ * host and count it in the step's wall time; this entry point moves that
+ * step onto the GPU.)
+ *
+ * Source: gist.science explainer, "Row-Local Bounds", "Compact Workqueue" and
+ * "2. Calibrated Adaptive Policy".  Three launches on `stream`:
+ *   1. a one-workgroup planner kernel: with mode = -1 it picks (mode, param)
+ *      exactly as pkv_policy would with `policy` limited to the capacity
+ *      (split_max <= max_splits; workqueue chunks c with
+ *      ceil(max_pages_per_row / c) <= max_splits); then it writes the same
+ *      split_offsets and task records as pkv_plan, and a header;
+ *   2. the persistent decode kernel, 2 * num_cus workgroups, reading the
+ *      task count from the header;
+ *   3. the merge kernel, which returns at once when the header says the
+ *      decode kernel merged (the fused form: no row deeper than
+ *      policy->fuse_max_splits and B * Hkv <= PKV_MAX_FUSED_GROUPS).
+ * Arguments as for pkv_decode, except:
+ *   seq_lens     device int32 [B]; a row with N_b < 0 or needing more than
+ *                max_pages_per_row pages is planned as empty (out = 0,
+ *                lse = -inf) and flagged with PKV_DEVERR_ROW
+ *   mode, param  -1 (any param): the policy on the device; else an explicit
+ *                schedule, which must fit the capacity
+ *   max_splits   capacity: the most splits any row may get (>= 1)
+ *   policy       candidate sets and model constants; NULL = the defaults
+ *   num_cus      CUs of the device for the model and the grid; 0 = query
+ *   workspace    >= pkv_workspace_size_device_plan(B, Hq, Hkv, head_dim,
+ *                max_splits) bytes, 256-byte aligned, initialised once by
+ *                pkv_workspace_init.  Layout: the pkv_decode workspace for
+ *                B * max_splits partial slots, then the plan area: header
+ *                (16 int32), split_offsets (B+1, padded to 16 B), records.
+ * Errors: those of pkv_decode; PKV_ERR_INVALID_ARG for mode outside
+ * {-1, 0, 1}, max_splits < 1, an explicit schedule that could exceed
+ * max_splits for some row of up to max_pages_per_row pages, or invalid
+ * policy constants.
+ */
+int pkv_workspace_size_device_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                   int32_t max_splits, size_t* bytes);
+
+int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool,
+                           int64_t num_pages, const int32_t* block_table,
+                           int32_t max_pages_per_row, const int32_t* seq_lens, int32_t B,
+                           int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                           float scale, int32_t mode, int32_t param, int32_t max_splits,
+                           const pkv_policy_params* policy, int32_t num_cus, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Read back the plan the last pkv_decode_device_plan on this workspace built
+ * (after synchronizing `stream`): header[8] = {tasks, fused (1) or
+ * two-launch (0), mode, param, partial slots, deepest row's splits, 1 if a
+ * row was flagged, 0}; split_offsets [B+1] and tasks [header[0]][4] are
+ * optional (NULL skips them; task_capacity is the record capacity of
+ * `tasks`).  For tests and tools.  Errors: PKV_ERR_INVALID_ARG,
+ * PKV_ERR_BUFFER_TOO_SMALL (workspace or task_capacity), PKV_ERR_HIP. */
+int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t head_dim, int32_t max_splits, int32_t* header,
+                         int32_t* split_offsets, int32_t* tasks, int64_t task_capacity,
+                         void* stream);
+
+/*
  * Step runner -- the whole hot path of one decode step in one call:
  * policy, host plan, then the decode kernel and the merge kernel on the
  * caller's stream.

@@ -42,6 +42,7 @@ ABI_SYMBOLS = (
     "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_policy_defaults",
     "pkv_policy", "pkv_policy_predict", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
     "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_splits", "pkv_merge",
+    "pkv_workspace_size_device_plan", "pkv_decode_device_plan", "pkv_device_plan_read",
     "pkv_runner_create", "pkv_runner_step", "pkv_runner_destroy", "pkv_runner_last_plan",
 )
 
@@ -121,6 +122,14 @@ def _load():
                         i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "pkv_merge": ([_vp, i64, i32, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                       ctypes.c_int),
+        "pkv_workspace_size_device_plan": ([i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+        "pkv_decode_device_plan": ([_vp, _vp, _vp, i64, _vp, i32, _vp, i32, i32, i32, i32, i32,
+                                    ctypes.c_float, i32, i32, i32,
+                                    ctypes.POINTER(pkv_policy_params), i32, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp], ctypes.c_int),
+        "pkv_device_plan_read": ([_vp, ctypes.c_size_t, i32, i32, i32, i32, i32, _i32p, _vp, _vp,
+                                  i64, _vp], ctypes.c_int),
         "pkv_runner_create": ([i32, ctypes.POINTER(pkv_policy_params), i32, ctypes.POINTER(_vp)],
                               ctypes.c_int),
         "pkv_runner_step": ([_vp, ctypes.POINTER(pkv_step_args)], ctypes.c_int),
@@ -332,6 +341,59 @@ def pkv_merge(split_offsets, num_partial_slots: int, Hkv: int, out, workspace, l
         _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
         "pkv_merge")
+
+
+# --------------------------------------------------------------------------- device-side plan
+
+def pkv_workspace_size_device_plan(B: int, Hq: int, Hkv: int, head_dim: int,
+                                   max_splits: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_load().pkv_workspace_size_device_plan(B, Hq, Hkv, head_dim, max_splits,
+                                                  ctypes.byref(n)),
+           "pkv_workspace_size_device_plan")
+    return n.value
+
+
+def pkv_decode_device_plan(q, k_pool, v_pool, block_table, seq_lens, scale: float, out,
+                           workspace, max_splits: int, lse=None, mode: int = -1, param: int = 0,
+                           params: Optional[pkv_policy_params] = None, num_cus: int = 0,
+                           stream=None):
+    """One step planned on the device; see pkv_decode_device_plan in include/pkv.h.
+    seq_lens is a device tensor: nothing is read on the host."""
+    import torch
+    f16, i32 = torch.float16, torch.int32
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, Dk = k_pool.shape
+    if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("shape mismatch between q, k_pool, v_pool and out")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if lse is not None and tuple(lse.shape) != (B, Hq):
+        raise ValueError("lse must be [B, Hq]")
+    pp = ctypes.byref(params) if params is not None else None
+    _check(_load().pkv_decode_device_plan(
+        _dev(q, f16, "q"), _dev(k_pool, f16, "k_pool"), _dev(v_pool, f16, "v_pool"), num_pages,
+        _dev(block_table, i32, "block_table"), block_table.shape[1], _dev(seq_lens, i32, "seq_lens"),
+        B, Hq, Hkv, D, P, float(scale), mode, param, max_splits, pp, num_cus,
+        _dev(out, f16, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
+        "pkv_decode_device_plan")
+
+
+def pkv_device_plan_read(workspace, B: int, Hq: int, Hkv: int, head_dim: int, max_splits: int,
+                         stream=None):
+    """(header dict, tasks [T,4], split_offsets [B+1]) of the last device plan."""
+    import torch
+    hdr = np.zeros(8, dtype=np.int32)
+    offs = np.zeros(B + 1, dtype=np.int32)
+    cap = Hkv * B * max_splits
+    tasks = np.zeros((max(cap, 1), 4), dtype=np.int32)
+    _check(_load().pkv_device_plan_read(
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), B, Hq, Hkv, head_dim,
+        max_splits, hdr.ctypes.data_as(_i32p), _ptr(offs), _ptr(tasks), cap, _stream_ptr(stream)),
+        "pkv_device_plan_read")
+    keys = ("num_tasks", "fused", "mode", "param", "num_partial_slots", "max_splits", "row_flagged")
+    return dict(zip(keys, (int(x) for x in hdr[:7]))), tasks[:hdr[0]].copy(), offs
 
 
 # --------------------------------------------------------------------------- runner

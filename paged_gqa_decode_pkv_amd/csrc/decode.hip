@@ -45,6 +45,7 @@
 #include <cstdint>
 
 #include "pkv.h"
+#include "policy_model.h"
 #include "internal.h"
 
 namespace pkv {
@@ -72,7 +73,9 @@ struct DecodeArgs {
   int32_t max_pages;
   const int32_t* seq_lens;
   const int32_t* tasks;
-  int32_t num_tasks;
+  int32_t num_tasks;  // tasks of a host plan
+  int32_t task_cap;   // records readable at `tasks` (>= 1)
+  const int32_t* plan_hdr;  // device plan: [0] tasks, [1] fuse; NULL for a host plan
   const int32_t* split_offsets;
   int64_t num_slots;
   int32_t B, Hq, Hkv, G;
@@ -214,6 +217,7 @@ struct MergeArgs {
   const int32_t* split_offsets;
   int64_t num_slots;
   int32_t B, Hq, Hkv, G;
+  const int32_t* plan_hdr;   // device plan: [1] != 0 means the decode kernel merged
   const float* part_o;
   const float2* part_ml;
   _Float16* out;
@@ -360,23 +364,25 @@ struct Meta {
 // flagged in the error word and leaves ok = false (all pages disabled).
 // The read-only inputs arrive as restrict pointers, so uniform loads from
 // them are scalar (SMEM) loads, whose waits never cover vector page loads.
-// The record of task t (a scalar load), or zeros past the end of the list.
+// The record of task t (a scalar load).  The index is clamped to the
+// readable records, so the load does not wait for the task count; records
+// past the count are never used.
 __device__ __forceinline__ int4 load_record(const DecodeArgs& a, const int4* __restrict__ tasks,
                                             int t) {
-  return t < a.num_tasks ? tasks[t] : int4{0, 0, 0, 0};
+  return tasks[t < a.task_cap ? t : a.task_cap - 1];
 }
 
 template <bool kStaged>
 __device__ __forceinline__ Meta decode_meta(const DecodeArgs& a, const int32_t* __restrict__ seq_lens,
                                             const int32_t* __restrict__ offs, const int* s_len,
-                                            const int* s_off, int t, int4 rec) {
+                                            const int* s_off, int num_tasks, int t, int4 rec) {
   Meta m;
   m.t = t;
   m.b = m.g = m.N = m.p0 = m.p1 = m.Sb = m.o0 = 0;
   m.slot = 0;
   m.rounds = 1;
   m.ok = false;
-  if (t >= a.num_tasks) return m;
+  if (t >= num_tasks) return m;
   const int b = __builtin_amdgcn_readfirstlane(rec.x);
   const int g = __builtin_amdgcn_readfirstlane(rec.y);
   const int s = __builtin_amdgcn_readfirstlane(rec.z);
@@ -433,8 +439,9 @@ template <bool kStaged>
 __device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __restrict__ tasks,
                                           const int32_t* __restrict__ seq_lens,
                                           const int32_t* __restrict__ offs, const int* s_len,
-                                          const int* s_off, int t) {
-  return decode_meta<kStaged>(a, seq_lens, offs, s_len, s_off, t, load_record(a, tasks, t));
+                                          const int* s_off, int num_tasks, int t) {
+  return decode_meta<kStaged>(a, seq_lens, offs, s_len, s_off, num_tasks, t,
+                              load_record(a, tasks, t));
 }
 
 // Count in n deferred split tasks (row, KV head, first slot, splits) of this
@@ -511,8 +518,16 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ int s_lastf[kMaxDone];
   static_assert(kWaves * kMaxG * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
 
-  const MergeArgs ma{a.split_offsets, a.num_slots, a.B, a.Hq, a.Hkv, a.G,
+  const MergeArgs ma{a.split_offsets, a.num_slots, a.B, a.Hq, a.Hkv, a.G, nullptr,
                      a.part_o, a.part_ml, a.out, a.lse, a.ctrl};
+  // Task count and merge form: kernel arguments, or the header the
+  // device-side planner wrote before this launch.
+  int num_tasks = a.num_tasks;
+  int fuse = a.fuse;
+  if (a.plan_hdr) {
+    num_tasks = __builtin_amdgcn_readfirstlane(a.plan_hdr[0]);
+    fuse = __builtin_amdgcn_readfirstlane(a.plan_hdr[1]);
+  }
   // Staging loads first (vector), then the first task record (scalar), then
   // the LDS stores: the two load latencies overlap instead of adding up.
   int4 rec0;
@@ -536,7 +551,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     rec0 = load_record(a, tasks_in, blockIdx.x);
   }
   __syncthreads();
-  if (a.fuse) {
+  if (fuse) {
     // rows without tasks (N_b = 0): out = 0, lse = -inf
     for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
       const int sb = kStaged ? s_off[b + 1] - s_off[b] : offs_in[b + 1] - offs_in[b];
@@ -585,7 +600,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   };
 
   // ---- prologue: task 0 = blockIdx.x, task 1 = blockIdx.x + gridDim.x
-  Meta cur = decode_meta<kStaged>(a, seq_lens_in, offs_in, s_len, s_off, blockIdx.x, rec0);
+  Meta cur = decode_meta<kStaged>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, blockIdx.x,
+                                  rec0);
   int t_nxt = blockIdx.x + gridDim.x;
   PageRegs<D> ring[kRing];
   bool valid[kRing];
@@ -602,24 +618,25 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __syncthreads();
 
   int n_done = 0;   // entries of s_done (workgroup-uniform)
-  for (int it = 0; cur.t < a.num_tasks; ++it) {
+  for (int it = 0; cur.t < num_tasks; ++it) {
     const int par = it & 1;
     // next task's metadata, its first round of table entries and its q;
     // the index of the task after it (counter values start at 2*gridDim.x)
-    const Meta nxt = load_meta<kStaged>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, t_nxt);
+    const Meta nxt =
+        load_meta<kStaged>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, num_tasks, t_nxt);
     const Round nr0 = load_round(a, bt_in, nxt, wave, 0);
     // Wave 0: the index after next and the next task's q, both to LDS.
     // Their loads queue behind this task's first round, which the wave has
     // to wait for next anyway, so the wait costs nothing extra.
     if (wave == 0) {
-      const bool fetch = t_nxt < a.num_tasks;
+      const bool fetch = t_nxt < num_tasks;
       uint32_t raw_nn = 0;
       if (fetch && lane == 0) raw_nn = atomicAdd(a.ctrl, 1u);
       half8 qn[KK];
       load_q(nxt, qn);
       store_q(nxt, qn, s_q[par ^ 1]);
       if (lane == 0)
-        s_next[par] = fetch ? static_cast<int>(2u * gridDim.x + raw_nn) : a.num_tasks;
+        s_next[par] = fetch ? static_cast<int>(2u * gridDim.x + raw_nn) : num_tasks;
     }
 
     WaveState<D> st;
@@ -697,7 +714,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
           }
         }
       }
-      if (a.fuse && !direct) {
+      if (fuse && !direct) {
         // Fused merge, deferred: the split is counted in later, so waiting
         // for its stores does not also wait for the page loads of the tasks
         // behind it.
@@ -728,6 +745,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
 template <int D>
 __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) float lds[merge_lds_floats<D>()];
+  if (a.plan_hdr && a.plan_hdr[1]) return;   // merged inside the decode kernel
   const int b = blockIdx.x / a.Hkv;
   const int g = blockIdx.x - b * a.Hkv;
   const int o0 = __builtin_amdgcn_readfirstlane(a.split_offsets[b]);
@@ -739,6 +757,206 @@ __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
     return;
   }
   merge_group<D, kMergeBatch>(a, b, g, o0, S, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Device-side planner: the plan (and, if asked, the policy's choice) from the
+// row lengths in device memory, so a step needs no host copy of them.
+//
+// "2. Calibrated Adaptive Policy" / "Row-Local Bounds" / "Compact Workqueue"
+// (gist.science explainer): the same candidate search and time model as
+// pkv_policy (policy_model.h), and the same records, offsets and order as
+// pkv_plan, computed by one workgroup:
+//   1. policy (mode < 0): each wave evaluates every 4th candidate over all
+//      rows (lanes stride the rows; wave reductions), lane 0 evaluates the
+//      model; the earliest fastest candidate wins.
+//   2. rows in chunks of 256: S_b per thread, an exclusive scan in LDS gives
+//      split_offsets; then, row by row, all threads write the row's records.
+//   3. the header: tasks, fused or not, mode, param, slots, deepest row.
+// A row with N_b < 0 or more than max_pages pages is flagged
+// (PKV_DEVERR_ROW) and planned as empty.
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t B, Hkv, head_dim, page_size, num_cus;
+  int32_t max_pages;
+  int32_t mode, param;      // mode < 0: the policy chooses
+  int32_t groups_fit;       // B * Hkv fits the fused merge's arrival counters
+  pkv_policy_params pol;    // candidate sets already limited to the capacity
+  int32_t* hdr;             // [kPlanHdrInts]
+  int32_t* offs;            // [B + 1]
+  int4* tasks;              // capacity Hkv * B * max_splits
+  uint32_t* ctrl;
+};
+
+constexpr int kPlanHdrInts = 16;
+
+__device__ __forceinline__ int64_t plan_row_pages(const PlanArgs& a, int b, bool* bad) {
+  const int32_t N = a.seq_lens[b];
+  if (N < 0) {
+    *bad = true;
+    return 0;
+  }
+  const int64_t n = cdiv(N, a.page_size);
+  if (n > a.max_pages) {
+    *bad = true;
+    return 0;
+  }
+  return n;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ int64_t wave_max64(int64_t v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
+  __shared__ double s_best_t[kWaves];
+  __shared__ int s_best_i[kWaves];
+  __shared__ int s_scan[kThreads];
+  __shared__ int s_S[kThreads];
+  __shared__ int s_c[kThreads];
+  __shared__ int s_pick[2];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // ---- 1. policy
+  int mode = a.mode, param = a.param;
+  if (mode < 0) {
+    const pkv_policy_params& p = a.pol;
+    int nsplit = 0;
+    for (int64_t S = 1; S <= p.split_max; S *= 2) ++nsplit;
+    int nchunk = 0;
+    for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) ++nchunk;
+    double best_t = 0.0;
+    int best_i = -1;
+    bool active = false;
+    for (int i = wave; i < nsplit + nchunk; i += kWaves) {
+      const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
+      const int64_t v = i < nsplit ? (int64_t(1) << i)
+                                   : static_cast<int64_t>(p.chunk_min) << (i - nsplit);
+      PlanShape f;
+      bool bad = false;
+      for (int b = lane; b < a.B; b += 64) shape_add_row(f, plan_row_pages(a, b, &bad), a.Hkv, m, v);
+      f.T = wave_sum64(f.T);
+      f.P = wave_sum64(f.P);
+      f.pmax = wave_max64(f.pmax);
+      f.maxS = wave_max64(f.maxS);
+      active = f.P > 0;
+      const double t = model_us(p, f, a.num_cus, a.head_dim, a.page_size,
+                                f.maxS > p.fuse_max_splits);
+      if (best_i < 0 || t < best_t) {
+        best_t = t;
+        best_i = i;
+      }
+    }
+    if (lane == 0) {
+      s_best_t[wave] = best_t;
+      s_best_i[wave] = best_i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int bi = -1;
+      double bt = 0.0;
+      for (int w = 0; w < kWaves; ++w) {
+        const int i = s_best_i[w];
+        if (i < 0) continue;
+        const double t = s_best_t[w];
+        if (bi < 0 || t < bt || (t == bt && i < bi)) {
+          bi = i;
+          bt = t;
+        }
+      }
+      if (!active || bi < 0) {
+        s_pick[0] = PKV_MODE_SPLIT;
+        s_pick[1] = 1;
+      } else if (bi < nsplit) {
+        s_pick[0] = PKV_MODE_SPLIT;
+        s_pick[1] = 1 << bi;
+      } else {
+        s_pick[0] = PKV_MODE_WORKQUEUE;
+        s_pick[1] = p.chunk_min << (bi - nsplit);
+      }
+    }
+    __syncthreads();
+    mode = s_pick[0];
+    param = s_pick[1];
+  }
+
+  // ---- 2. split offsets and records, 256 rows at a time
+  int carry = 0;
+  int64_t maxS = 0;
+  for (int base = 0; base < a.B; base += kThreads) {
+    const int b = base + tid;
+    int S = 0, c = 0;
+    if (b < a.B) {
+      bool bad = false;
+      const int64_t n = plan_row_pages(a, b, &bad);
+      if (bad) s_bad = 1;
+      if (n > 0) {
+        c = static_cast<int>(mode == PKV_MODE_SPLIT ? cdiv(n, param) : param);
+        S = static_cast<int>(cdiv(n, c));
+      }
+    }
+    if (S > maxS) maxS = S;
+    s_S[tid] = S;
+    s_c[tid] = c;
+    s_scan[tid] = S;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {   // inclusive scan
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const int excl = carry + s_scan[tid] - S;
+    if (b < a.B) a.offs[b] = excl;
+    const int rows = a.B - base < kThreads ? a.B - base : kThreads;
+    for (int r = 0; r < rows; ++r) {
+      const int Sr = s_S[r];
+      const int cr = s_c[r];
+      const int o = carry + s_scan[r] - Sr;
+      const int64_t t0 = static_cast<int64_t>(a.Hkv) * o;
+      for (int i = tid; i < a.Hkv * Sr; i += kThreads) {
+        const int g = i / Sr;
+        const int sp = i - g * Sr;
+        a.tasks[t0 + i] = int4{base + r, g, sp, cr};
+      }
+    }
+    carry += s_scan[kThreads - 1];
+    __syncthreads();   // the chunk's LDS is reused
+  }
+  if (tid == 0) a.offs[a.B] = carry;
+
+  // ---- 3. header
+  maxS = wave_max64(maxS);
+  if (lane == 0) s_best_i[wave] = static_cast<int>(maxS);
+  __syncthreads();
+  if (tid == 0) {
+    int deep = 0;
+    for (int w = 0; w < kWaves; ++w) deep = s_best_i[w] > deep ? s_best_i[w] : deep;
+    const int T = a.Hkv * carry;
+    a.hdr[0] = T;
+    a.hdr[1] = (T == 0 || (deep <= a.pol.fuse_max_splits && a.groups_fit)) ? 1 : 0;
+    a.hdr[2] = mode;
+    a.hdr[3] = param;
+    a.hdr[4] = carry;
+    a.hdr[5] = deep;
+    a.hdr[6] = s_bad;
+    if (s_bad) flag_error(a.ctrl, PKV_DEVERR_ROW);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -768,8 +986,9 @@ int num_cus_of_current_device(int* cus) {
 }
 
 template <int D>
-int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream) {
-  if (da.num_tasks > 0) {
+int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
+           bool decode) {
+  if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     if (da.B <= kRowStage)
       hipLaunchKernelGGL((pkv_decode_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, da,
@@ -933,7 +1152,10 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
   }
   if (!do_merge) ma.B = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return head_dim == 128 ? pkv::launch<128>(da, ma, grid, s) : pkv::launch<64>(da, ma, grid, s);
+  const bool decode = da.num_tasks > 0;
+  da.task_cap = da.num_tasks > 0 ? da.num_tasks : 1;
+  return head_dim == 128 ? pkv::launch<128>(da, ma, grid, s, decode)
+                         : pkv::launch<64>(da, ma, grid, s, decode);
 }
 
 }  // namespace
@@ -968,6 +1190,168 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
   return run(nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, 0, split_offsets,
              num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, 1.0f, out, lse, workspace,
              workspace_bytes, stream, false, true, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Layout of the device-planned workspace: the ordinary workspace for
+// B * max_splits partial slots, then the plan area: the header (64 B), the
+// split offsets (B+1, padded to 16 B), the task records.
+struct DevicePlanLayout {
+  int64_t slot_cap = 0, task_cap = 0;
+  size_t plan_off = 0, offs_off = 0, tasks_off = 0, bytes = 0;
+};
+
+int device_plan_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t max_splits,
+                       DevicePlanLayout* L) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || head_dim < 1 || max_splits < 1) return PKV_ERR_INVALID_ARG;
+  L->slot_cap = static_cast<int64_t>(B) * max_splits;
+  L->task_cap = L->slot_cap * Hkv;
+  if (L->task_cap > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  size_t ws = 0;
+  const int st = pkv_workspace_size(L->slot_cap, Hq, head_dim, &ws);
+  if (st != PKV_OK) return st;
+  L->plan_off = ws;
+  L->offs_off = ws + pkv::kPlanHdrInts * sizeof(int32_t);
+  const size_t offs_bytes = ((static_cast<size_t>(B) + 1) * sizeof(int32_t) + 15) & ~size_t(15);
+  L->tasks_off = L->offs_off + offs_bytes;
+  const size_t task_bytes = static_cast<size_t>(L->task_cap > 0 ? L->task_cap : 1) * 16;
+  L->bytes = (L->tasks_off + task_bytes + 255) & ~size_t(255);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_workspace_size_device_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                   int32_t max_splits, size_t* bytes) {
+  if (!bytes) return PKV_ERR_INVALID_ARG;
+  DevicePlanLayout L;
+  const int st = device_plan_layout(B, Hq, Hkv, head_dim, max_splits, &L);
+  if (st != PKV_OK) return st;
+  *bytes = L.bytes;
+  return PKV_OK;
+}
+
+int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool,
+                           int64_t num_pages, const int32_t* block_table,
+                           int32_t max_pages_per_row, const int32_t* seq_lens, int32_t B,
+                           int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                           float scale, int32_t mode, int32_t param, int32_t max_splits,
+                           const pkv_policy_params* policy, int32_t num_cus, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_policy_params pol;
+  if (policy) {
+    pol = *policy;
+  } else {
+    pkv_policy_defaults(&pol);
+  }
+  if (mode < -1 || mode > PKV_MODE_WORKQUEUE || max_splits < 1 || max_pages_per_row < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (pol.split_max < 1 || pol.chunk_min < 1 || pol.chunk_max < pol.chunk_min ||
+      pol.fuse_max_splits < 0 || !(pol.cu_gbps > 0.0) || !(pol.hbm_gbps > 0.0))
+    return PKV_ERR_INVALID_ARG;
+  // Capacity: no row may get more than max_splits splits.  Checked on the
+  // host from max_pages_per_row alone, so the device never overruns.
+  const int64_t M = max_pages_per_row;
+  if (mode == PKV_MODE_SPLIT && (param < 1 || param > max_splits)) return PKV_ERR_INVALID_ARG;
+  if (mode == PKV_MODE_WORKQUEUE && (param < 1 || pkv::cdiv(M, param) > max_splits))
+    return PKV_ERR_INVALID_ARG;
+  if (mode < 0) {
+    // the candidate sets, limited to the capacity
+    if (pol.split_max > max_splits) pol.split_max = max_splits;
+    int64_t c = pol.chunk_min;
+    while (c <= pol.chunk_max && pkv::cdiv(M, c) > max_splits) c *= 2;
+    if (c > pol.chunk_max) {
+      pol.chunk_min = pol.chunk_max + 1;   // no workqueue candidate fits
+    } else {
+      pol.chunk_min = static_cast<int32_t>(c);
+    }
+  }
+  DevicePlanLayout L;
+  int st = device_plan_layout(B, Hq, Hkv, head_dim, max_splits, &L);
+  if (st != PKV_OK || B == 0) return st;
+  if (!workspace || !out || !seq_lens) return PKV_ERR_INVALID_ARG;
+  if (workspace_bytes < L.bytes) return PKV_ERR_BUFFER_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* hdr = reinterpret_cast<int32_t*>(ws + L.plan_off);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + L.offs_off);
+  int32_t* tasks = reinterpret_cast<int32_t*>(ws + L.tasks_off);
+
+  pkv::DecodeArgs da{};
+  pkv::MergeArgs ma{};
+  st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
+               L.task_cap, offs, L.slot_cap, B, Hq, Hkv, head_dim, page_size, scale, out, lse,
+               workspace, workspace_bytes, true, &da, &ma);
+  if (st != PKV_OK || B == 0) return st;
+  if (num_cus <= 0) {
+    st = pkv::num_cus_of_current_device(&num_cus);
+    if (st != PKV_OK) return st;
+  }
+  pkv::PlanArgs pa{};
+  pa.seq_lens = seq_lens;
+  pa.B = B;
+  pa.Hkv = Hkv;
+  pa.head_dim = head_dim;
+  pa.page_size = page_size;
+  pa.num_cus = num_cus;
+  pa.max_pages = max_pages_per_row;
+  pa.mode = mode;
+  pa.param = param;
+  pa.groups_fit = static_cast<int64_t>(B) * Hkv <= PKV_MAX_FUSED_GROUPS ? 1 : 0;
+  pa.pol = pol;
+  pa.hdr = hdr;
+  pa.offs = offs;
+  pa.tasks = reinterpret_cast<int4*>(tasks);
+  pa.ctrl = da.ctrl;
+  da.plan_hdr = hdr;
+  da.task_cap = static_cast<int32_t>(L.task_cap > 0 ? L.task_cap : 1);
+  da.num_tasks = 0;
+  ma.plan_hdr = hdr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(pkv::pkv_plan_kernel, dim3(1), dim3(pkv::kThreads), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    pkv::set_hip_error(static_cast<int>(e));
+    return PKV_ERR_HIP;
+  }
+  // The task count is known only on the device: a full persistent grid,
+  // whose workgroups past the count exit at once.
+  const int grid = 2 * num_cus;
+  return head_dim == 128 ? pkv::launch<128>(da, ma, grid, s, true)
+                         : pkv::launch<64>(da, ma, grid, s, true);
+}
+
+int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t head_dim, int32_t max_splits, int32_t* header,
+                         int32_t* split_offsets, int32_t* tasks, int64_t task_capacity,
+                         void* stream) {
+  if (!workspace || !header) return PKV_ERR_INVALID_ARG;
+  DevicePlanLayout L;
+  int st = device_plan_layout(B, Hq, Hkv, head_dim, max_splits, &L);
+  if (st != PKV_OK) return st;
+  if (workspace_bytes < L.bytes) return PKV_ERR_BUFFER_TOO_SMALL;
+  const char* ws = static_cast<const char*>(workspace);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = hipMemcpy(header, ws + L.plan_off, 8 * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && split_offsets)
+    e = hipMemcpy(split_offsets, ws + L.offs_off, (static_cast<size_t>(B) + 1) * sizeof(int32_t),
+                  hipMemcpyDeviceToHost);
+  if (e == hipSuccess && tasks) {
+    if (header[0] < 0 || header[0] > task_capacity) return PKV_ERR_BUFFER_TOO_SMALL;
+    if (header[0] > 0)
+      e = hipMemcpy(tasks, ws + L.tasks_off, static_cast<size_t>(header[0]) * 16,
+                    hipMemcpyDeviceToHost);
+  }
+  if (e != hipSuccess) {
+    pkv::set_hip_error(static_cast<int>(e));
+    return PKV_ERR_HIP;
+  }
+  return PKV_OK;
 }
 
 }  // extern "C"

@@ -8,6 +8,7 @@
 
 #include "pkv.h"
 #include "internal.h"
+#include "policy_model.h"
 
 #include <cstdint>
 #include <cstring>
@@ -67,58 +68,17 @@ int pkv_policy_defaults(pkv_policy_params* p) {
 
 namespace {
 
-// What the cost model needs to know about a candidate plan.
-struct PlanShape {
-  int64_t T = 0;      // tasks
-  int64_t P = 0;      // page tiles (page x KV head) in all
-  int64_t pmax = 0;   // pages of the largest task
-  int64_t maxS = 0;   // splits of the deepest row
-};
+using pkv::PlanShape;
 
 PlanShape plan_shape(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t page_size,
                      int32_t mode, int64_t param) {
   PlanShape f;
-  for (int32_t b = 0; b < B; ++b) {
-    const int64_t n = ceil_div(seq_lens[b], page_size);
-    if (n == 0) continue;
-    const int64_t c = mode == PKV_MODE_SPLIT ? ceil_div(n, param) : param;
-    const int64_t S = ceil_div(n, c);
-    f.T += Hkv * S;
-    f.P += Hkv * n;
-    const int64_t largest = c < n ? c : n;
-    if (largest > f.pmax) f.pmax = largest;
-    if (S > f.maxS) f.maxS = S;
-  }
+  for (int32_t b = 0; b < B; ++b)
+    pkv::shape_add_row(f, ceil_div(seq_lens[b], page_size), Hkv, mode, param);
   return f;
 }
 
-// The model of pkv_policy (include/pkv.h), in the documented order of
-// operations.  This file is compiled without floating-point contraction, so
-// every product and sum is rounded on its own.
-double model_us(const pkv_policy_params& p, const PlanShape& f, int32_t num_cus,
-                int32_t head_dim, int32_t page_size, bool two) {
-  if (f.T == 0) return p.t0_us;
-  const int64_t W = f.T < 2 * static_cast<int64_t>(num_cus) ? f.T : 2 * static_cast<int64_t>(num_cus);
-  const int64_t A = W < num_cus ? W : num_cus;
-  const double share = p.hbm_gbps / static_cast<double>(A);
-  const double rho = share < p.cu_gbps ? share : p.cu_gbps;
-  double load;
-  if (f.T <= W) {
-    load = static_cast<double>(ceil_div(f.T, A) * f.pmax);
-  } else {
-    load = static_cast<double>(f.P) / static_cast<double>(A) +
-           p.alpha * static_cast<double>(f.pmax);
-  }
-  const double tile = 2.0 * page_size * head_dim * 2.0;
-  double t = p.t0_us + p.t_round_us * static_cast<double>(ceil_div(f.T, W)) +
-             load * tile / (rho * 1e3);
-  if (two) {
-    t = t + p.t_two_us + p.t_two_split_us * static_cast<double>(f.maxS);
-  } else {
-    t = t + p.t_fused_split_us * static_cast<double>(f.maxS);
-  }
-  return t;
-}
+using pkv::model_us;
 
 int check_policy_args(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
                       int32_t page_size, int32_t num_cus, const pkv_policy_params& p) {

@@ -254,6 +254,31 @@ def test_decode_rejects_bad_scalars_before_touching_the_device():
     del common
 
 
+def test_device_plan_workspace_size_and_host_checks():
+    """pkv_decode_device_plan's capacity checks run on the host, before any
+    device call (so they work here without a GPU)."""
+    hdr_bytes, B, Hq, Hkv, D, cap = 64, 8, 32, 8, 128, 16
+    n = pkv.pkv_workspace_size_device_plan(B, Hq, Hkv, D, cap)
+    base = pkv.pkv_workspace_size(B * cap, Hq, D)
+    assert n % 256 == 0
+    assert n >= base + hdr_bytes + ((B + 1) * 4 + 15) // 16 * 16 + Hkv * B * cap * 16
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_workspace_size_device_plan(B, Hq, Hkv, D, 0)
+    lib = pkv._load()
+
+    def call(mode, param, max_splits, B=2, maxp=1024):
+        return lib.pkv_decode_device_plan(None, None, None, 0, None, maxp, None, B, 32, 8, 128, 16,
+                                          0.1, mode, param, max_splits, None, 256, None, None,
+                                          None, 0, None)
+    assert call(-1, 0, 8, B=0) == pkv.PKV_OK                   # nothing to do
+    assert call(2, 1, 8) == pkv.PKV_ERR_INVALID_ARG            # unknown mode
+    assert call(-1, 0, 0) == pkv.PKV_ERR_INVALID_ARG           # no capacity
+    assert call(0, 16, 8) == pkv.PKV_ERR_INVALID_ARG           # S = 16 > 8 splits
+    assert call(1, 4, 8) == pkv.PKV_ERR_INVALID_ARG            # 1024 / 4 = 256 splits > 8
+    assert call(1, 128, 8) == pkv.PKV_ERR_INVALID_ARG          # fits, but null pointers
+    assert call(-1, 0, 8) == pkv.PKV_ERR_INVALID_ARG           # null pointers
+
+
 def test_step_args_layout_matches_c(tmp_path):
     """The ctypes mirror of pkv_step_args has the C field offsets and size."""
     import shutil

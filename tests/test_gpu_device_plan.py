@@ -1,0 +1,186 @@
+"""GPU: the device-side planner (pkv_decode_device_plan).
+
+The plan the planner kernel writes must equal the host planner's, bit for bit,
+and the policy it evaluates on the device must take the host policy's
+decision (both limited to the capacity).  The outputs are checked against the
+float64 oracle like every other schedule.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import check_close, check_lse, log_case, oracle_rows
+from workloads import CALIBRATION_SEED, CONFIGS, HELD_OUT_SEEDS, Config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SEED = HELD_OUT_SEEDS[0]
+
+
+def _capped_params(pkv, max_pages, cap):
+    """The host policy's candidate sets limited the way the device path limits them."""
+    p = pkv.pkv_policy_defaults()
+    p.split_max = min(p.split_max, cap)
+    c = p.chunk_min
+    while c <= p.chunk_max and -(-max_pages // c) > cap:
+        c *= 2
+    p.chunk_min = c
+    return p
+
+
+def _run(wl, cap, mode=-1, param=0, workspace=None):
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    cfg = wl.cfg
+    B = len(wl.seq_lens_np)
+    need = pkv.pkv_workspace_size_device_plan(B, cfg.Hq, cfg.Hkv, cfg.D, cap)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        pkv.pkv_workspace_init(workspace)
+    out = torch.full_like(wl.q, float("nan"))
+    lse = torch.full((B, cfg.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.pkv_decode_device_plan(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, cfg.scale,
+                               out, workspace, cap, lse=lse, mode=mode, param=param)
+    torch.cuda.synchronize()
+    hdr, tasks, offs = pkv.pkv_device_plan_read(workspace, B, cfg.Hq, cfg.Hkv, cfg.D, cap)
+    return out, lse, hdr, tasks, offs, workspace
+
+
+def _check_plan(wl, cap, hdr, tasks, offs, mode, param):
+    import paged_gqa_decode_pkv_amd as pkv
+    cfg = wl.cfg
+    maxp = wl.block_table_np.shape[1]
+    if mode < 0:
+        p = _capped_params(pkv, maxp, cap)
+        if p.chunk_min <= p.chunk_max:
+            want = pkv.pkv_policy(wl.seq_lens_np, cfg.Hkv, _num_cus(), params=p, head_dim=cfg.D)
+        else:
+            # no workqueue schedule fits: the first fastest split candidate
+            best = None
+            S = 1
+            while S <= p.split_max:
+                t = pkv.pkv_policy_predict(wl.seq_lens_np, cfg.Hkv, _num_cus(), 0, S,
+                                           head_dim=cfg.D)
+                if best is None or t < best[0]:
+                    best = (t, (0, S))
+                S *= 2
+            want = best[1]
+        assert (hdr["mode"], hdr["param"]) == want
+        mode, param = want
+    assert (hdr["mode"], hdr["param"]) == (mode, param)
+    rt, ro, slots = pkv.pkv_plan(wl.seq_lens_np, cfg.Hkv, maxp, mode, param)
+    assert np.array_equal(tasks, rt)
+    assert np.array_equal(offs, ro)
+    assert hdr["num_tasks"] == len(rt) and hdr["num_partial_slots"] == slots
+    deepest = int(np.max(np.diff(ro))) if len(ro) > 1 else 0
+    assert hdr["max_splits"] == deepest
+    assert hdr["fused"] == int(len(rt) == 0 or deepest <= 16)
+    assert hdr["row_flagged"] == 0
+
+
+def _num_cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _parity(wl, out, lse, rows=None):
+    ref_out, ref_lse = oracle_rows(wl, rows)
+    sel = slice(None) if rows is None else list(rows)
+    check_close(out.float().cpu().numpy()[sel], ref_out)
+    check_lse(lse.cpu().numpy()[sel], ref_lse)
+
+
+@pytest.mark.parametrize("name", ["tiny", "b1", "b1_bucketed", "b4_bimodal", "b8_bimodal",
+                                  "b8_zipf", "b8_uniform"])
+def test_device_policy_plan_and_parity(name):
+    import paged_gqa_decode_pkv_amd as pkv
+    wl = make_workload(name, SEED, device="cuda")
+    log_case("device plan", name, "seed", SEED)
+    out, lse, hdr, tasks, offs, ws = _run(wl, cap=256)
+    _check_plan(wl, 256, hdr, tasks, offs, -1, 0)
+    _parity(wl, out, lse)
+    assert pkv.pkv_workspace_error_flags(ws) == 0
+
+
+@pytest.mark.parametrize("mode,param", [(0, 1), (0, 8), (0, 64), (1, 4), (1, 32), (1, 256)])
+def test_device_plan_explicit_schedules(mode, param):
+    wl = make_workload("b8_bimodal", CALIBRATION_SEED, device="cuda")
+    cap = 256
+    log_case("device plan explicit", mode, param)
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap, mode, param)
+    _check_plan(wl, cap, hdr, tasks, offs, mode, param)
+    _parity(wl, out, lse)
+
+
+def test_device_policy_under_a_small_capacity():
+    """max_splits = 4: the device policy only sees schedules that fit, and
+    takes the host policy's decision over the same limited candidates."""
+    wl = make_workload("b1", SEED, device="cuda")
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap=4)
+    _check_plan(wl, 4, hdr, tasks, offs, -1, 0)
+    assert hdr["max_splits"] <= 4
+    _parity(wl, out, lse)
+
+
+@pytest.mark.parametrize("G,D", [(1, 64), (2, 128), (8, 128), (4, 64)])
+def test_device_plan_ragged_edge_rows(G, D):
+    lens = [1, 15, 16, 17, 33, 0, 127, 128, 4000, 0]
+    cfg = Config(f"ragged_dp_G{G}_d{D}", B=len(lens), Hq=2 * G, Hkv=2, D=D,
+                 max_pages_per_row=256, pool_pages=600, lengths=None)
+    wl = make_workload(cfg, SEED, device="cuda", seq_lens=lens)
+    log_case("device plan ragged", G, D)
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap=64)
+    _check_plan(wl, 64, hdr, tasks, offs, -1, 0)
+    _parity(wl, out, lse)
+
+
+def test_device_plan_all_rows_empty():
+    import torch
+    lens = [0, 0, 0]
+    cfg = Config("empty_dp", B=3, Hq=8, Hkv=2, D=128, max_pages_per_row=4, pool_pages=16,
+                 lengths=None)
+    wl = make_workload(cfg, SEED, device="cuda", seq_lens=lens)
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap=8)
+    assert hdr["num_tasks"] == 0 and hdr["fused"] == 1
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_device_plan_reused_workspace_new_lengths():
+    """One workspace, steps with different device lengths (and so different
+    plans and policy choices): every step matches the oracle."""
+    ws = None
+    for seed in HELD_OUT_SEEDS[:3]:
+        for name in ("b8_bimodal", "b4_bimodal"):
+            wl = make_workload(name, seed, device="cuda")
+            log_case("device plan reuse", name, seed)
+            out, lse, hdr, tasks, offs, ws = _run(wl, cap=256, workspace=ws)
+            _check_plan(wl, 256, hdr, tasks, offs, -1, 0)
+            _parity(wl, out, lse)
+
+
+def test_device_plan_flags_overlong_row_and_plans_it_empty():
+    """A length beyond max_pages_per_row * 16 is caught by the planner's own
+    bounds check: that row comes out empty and the error word is set; the
+    other rows are exact."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    lens = [100, 300, 50]
+    cfg = Config("overlong_dp", B=3, Hq=8, Hkv=2, D=128, max_pages_per_row=32, pool_pages=128,
+                 lengths=None)
+    wl = make_workload(cfg, SEED, device="cuda", seq_lens=lens)
+    bad = wl.seq_lens.clone()
+    bad[1] = 32 * 16 + 1                      # one token past the table
+    B = 3
+    need = pkv.pkv_workspace_size_device_plan(B, cfg.Hq, cfg.Hkv, cfg.D, 8)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    pkv.pkv_workspace_init(ws)
+    out = torch.full_like(wl.q, float("nan"))
+    lse = torch.full((B, cfg.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.pkv_decode_device_plan(wl.q, wl.k_pool, wl.v_pool, wl.block_table, bad, cfg.scale, out,
+                               ws, 8, lse=lse)
+    torch.cuda.synchronize()
+    hdr, _, offs = pkv.pkv_device_plan_read(ws, B, cfg.Hq, cfg.Hkv, cfg.D, 8)
+    assert hdr["row_flagged"] == 1 and offs[2] - offs[1] == 0
+    assert pkv.pkv_workspace_error_flags(ws) & pkv.PKV_DEVERR_ROW
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    _parity(wl, out, lse, rows=[0, 2])
