@@ -346,11 +346,13 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
  *      (split_max <= max_splits; workqueue chunks c with
  *      ceil(max_pages_per_row / c) <= max_splits); then it writes the same
  *      split_offsets and task records as pkv_plan, and a header;
- *   2. the persistent decode kernel, 2 * num_cus workgroups, reading the
- *      task count from the header;
+ *   2. the persistent decode kernel, num_cus workgroups, reading the task
+ *      count from the header;
  *   3. the merge kernel, which returns at once when the header says the
  *      decode kernel merged (the fused form: no row deeper than
- *      policy->fuse_max_splits and B * Hkv <= PKV_MAX_FUSED_GROUPS).
+ *      policy->fuse_max_splits and B * Hkv <= PKV_MAX_FUSED_GROUPS).  It is
+ *      not launched when max_splits <= fuse_max_splits (every plan is then
+ *      fused): two launches per step.
  * Arguments as for pkv_decode, except:
  *   seq_lens     device int32 [B]; a row with N_b < 0 or needing more than
  *                max_pages_per_row pages is planned as empty (out = 0,

@@ -767,9 +767,9 @@ __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
 // (gist.science explainer): the same candidate search and time model as
 // pkv_policy (policy_model.h), and the same records, offsets and order as
 // pkv_plan, computed by one workgroup:
-//   1. policy (mode < 0): each wave evaluates every 4th candidate over all
-//      rows (lanes stride the rows; wave reductions), lane 0 evaluates the
-//      model; the earliest fastest candidate wins.
+//   1. policy (mode < 0): 16 candidates at a time, each over 16 groups of
+//      rows in parallel; 16 threads evaluate the model; the earliest fastest
+//      candidate wins.
 //   2. rows in chunks of 256: S_b per thread, an exclusive scan in LDS gives
 //      split_offsets; then, row by row, all threads write the row's records.
 //   3. the header: tasks, fused or not, mode, param, slots, deepest row.
@@ -790,24 +790,34 @@ struct PlanArgs {
 };
 
 constexpr int kPlanHdrInts = 16;
+constexpr int kPlanStage = 4096;   // rows whose page counts the planner keeps in LDS
+constexpr int kCandBatch = 16;     // policy candidates evaluated together
+constexpr int kCandGroups = kThreads / kCandBatch;
 
-__device__ __forceinline__ int64_t plan_row_pages(const PlanArgs& a, int b, bool* bad) {
+__device__ __forceinline__ uint32_t cdiv32(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+// Pages of row b, or -1 for a row to flag (N_b < 0 or more than max_pages
+// pages).  Read from global memory; the planner stages the first kPlanStage.
+__device__ __forceinline__ int32_t plan_row_pages_global(const PlanArgs& a, int b) {
   const int32_t N = a.seq_lens[b];
-  if (N < 0) {
-    *bad = true;
-    return 0;
-  }
-  const int64_t n = cdiv(N, a.page_size);
-  if (n > a.max_pages) {
-    *bad = true;
-    return 0;
-  }
-  return n;
+  if (N < 0) return -1;
+  const int64_t n = (static_cast<int64_t>(N) + a.page_size - 1) / a.page_size;
+  return n > a.max_pages ? -1 : static_cast<int32_t>(n);
 }
 
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Add one row of n pages to the plan shape (mode, param): the arithmetic of
+// shape_add_row in 32 bits (n, c, S fit) with 64-bit sums.
+__device__ __forceinline__ void plan_shape_add(PlanShape& f, int32_t n, int32_t Hkv, int m,
+                                               uint32_t v) {
+  if (n <= 0) return;
+  const uint32_t un = static_cast<uint32_t>(n);
+  const uint32_t c = m == PKV_MODE_SPLIT ? cdiv32(un, v) : v;
+  const uint32_t S = cdiv32(un, c);
+  f.T += static_cast<int64_t>(Hkv) * S;
+  f.P += static_cast<int64_t>(Hkv) * un;
+  const int64_t largest = c < un ? c : un;
+  if (largest > f.pmax) f.pmax = largest;
+  if (static_cast<int64_t>(S) > f.maxS) f.maxS = S;
 }
 
 __device__ __forceinline__ int64_t wave_max64(int64_t v) {
@@ -819,7 +829,13 @@ __device__ __forceinline__ int64_t wave_max64(int64_t v) {
 }
 
 __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
-  __shared__ double s_best_t[kWaves];
+  __shared__ int32_t s_n[kPlanStage];
+  __shared__ int64_t s_cT[kCandGroups][kCandBatch];
+  __shared__ int64_t s_cP[kCandGroups][kCandBatch];
+  __shared__ int64_t s_cpmax[kCandGroups][kCandBatch];
+  __shared__ int64_t s_cmaxS[kCandGroups][kCandBatch];
+  __shared__ double s_ct[kCandBatch];
+  __shared__ int64_t s_cpages;
   __shared__ int s_best_i[kWaves];
   __shared__ int s_scan[kThreads];
   __shared__ int s_S[kThreads];
@@ -829,10 +845,28 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int staged = a.B < kPlanStage ? a.B : kPlanStage;
+
+  // ---- 0. page counts of the rows, once
+  int bad = 0;
+  for (int b = tid; b < staged; b += kThreads) {
+    const int32_t n = plan_row_pages_global(a, b);
+    bad |= n < 0;
+    s_n[b] = n < 0 ? 0 : n;
+  }
+  for (int b = staged + tid; b < a.B; b += kThreads) bad |= plan_row_pages_global(a, b) < 0;
   if (tid == 0) s_bad = 0;
   __syncthreads();
+  if (bad) s_bad = 1;
+  auto row_n = [&](int b) -> int32_t {
+    if (b < kPlanStage) return s_n[b];
+    const int32_t n = plan_row_pages_global(a, b);
+    return n < 0 ? 0 : n;
+  };
 
-  // ---- 1. policy
+  // ---- 1. policy: candidates in batches of 16; thread (candidate j, group
+  // r) folds rows r, r+16, ... into a plan shape; 16 threads then sum the
+  // groups, evaluate the model, and thread 0 keeps the first fastest.
   int mode = a.mode, param = a.param;
   if (mode < 0) {
     const pkv_policy_params& p = a.pol;
@@ -840,54 +874,59 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
     for (int64_t S = 1; S <= p.split_max; S *= 2) ++nsplit;
     int nchunk = 0;
     for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) ++nchunk;
+    const int ncand = nsplit + nchunk;
+    const int j = tid % kCandBatch;
+    const int grp = tid / kCandBatch;
     double best_t = 0.0;
     int best_i = -1;
-    bool active = false;
-    for (int i = wave; i < nsplit + nchunk; i += kWaves) {
-      const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
-      const int64_t v = i < nsplit ? (int64_t(1) << i)
-                                   : static_cast<int64_t>(p.chunk_min) << (i - nsplit);
+    int64_t total_pages = 0;
+    for (int cb = 0; cb < ncand; cb += kCandBatch) {
+      const int i = cb + j;
       PlanShape f;
-      bool bad = false;
-      for (int b = lane; b < a.B; b += 64) shape_add_row(f, plan_row_pages(a, b, &bad), a.Hkv, m, v);
-      f.T = wave_sum64(f.T);
-      f.P = wave_sum64(f.P);
-      f.pmax = wave_max64(f.pmax);
-      f.maxS = wave_max64(f.maxS);
-      active = f.P > 0;
-      const double t = model_us(p, f, a.num_cus, a.head_dim, a.page_size,
-                                f.maxS > p.fuse_max_splits);
-      if (best_i < 0 || t < best_t) {
-        best_t = t;
-        best_i = i;
+      if (i < ncand) {
+        const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
+        const uint32_t v = i < nsplit ? (1u << i)
+                                      : static_cast<uint32_t>(p.chunk_min) << (i - nsplit);
+        for (int b = grp; b < a.B; b += kCandGroups) plan_shape_add(f, row_n(b), a.Hkv, m, v);
       }
-    }
-    if (lane == 0) {
-      s_best_t[wave] = best_t;
-      s_best_i[wave] = best_i;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int bi = -1;
-      double bt = 0.0;
-      for (int w = 0; w < kWaves; ++w) {
-        const int i = s_best_i[w];
-        if (i < 0) continue;
-        const double t = s_best_t[w];
-        if (bi < 0 || t < bt || (t == bt && i < bi)) {
-          bi = i;
-          bt = t;
+      s_cT[grp][j] = f.T;
+      s_cP[grp][j] = f.P;
+      s_cpmax[grp][j] = f.pmax;
+      s_cmaxS[grp][j] = f.maxS;
+      __syncthreads();
+      if (tid < kCandBatch && i < ncand) {
+        PlanShape F;
+        for (int r = 0; r < kCandGroups; ++r) {
+          F.T += s_cT[r][j];
+          F.P += s_cP[r][j];
+          F.pmax = s_cpmax[r][j] > F.pmax ? s_cpmax[r][j] : F.pmax;
+          F.maxS = s_cmaxS[r][j] > F.maxS ? s_cmaxS[r][j] : F.maxS;
+        }
+        s_ct[j] = model_us(p, F, a.num_cus, a.head_dim, a.page_size, F.maxS > p.fuse_max_splits);
+        if (j == 0) s_cpages = F.P;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        total_pages = s_cpages;
+        for (int k = 0; k < kCandBatch && cb + k < ncand; ++k) {
+          if (best_i < 0 || s_ct[k] < best_t) {
+            best_t = s_ct[k];
+            best_i = cb + k;
+          }
         }
       }
-      if (!active || bi < 0) {
+      __syncthreads();   // s_c* are rewritten by the next batch
+    }
+    if (tid == 0) {
+      if (total_pages == 0 || best_i < 0) {
         s_pick[0] = PKV_MODE_SPLIT;
         s_pick[1] = 1;
-      } else if (bi < nsplit) {
+      } else if (best_i < nsplit) {
         s_pick[0] = PKV_MODE_SPLIT;
-        s_pick[1] = 1 << bi;
+        s_pick[1] = 1 << best_i;
       } else {
         s_pick[0] = PKV_MODE_WORKQUEUE;
-        s_pick[1] = p.chunk_min << (bi - nsplit);
+        s_pick[1] = p.chunk_min << (best_i - nsplit);
       }
     }
     __syncthreads();
@@ -897,20 +936,18 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
 
   // ---- 2. split offsets and records, 256 rows at a time
   int carry = 0;
-  int64_t maxS = 0;
+  int maxS = 0;
   for (int base = 0; base < a.B; base += kThreads) {
     const int b = base + tid;
     int S = 0, c = 0;
     if (b < a.B) {
-      bool bad = false;
-      const int64_t n = plan_row_pages(a, b, &bad);
-      if (bad) s_bad = 1;
+      const uint32_t n = static_cast<uint32_t>(row_n(b));
       if (n > 0) {
-        c = static_cast<int>(mode == PKV_MODE_SPLIT ? cdiv(n, param) : param);
-        S = static_cast<int>(cdiv(n, c));
+        c = static_cast<int>(mode == PKV_MODE_SPLIT ? cdiv32(n, param) : param);
+        S = static_cast<int>(cdiv32(n, c));
       }
     }
-    if (S > maxS) maxS = S;
+    maxS = S > maxS ? S : maxS;
     s_S[tid] = S;
     s_c[tid] = c;
     s_scan[tid] = S;
@@ -921,14 +958,12 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
       s_scan[tid] += v;
       __syncthreads();
     }
-    const int excl = carry + s_scan[tid] - S;
-    if (b < a.B) a.offs[b] = excl;
+    if (b < a.B) a.offs[b] = carry + s_scan[tid] - S;
     const int rows = a.B - base < kThreads ? a.B - base : kThreads;
     for (int r = 0; r < rows; ++r) {
       const int Sr = s_S[r];
       const int cr = s_c[r];
-      const int o = carry + s_scan[r] - Sr;
-      const int64_t t0 = static_cast<int64_t>(a.Hkv) * o;
+      const int64_t t0 = static_cast<int64_t>(a.Hkv) * (carry + s_scan[r] - Sr);
       for (int i = tid; i < a.Hkv * Sr; i += kThreads) {
         const int g = i / Sr;
         const int sp = i - g * Sr;
@@ -941,8 +976,8 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   if (tid == 0) a.offs[a.B] = carry;
 
   // ---- 3. header
-  maxS = wave_max64(maxS);
-  if (lane == 0) s_best_i[wave] = static_cast<int>(maxS);
+  const int deep_w = static_cast<int>(wave_max64(maxS));
+  if (lane == 0) s_best_i[wave] = deep_w;
   __syncthreads();
   if (tid == 0) {
     int deep = 0;
@@ -1318,9 +1353,13 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
     pkv::set_hip_error(static_cast<int>(e));
     return PKV_ERR_HIP;
   }
-  // The task count is known only on the device: a full persistent grid,
-  // whose workgroups past the count exit at once.
-  const int grid = 2 * num_cus;
+  // The task count is known only on the device: one workgroup per CU (as
+  // fast as two per CU on the measured workloads, and with no pair of
+  // workgroups sharing a CU while others idle); workgroups past the count
+  // exit at once.  With a capacity of at most fuse_max_splits splits per row
+  // every plan is fused, and the merge kernel is not launched at all.
+  const int grid = num_cus;
+  if (max_splits <= pol.fuse_max_splits && pa.groups_fit) ma.B = 0;
   return head_dim == 128 ? pkv::launch<128>(da, ma, grid, s, true)
                          : pkv::launch<64>(da, ma, grid, s, true);
 }
