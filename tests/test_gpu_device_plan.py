@@ -184,3 +184,67 @@ def test_device_plan_flags_overlong_row_and_plans_it_empty():
     assert pkv.pkv_workspace_error_flags(ws) & pkv.PKV_DEVERR_ROW
     assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
     _parity(wl, out, lse, rows=[0, 2])
+
+
+def test_device_plan_step_in_a_graph_follows_new_lengths():
+    """The device-planned step needs nothing from the host, so it can be
+    captured once in a graph and replayed while the lengths in device memory
+    change: every replay equals the eager step on the same lengths, bit for
+    bit, and the oracle."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    cfg = wl.cfg
+    B, cap = cfg.B, 64
+    need = pkv.pkv_workspace_size_device_plan(B, cfg.Hq, cfg.Hkv, cfg.D, cap)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    pkv.pkv_workspace_init(ws)
+    lens_dev = wl.seq_lens.clone()
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((B, cfg.Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        pkv.pkv_decode_device_plan(wl.q, wl.k_pool, wl.v_pool, wl.block_table, lens_dev,
+                                   cfg.scale, out, ws, cap, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    base = wl.seq_lens_np.astype(np.int64)
+    for rep in range(4):
+        # shorter rows only: their pages are already in the block table
+        new = np.maximum(base - rng.integers(0, 3000, size=B), 0).astype(np.int32)
+        if rep == 3:
+            new[:] = 0
+        lens_dev.copy_(torch.from_numpy(new).cuda())
+        torch.cuda.synchronize()
+        log_case("graph replay", rep, new.tolist())
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got, got_lse = out.clone(), lse.clone()
+        out.fill_(float("nan"))
+        step()                                    # eager, same lengths
+        torch.cuda.synchronize()
+        assert torch.equal(got, out) and torch.equal(got_lse, lse)
+        wl_new = _with_lengths(wl, new)
+        ref_out, ref_lse = oracle_rows(wl_new)
+        check_close(got.float().cpu().numpy(), ref_out)
+        check_lse(got_lse.cpu().numpy(), ref_lse)
+    assert pkv.pkv_workspace_error_flags(ws) == 0
+
+
+def _with_lengths(wl, lens):
+    """The same pages and table, shorter lengths (for the oracle)."""
+    import dataclasses
+    import torch
+    return dataclasses.replace(wl, seq_lens_np=np.asarray(lens, dtype=np.int32),
+                               seq_lens=torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda())
