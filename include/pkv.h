@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 /* Fixed-size head of every workspace: control words (task counter, exit
  * counter, error word) and the per-(row, KV head) arrival counters of the
@@ -63,6 +63,13 @@ enum pkv_status {
   PKV_ERR_BUFFER_TOO_SMALL = 3, /* caller buffer too small; size outputs hold the need */
   PKV_ERR_BAD_INDEX = 4,        /* block-table entry outside [0, num_pages) */
   PKV_ERR_HIP = 5               /* a HIP runtime call failed; see pkv_last_hip_error */
+};
+
+/* Element type of q, K, V and out (scores, softmax state and accumulators
+ * are fp32 either way; lse is fp32). */
+enum pkv_dtype {
+  PKV_DTYPE_F16 = 0,   /* IEEE half */
+  PKV_DTYPE_BF16 = 1   /* bfloat16 */
 };
 
 /* Scheduling modes of the task list (gist.science explainer, "2. Calibrated
@@ -255,23 +262,25 @@ int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stre
  * launches per step (fugumt.com abstract).  That form is
  * pkv_decode_splits followed by pkv_merge.  Here the workgroup that finishes
  * the last split of a (row, KV head) merges that group instead.  It finds
- * out through a device-scope arrival counter, after a release fence by every
- * split.  The arithmetic is that of pkv_merge.  A row with a single split
+ * out through a device-scope arrival counter, which every workgroup bumps
+ * for its splits once its write-through partial stores are acknowledged.
+ * The arithmetic is that of pkv_merge.  A row with a single split
  * writes its output directly.  A row with N_b = 0 gets out = 0 and
  * lse = -inf.  With B * Hkv > PKV_MAX_FUSED_GROUPS, or no task at all, the
  * call falls back to the two-launch form.
  *
- * All pointers are device pointers.  Tensors are contiguous, row-major:
- *   q            fp16  [B, Hq, head_dim]
- *   k_pool       fp16  [num_pages, Hkv, page_size, head_dim]
- *   v_pool       fp16  [num_pages, Hkv, page_size, head_dim]
+ * All pointers are device pointers.  Tensors are contiguous, row-major; E is
+ * the element type `dtype` (pkv_dtype: fp16 or bf16):
+ *   q            E     [B, Hq, head_dim]
+ *   k_pool       E     [num_pages, Hkv, page_size, head_dim]
+ *   v_pool       E     [num_pages, Hkv, page_size, head_dim]
  *   block_table  int32 [B, max_pages_per_row]
  *   seq_lens     int32 [B]
  *   tasks        int32 [num_tasks][4] and split_offsets int32 [B+1], as
  *                written by pkv_plan for the same seq_lens, Hkv and
  *                page_size.  Device memory or device-mapped pinned host
  *                memory (the runner uses the latter).
- *   out          fp16  [B, Hq, head_dim]
+ *   out          E     [B, Hq, head_dim], rounded to nearest even
  *   lse          fp32  [B, Hq] natural-log log-sum-exp, or NULL
  *   workspace    >= pkv_workspace_size(num_partial_slots, Hq, head_dim)
  *                bytes, 256-byte aligned, initialised once by
@@ -292,8 +301,8 @@ int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t nu
                const int32_t* block_table, int32_t max_pages_per_row,
                const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
-               int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, float scale,
-               void* out, float* lse, void* workspace, size_t workspace_bytes,
+               int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, int32_t dtype,
+               float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                void* stream);
 
 /*
@@ -309,7 +318,7 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
                       const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                       const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
                       int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                      float scale, void* out, float* lse, void* workspace,
+                      int32_t dtype, float scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
 
 /*
@@ -318,7 +327,7 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
  * combines the split states exactly).  For every row b with S_b =
  * split_offsets[b+1] - split_offsets[b] != 1 and every query head h:
  *   M = max_s m_s,  w_s = 2^(m_s - M),
- *   out[b,h] = sum_s w_s o_s / sum_s w_s l_s   (fp16),
+ *   out[b,h] = sum_s w_s o_s / sum_s w_s l_s   (dtype E),
  *   lse[b,h] = (M + log2 sum_s w_s l_s) * ln 2.
  * Here (m_s, l_s, o_s) are the base-2 partial states that pkv_decode_splits
  * left in the workspace.  S_b = 0 (an empty row) writes out = 0 and lse =
@@ -329,8 +338,8 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
  * PKV_ERR_BUFFER_TOO_SMALL, PKV_ERR_HIP.
  */
 int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B, int32_t Hq,
-              int32_t Hkv, int32_t head_dim, void* out, float* lse, void* workspace,
-              size_t workspace_bytes, void* stream);
+              int32_t Hkv, int32_t head_dim, int32_t dtype, void* out, float* lse,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Device-side planning -- one decode step whose plan is built on the device
@@ -379,9 +388,10 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
                            int64_t num_pages, const int32_t* block_table,
                            int32_t max_pages_per_row, const int32_t* seq_lens, int32_t B,
                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                           float scale, int32_t mode, int32_t param, int32_t max_splits,
-                           const pkv_policy_params* policy, int32_t num_cus, void* out,
-                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                           int32_t dtype, float scale, int32_t mode, int32_t param,
+                           int32_t max_splits, const pkv_policy_params* policy, int32_t num_cus,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Read back the plan the last pkv_decode_device_plan on this workspace built
  * (after synchronizing `stream`): header[8] = {tasks, fused (1) or
@@ -440,6 +450,7 @@ typedef struct pkv_step_args {
   int32_t Hkv;
   int32_t head_dim;
   int32_t page_size;
+  int32_t dtype;                 /* pkv_dtype of q, the pools and out */
   float scale;
   /* device outputs and scratch */
   void* out;                     /* fp16 [B, Hq, head_dim] */

@@ -26,6 +26,8 @@ PKV_ERR_BUFFER_TOO_SMALL = 3
 PKV_ERR_BAD_INDEX = 4
 PKV_ERR_HIP = 5
 
+PKV_DTYPE_F16 = 0
+PKV_DTYPE_BF16 = 1
 PKV_MODE_SPLIT = 0
 PKV_MODE_WORKQUEUE = 1
 
@@ -78,7 +80,7 @@ class pkv_step_args(ctypes.Structure):
         ("num_pages", ctypes.c_int64), ("block_table", ctypes.c_void_p),
         ("max_pages_per_row", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
         ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-        ("page_size", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
         ("event_before_decode", ctypes.c_void_p), ("event_after_decode", ctypes.c_void_p),
@@ -119,13 +121,14 @@ def _load():
         "pkv_workspace_init": ([_vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "pkv_workspace_error_flags": ([_vp, ctypes.POINTER(ctypes.c_uint32), _vp], ctypes.c_int),
         "pkv_decode": ([_vp, _vp, _vp, i64, _vp, i32, _vp, _vp, i64, _vp, i64, i32, i32, i32, i32,
-                        i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
-        "pkv_merge": ([_vp, i64, i32, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+                        i32, i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+                       ctypes.c_int),
+        "pkv_merge": ([_vp, i64, i32, i32, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                       ctypes.c_int),
         "pkv_workspace_size_device_plan": ([i32, i32, i32, i32, i32,
                                             ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "pkv_decode_device_plan": ([_vp, _vp, _vp, i64, _vp, i32, _vp, i32, i32, i32, i32, i32,
-                                    ctypes.c_float, i32, i32, i32,
+                                    i32, ctypes.c_float, i32, i32, i32,
                                     ctypes.POINTER(pkv_policy_params), i32, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp], ctypes.c_int),
         "pkv_device_plan_read": ([_vp, ctypes.c_size_t, i32, i32, i32, i32, i32, _i32p, _vp, _vp,
@@ -252,6 +255,19 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _elem_dtype(*tensors):
+    """pkv_dtype code of fp16 / bf16 tensors that must all share one type."""
+    import torch
+    codes = {torch.float16: PKV_DTYPE_F16, torch.bfloat16: PKV_DTYPE_BF16}
+    dt = tensors[0].dtype
+    if dt not in codes:
+        raise TypeError(f"q, the pools and out must be float16 or bfloat16, got {dt}")
+    for t in tensors[1:]:
+        if t.dtype != dt:
+            raise TypeError(f"q, the pools and out must share one dtype ({dt} vs {t.dtype})")
+    return codes[dt], dt
+
+
 def _dev(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -287,7 +303,8 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
     [B+1] int32, out [B,Hq,d] fp16, lse [B,Hq] fp32 or None, workspace uint8.
     """
     import torch
-    f16, i32 = torch.float16, torch.int32
+    i32 = torch.int32
+    code, f16 = _elem_dtype(q, k_pool, v_pool, out)
     B, Hq, D = q.shape
     num_pages, Hkv, P, Dk = k_pool.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
@@ -302,7 +319,7 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
         _dev(q, f16, "q"), _dev(k_pool, f16, "k_pool"), _dev(v_pool, f16, "v_pool"), num_pages,
         _dev(block_table, i32, "block_table"), block_table.shape[1],
         _dev(seq_lens, i32, "seq_lens"), _dev(tasks, i32, "tasks"), tasks.shape[0],
-        _dev(split_offsets, i32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D, P,
+        _dev(split_offsets, i32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D, P, code,
         float(scale), _dev(out, f16, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream),
@@ -330,14 +347,15 @@ def pkv_merge(split_offsets, num_partial_slots: int, Hkv: int, out, workspace, l
               stream=None):
     """Enqueue the merge kernel only; see pkv_merge in include/pkv.h."""
     import torch
+    code, edt = _elem_dtype(out)
     B, Hq, D = out.shape
     if split_offsets.shape != (B + 1,):
         raise ValueError("split_offsets must be [B+1]")
     if lse is not None and tuple(lse.shape) != (B, Hq):
         raise ValueError("lse must be [B, Hq]")
     _check(_load().pkv_merge(
-        _dev(split_offsets, torch.int32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D,
-        _dev(out, torch.float16, "out"),
+        _dev(split_offsets, torch.int32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D, code,
+        _dev(out, edt, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
         "pkv_merge")
@@ -361,7 +379,8 @@ def pkv_decode_device_plan(q, k_pool, v_pool, block_table, seq_lens, scale: floa
     """One step planned on the device; see pkv_decode_device_plan in include/pkv.h.
     seq_lens is a device tensor: nothing is read on the host."""
     import torch
-    f16, i32 = torch.float16, torch.int32
+    i32 = torch.int32
+    code, f16 = _elem_dtype(q, k_pool, v_pool, out)
     B, Hq, D = q.shape
     num_pages, Hkv, P, Dk = k_pool.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
@@ -374,7 +393,7 @@ def pkv_decode_device_plan(q, k_pool, v_pool, block_table, seq_lens, scale: floa
     _check(_load().pkv_decode_device_plan(
         _dev(q, f16, "q"), _dev(k_pool, f16, "k_pool"), _dev(v_pool, f16, "v_pool"), num_pages,
         _dev(block_table, i32, "block_table"), block_table.shape[1], _dev(seq_lens, i32, "seq_lens"),
-        B, Hq, Hkv, D, P, float(scale), mode, param, max_splits, pp, num_cus,
+        B, Hq, Hkv, D, P, code, float(scale), mode, param, max_splits, pp, num_cus,
         _dev(out, f16, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
         "pkv_decode_device_plan")
@@ -488,13 +507,15 @@ class PagedDecoder:
         if lse is not None and tuple(lse.shape) != (B, Hq):
             raise ValueError("lse must be [B, Hq]")
         a = self.args
-        a.q = _dev(q, torch.float16, "q").value
-        a.k_pool = _dev(k_pool, torch.float16, "k_pool").value
-        a.v_pool = _dev(v_pool, torch.float16, "v_pool").value
+        code, edt = _elem_dtype(q, k_pool, v_pool, out)
+        a.dtype = code
+        a.q = _dev(q, edt, "q").value
+        a.k_pool = _dev(k_pool, edt, "k_pool").value
+        a.v_pool = _dev(v_pool, edt, "v_pool").value
         a.num_pages = k_pool.shape[0]
         a.block_table = _dev(block_table, torch.int32, "block_table").value
         a.seq_lens = _dev(seq_lens, torch.int32, "seq_lens").value
-        a.out = _dev(out, torch.float16, "out").value
+        a.out = _dev(out, edt, "out").value
         a.lse = _dev(lse, torch.float32, "lse").value if lse is not None else None
         a.scale = float(scale)
         self._seq_host = np.ascontiguousarray(seq_lens_h, dtype=np.int32)

@@ -57,6 +57,40 @@ typedef unsigned uint2x __attribute__((ext_vector_type(2)));
 
 template <int N>
 using halfN = _Float16 __attribute__((ext_vector_type(N)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Vectors of the element type E of q, K, V and out: _Float16 or __bf16.
+template <class E, int N>
+using vecE = E __attribute__((ext_vector_type(N)));
+
+// The two MFMA shapes for each element type (fp32 accumulate):
+//   k32: 16x16x32, A and B are 8 elements per lane;
+//   k16: 16x16x16, A and B are 4 elements per lane.
+template <class E>
+struct Mfma;
+template <>
+struct Mfma<_Float16> {
+  static __device__ __forceinline__ floatx4 k32(vecE<_Float16, 8> a, vecE<_Float16, 8> b,
+                                                floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ floatx4 k16(vecE<_Float16, 4> a, vecE<_Float16, 4> b,
+                                                floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<__bf16> {
+  static __device__ __forceinline__ floatx4 k32(vecE<__bf16, 8> a, vecE<__bf16, 8> b,
+                                                floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ floatx4 k16(vecE<__bf16, 4> a, vecE<__bf16, 4> b,
+                                                floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a),
+                                                     __builtin_bit_cast(shortx4, b), c, 0, 0, 0);
+  }
+};
 
 constexpr int kPage = 16;
 constexpr int kWaves = 4;             // waves per workgroup (one task at a time)
@@ -65,9 +99,9 @@ constexpr int kMaxG = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct DecodeArgs {
-  const _Float16* q;
-  const _Float16* k;
-  const _Float16* v;
+  const void* q;      // E [B, Hq, D]
+  const void* k;      // E [pages, Hkv, 16, D]
+  const void* v;
   int64_t num_pages;
   const int32_t* block_table;
   int32_t max_pages;
@@ -80,7 +114,7 @@ struct DecodeArgs {
   int64_t num_slots;
   int32_t B, Hq, Hkv, G;
   float scale_log2;   // softmax scale * log2(e)
-  _Float16* out;
+  void* out;          // E [B, Hq, D]
   float* lse;
   uint32_t* ctrl;     // [0] task counter, [1] exit counter, [2] error word
   uint32_t* arrive;   // [B*Hkv] arrival counters of the fused merge
@@ -96,12 +130,12 @@ __device__ __forceinline__ void flag_error(uint32_t* ctrl, uint32_t bits) {
 }
 
 // Per-page registers of one wave: the K operand and the raw V rows.
-template <int D>
+template <int D, class E>
 struct PageRegs {
   static constexpr int KK = D / 32;
   static constexpr int VW = D / 16;
-  half8 k[KK];
-  halfN<VW> v[4];
+  vecE<E, 8> k[KK];
+  vecE<E, VW> v[4];
 };
 
 // Buffer resource for raw buffer loads (gfx9 dword3).  Loads at offsets
@@ -127,21 +161,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // voff = 2*(4*grp*D + VW*col)).  Each K instruction reads 16 runs of 64
 // contiguous bytes, and each V instruction reads 4 whole 2*D-byte rows of
 // the contiguous page tile.
-template <int D>
-__device__ __forceinline__ void load_page(PageRegs<D>& r, __amdgpu_buffer_rsrc_t kr,
+template <int D, class E>
+__device__ __forceinline__ void load_page(PageRegs<D, E>& r, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, int koff, int voff) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    r.k[kk] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
+    r.k[kk] = __builtin_bit_cast(vecE<E, 8>,
+                                 __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if constexpr (VW == 8)
-      r.v[j] = __builtin_bit_cast(halfN<VW>,
+      r.v[j] = __builtin_bit_cast(vecE<E, VW>,
                                   __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
     else
-      r.v[j] = __builtin_bit_cast(halfN<VW>,
+      r.v[j] = __builtin_bit_cast(vecE<E, VW>,
                                   __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, 0));
   }
 }
@@ -164,9 +199,9 @@ struct WaveState {
   floatx4 acc[VW];      // O^T block e: lane holds O[head col][VW*(4*grp+j)+e]
 };
 
-template <int D>
-__device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D>& pg,
-                                             const half8* __restrict__ qf_lds, int nvalid,
+template <int D, class E>
+__device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D, E>& pg,
+                                             const vecE<E, 8>* __restrict__ qf_lds, int nvalid,
                                              float scale_log2, int lane) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
@@ -176,7 +211,7 @@ __device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D>& pg,
   floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pg.k[kk], qf_lds[kk * 64 + lane], sacc, 0, 0, 0);
+    sacc = Mfma<E>::k32(pg.k[kk], qf_lds[kk * 64 + lane], sacc);
   float sc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) sc[j] = sacc[j] * scale_log2;
@@ -185,7 +220,7 @@ __device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D>& pg,
     for (int j = 0; j < 4; ++j) {
       const bool live = 4 * grp + j < nvalid;
       sc[j] = live ? sc[j] : -INFINITY;
-      if (!live) pg.v[j] = halfN<VW>{};
+      if (!live) pg.v[j] = vecE<E, VW>{};
     }
   }
   const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -200,16 +235,16 @@ __device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D>& pg,
     for (int e = 0; e < VW; ++e) st.acc[e] *= alpha;
     st.m = m_new;
   }
-  half4 pb;
+  vecE<E, 4> pb;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pb[j] = static_cast<_Float16>(fast_exp2(sc[j] - st.m));
+  for (int j = 0; j < 4; ++j) pb[j] = static_cast<E>(fast_exp2(sc[j] - st.m));
   st.l += (static_cast<float>(pb[0]) + static_cast<float>(pb[1])) +
           (static_cast<float>(pb[2]) + static_cast<float>(pb[3]));
   // O^T += V^T . P^T, one 16x16x16 MFMA per 16 output columns
 #pragma unroll
   for (int e = 0; e < VW; ++e) {
-    const half4 av = {pg.v[0][e], pg.v[1][e], pg.v[2][e], pg.v[3][e]};
-    st.acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, st.acc[e], 0, 0, 0);
+    const vecE<E, 4> av = {pg.v[0][e], pg.v[1][e], pg.v[2][e], pg.v[3][e]};
+    st.acc[e] = Mfma<E>::k16(av, pb, st.acc[e]);
   }
 }
 
@@ -220,7 +255,7 @@ struct MergeArgs {
   const int32_t* plan_hdr;   // device plan: [1] != 0 means the decode kernel merged
   const float* part_o;
   const float2* part_ml;
-  _Float16* out;
+  void* out;          // E [B, Hq, D]
   float* lse;
   uint32_t* ctrl;
 };
@@ -246,7 +281,7 @@ constexpr int merge_lds_floats() {
   return kThreads * 6;
 }
 
-template <int D, int kB>
+template <int D, int kB, class E>
 __device__ void merge_group(const MergeArgs& a, int b, int g, int o0, int S, float* lds) {
   const int tid = threadIdx.x;
   const int G = a.G;
@@ -319,22 +354,22 @@ __device__ void merge_group(const MergeArgs& a, int b, int g, int o0, int S, flo
       Ot += w * s_O[tid + j * cols];
     }
     const float inv = 1.f / Lt;
-    _Float16* dst = a.out + head0 * D + 4 * c;
-    dst[0] = static_cast<_Float16>(Ot[0] * inv);
-    dst[1] = static_cast<_Float16>(Ot[1] * inv);
-    dst[2] = static_cast<_Float16>(Ot[2] * inv);
-    dst[3] = static_cast<_Float16>(Ot[3] * inv);
+    E* dst = static_cast<E*>(a.out) + head0 * D + 4 * c;
+    dst[0] = static_cast<E>(Ot[0] * inv);
+    dst[1] = static_cast<E>(Ot[1] * inv);
+    dst[2] = static_cast<E>(Ot[2] * inv);
+    dst[3] = static_cast<E>(Ot[3] * inv);
     if ((4 * c) % D == 0 && a.lse) a.lse[head0 + h] = (Mt + __log2f(Lt)) * kLn2;
   }
 }
 
 // Output of an empty row (N_b = 0): out = 0, lse = -inf, for the G heads of
 // KV head g.
-template <int D>
+template <int D, class E>
 __device__ __forceinline__ void write_empty_group(const MergeArgs& a, int b, int g) {
   const int64_t head0 = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * a.G;
   for (int i = threadIdx.x; i < a.G * D; i += kThreads)
-    a.out[head0 * D + i] = static_cast<_Float16>(0.f);
+    static_cast<E*>(a.out)[head0 * D + i] = static_cast<E>(0.f);
   if (static_cast<int>(threadIdx.x) < a.G && a.lse) a.lse[head0 + threadIdx.x] = -INFINITY;
 }
 
@@ -448,7 +483,7 @@ __device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __res
 // workgroup: one wait for all of its write-through partial stores, one
 // arrival per task (in parallel), then the workgroup merges, one after
 // another, the groups whose last split it holds.  All threads call it.
-template <int D, int kB>
+template <int D, int kB, class E>
 __device__ __forceinline__ void flush_done(const DecodeArgs& a, const MergeArgs& ma, int n,
                                         const int4* s_done, int* s_lastf, float* scratch) {
   const int tid = threadIdx.x;
@@ -463,7 +498,7 @@ __device__ __forceinline__ void flush_done(const DecodeArgs& a, const MergeArgs&
   for (int i = 0; i < n; ++i) {
     if (s_lastf[i]) {
       const int4 d = s_done[i];
-      merge_group<D, kB>(ma, d.x, d.y, d.z, d.w, scratch);
+      merge_group<D, kB, E>(ma, d.x, d.y, d.z, d.w, scratch);
       if (tid == 0) atomicExch(a.arrive + static_cast<int64_t>(d.x) * a.Hkv + d.y, 0u);
       __syncthreads();   // the scratch is reused by the next merge
     }
@@ -491,7 +526,7 @@ __device__ __forceinline__ Round load_round(const DecodeArgs& a, const int32_t* 
   return r;
 }
 
-template <int D, bool kStaged>
+template <int D, bool kStaged, class E>
 __global__ void __launch_bounds__(kThreads, 2)
 pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
@@ -510,7 +545,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ int s_len[kStaged ? kRowStage : 1];
   __shared__ int s_off[kStaged ? kRowStage + 1 : 1];
   __shared__ int s_next[2];
-  __shared__ half8 s_q[2][KK * 64];                 // q operand of a task, per lane
+  __shared__ vecE<E, 8> s_q[2][KK * 64];            // q operand of a task, per lane
   __shared__ float s_m[2][kWaves][16];
   __shared__ float s_l[2][kWaves][16];
   __shared__ __attribute__((aligned(16))) float s_o[2][kWaves][kMaxG][LDS_STRIDE];
@@ -556,7 +591,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
       const int sb = kStaged ? s_off[b + 1] - s_off[b] : offs_in[b + 1] - offs_in[b];
       if (sb == 0)
-        for (int g = 0; g < a.Hkv; ++g) write_empty_group<D>(ma, b, g);
+        for (int g = 0; g < a.Hkv; ++g) write_empty_group<D, E>(ma, b, g);
     }
   }
 
@@ -571,7 +606,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   // Load the page at position `pos` of task m (entry e) into `r`.  A
   // position past the range, an invalid task or an out-of-pool entry loads
   // nothing (num_records = 0) and returns false.
-  auto issue = [&](const Meta& m, int pos, int e, PageRegs<D>& r) -> bool {
+  auto issue = [&](const Meta& m, int pos, int e, PageRegs<D, E>& r) -> bool {
     const int page = m.p0 + wave + kWaves * pos;
     const bool want = m.ok && page < m.p1;
     const bool inr = e >= 0 && static_cast<int64_t>(e) < a.num_pages;
@@ -580,37 +615,38 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const int64_t off = static_cast<int64_t>(m.g) * tile_elems * 2 +
                         (live ? static_cast<int64_t>(e) * stride_bytes : 0);
     const uint32_t bytes = live ? kTileBytes : 0u;
-    load_page<D>(r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff, voff);
+    load_page<D, E>(r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff, voff);
     return live;
   };
   // q of task m (B operand of the score MFMA, column = head within the
   // group).  Raw loads; columns >= G are zeroed when stored to LDS, so the
   // loads can stay in flight until then.
-  auto load_q = [&](const Meta& m, half8 (&qf)[KK]) {
+  auto load_q = [&](const Meta& m, vecE<E, 8> (&qf)[KK]) {
     const bool live = m.ok && col < G;
-    const _Float16* qp = a.q + (static_cast<int64_t>(m.b) * a.Hq +
+    const E* qp = static_cast<const E*>(a.q) + (static_cast<int64_t>(m.b) * a.Hq +
                                 static_cast<int64_t>(m.g) * G + (live ? col : 0)) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qp + 8 * (4 * kk + grp));
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = *reinterpret_cast<const vecE<E, 8>*>(qp + 8 * (4 * kk + grp));
   };
-  auto store_q = [&](const Meta& m, const half8 (&qf)[KK], half8* dst) {
+  auto store_q = [&](const Meta& m, const vecE<E, 8> (&qf)[KK], vecE<E, 8>* dst) {
     const bool live = m.ok && col < G;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) dst[kk * 64 + lane] = live ? qf[kk] : half8{};
+    for (int kk = 0; kk < KK; ++kk) dst[kk * 64 + lane] = live ? qf[kk] : vecE<E, 8>{};
   };
 
   // ---- prologue: task 0 = blockIdx.x, task 1 = blockIdx.x + gridDim.x
   Meta cur = decode_meta<kStaged>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, blockIdx.x,
                                   rec0);
   int t_nxt = blockIdx.x + gridDim.x;
-  PageRegs<D> ring[kRing];
+  PageRegs<D, E> ring[kRing];
   bool valid[kRing];
   {
     const Round r0 = load_round(a, bt_in, cur, wave, 0);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
     if (wave == 0) {
-      half8 qf[KK];
+      vecE<E, 8> qf[KK];
       load_q(cur, qf);
       store_q(cur, qf, s_q[0]);
     }
@@ -632,7 +668,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       const bool fetch = t_nxt < num_tasks;
       uint32_t raw_nn = 0;
       if (fetch && lane == 0) raw_nn = atomicAdd(a.ctrl, 1u);
-      half8 qn[KK];
+      vecE<E, 8> qn[KK];
       load_q(nxt, qn);
       store_q(nxt, qn, s_q[par ^ 1]);
       if (lane == 0)
@@ -652,7 +688,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       for (int r = 0; r < kRing; ++r) {
         if (valid[r]) {
           const int page = cur.p0 + wave + kWaves * (kRing * j + r);
-          process_page<D>(st, ring[r], s_q[par], cur.N - page * kPage, a.scale_log2, lane);
+          process_page<D, E>(st, ring[r], s_q[par], cur.N - page * kPage, a.scale_log2, lane);
         }
         // refill the slot with the position one round ahead
         if (last)
@@ -696,7 +732,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
         }
         const int64_t hq = static_cast<int64_t>(cur.g) * G + h;
         if (direct) {
-          a.out[(static_cast<int64_t>(cur.b) * a.Hq + hq) * D + d] = static_cast<_Float16>(O / L);
+          static_cast<E*>(a.out)[(static_cast<int64_t>(cur.b) * a.Hq + hq) * D + d] =
+              static_cast<E>(O / L);
           if (d == 0 && a.lse)
             a.lse[static_cast<int64_t>(cur.b) * a.Hq + hq] = (M + __log2f(L)) * kLn2;
         } else {
@@ -720,7 +757,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
         // behind it.
         if (tid == 0) s_done[n_done] = int4{cur.b, cur.g, cur.o0, cur.Sb};
         if (++n_done == kMaxDone) {
-          flush_done<D, kMergeBatch>(a, ma, n_done, s_done, s_lastf, &s_o[par][0][0][0]);
+          flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[par][0][0][0]);
           n_done = 0;
         }
       }
@@ -729,7 +766,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     cur = nxt;
   }
 
-  if (n_done > 0) flush_done<D, kMergeBatch>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0][0]);
+  if (n_done > 0) flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0][0]);
 
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
@@ -742,7 +779,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
 }
 
 // Kernel 2 of the two-launch form: one workgroup per (row, KV head).
-template <int D>
+template <int D, class E>
 __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) float lds[merge_lds_floats<D>()];
   if (a.plan_hdr && a.plan_hdr[1]) return;   // merged inside the decode kernel
@@ -753,10 +790,10 @@ __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
   if (S == 1) return;   // written directly by the decode kernel
   if (S <= 0 || o0 < 0 || static_cast<int64_t>(o0) + S > a.num_slots) {
     if (S != 0 && threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_SLOT);
-    write_empty_group<D>(a, b, g);
+    write_empty_group<D, E>(a, b, g);
     return;
   }
-  merge_group<D, kMergeBatch>(a, b, g, o0, S, lds);
+  merge_group<D, kMergeBatch, E>(a, b, g, o0, S, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1020,16 +1057,16 @@ int num_cus_of_current_device(int* cus) {
   return PKV_OK;
 }
 
-template <int D>
+template <int D, class E>
 int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
            bool decode) {
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     if (da.B <= kRowStage)
-      hipLaunchKernelGGL((pkv_decode_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, da,
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E>), dim3(grid), dim3(kThreads), 0, stream, da,
                          tasks, da.block_table, da.seq_lens, da.split_offsets);
     else
-      hipLaunchKernelGGL((pkv_decode_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, da,
+      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E>), dim3(grid), dim3(kThreads), 0, stream, da,
                          tasks, da.block_table, da.seq_lens, da.split_offsets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -1038,7 +1075,8 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
     }
   }
   if (ma.B > 0) {
-    hipLaunchKernelGGL(pkv_merge_kernel<D>, dim3(ma.B * ma.Hkv), dim3(kThreads), 0, stream, ma);
+    hipLaunchKernelGGL((pkv_merge_kernel<D, E>), dim3(ma.B * ma.Hkv), dim3(kThreads), 0, stream,
+                       ma);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       set_hip_error(static_cast<int>(e));
@@ -1046,6 +1084,17 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
     }
   }
   return PKV_OK;
+}
+
+// The kernels of one head dimension and element type (both checked by the
+// caller).
+int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& ma, int grid,
+               hipStream_t stream, bool decode) {
+  if (dtype == PKV_DTYPE_BF16)
+    return head_dim == 128 ? launch<128, __bf16>(da, ma, grid, stream, decode)
+                           : launch<64, __bf16>(da, ma, grid, stream, decode);
+  return head_dim == 128 ? launch<128, _Float16>(da, ma, grid, stream, decode)
+                         : launch<64, _Float16>(da, ma, grid, stream, decode);
 }
 
 }  // namespace pkv
@@ -1085,12 +1134,13 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
             const int32_t* block_table, int32_t max_pages_per_row, const int32_t* seq_lens,
             const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,
             int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
-            int32_t page_size, float scale, void* out, float* lse, void* workspace,
+            int32_t page_size, int32_t dtype, float scale, void* out, float* lse, void* workspace,
             size_t workspace_bytes, bool need_decode, pkv::DecodeArgs* da, pkv::MergeArgs* ma) {
   if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 0 || max_pages_per_row < 0 || num_tasks < 0 ||
       num_tasks > INT32_MAX || num_partial_slots < 0 || !(scale == scale))
     return PKV_ERR_INVALID_ARG;
-  if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128) || Hq % Hkv != 0)
+  if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128) || Hq % Hkv != 0 ||
+      (dtype != PKV_DTYPE_F16 && dtype != PKV_DTYPE_BF16))
     return PKV_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
@@ -1117,9 +1167,9 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
                                                   head_dim * sizeof(float));
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws);
 
-  da->q = static_cast<const _Float16*>(q);
-  da->k = static_cast<const _Float16*>(k_pool);
-  da->v = static_cast<const _Float16*>(v_pool);
+  da->q = q;
+  da->k = k_pool;
+  da->v = v_pool;
   da->num_pages = num_pages;
   da->block_table = block_table;
   da->max_pages = max_pages_per_row;
@@ -1133,7 +1183,7 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   da->Hkv = Hkv;
   da->G = G;
   da->scale_log2 = scale * 1.44269504088896340736f;
-  da->out = static_cast<_Float16*>(out);
+  da->out = out;
   da->lse = lse;
   da->ctrl = ctrl;
   da->arrive = ctrl + 64;
@@ -1149,7 +1199,7 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   ma->G = G;
   ma->part_o = part_o;
   ma->part_ml = part_ml;
-  ma->out = static_cast<_Float16*>(out);
+  ma->out = out;
   ma->lse = lse;
   ma->ctrl = ctrl;
   return PKV_OK;
@@ -1159,13 +1209,13 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
         const int32_t* block_table, int32_t max_pages_per_row, const int32_t* seq_lens,
         const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,
         int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
-        int32_t page_size, float scale, void* out, float* lse, void* workspace,
+        int32_t page_size, int32_t dtype, float scale, void* out, float* lse, void* workspace,
         size_t workspace_bytes, void* stream, bool do_decode, bool do_merge, bool fused) {
   pkv::DecodeArgs da{};
   pkv::MergeArgs ma{};
   int st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
                    num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size,
-                   scale, out, lse, workspace, workspace_bytes, do_decode, &da, &ma);
+                   dtype, scale, out, lse, workspace, workspace_bytes, do_decode, &da, &ma);
   if (st != PKV_OK || B == 0) return st;
   // Fused single launch when the arrival counters fit and there is work for
   // the decode kernel; otherwise the two-launch form.
@@ -1189,8 +1239,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool decode = da.num_tasks > 0;
   da.task_cap = da.num_tasks > 0 ? da.num_tasks : 1;
-  return head_dim == 128 ? pkv::launch<128>(da, ma, grid, s, decode)
-                         : pkv::launch<64>(da, ma, grid, s, decode);
+  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode);
 }
 
 }  // namespace
@@ -1199,12 +1248,12 @@ int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t nu
                const int32_t* block_table, int32_t max_pages_per_row,
                const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
-               int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, float scale,
-               void* out, float* lse, void* workspace, size_t workspace_bytes,
+               int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, int32_t dtype,
+               float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                void* stream) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
-             num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, scale,
-             out, lse, workspace, workspace_bytes, stream, true, true, true);
+             num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
+             scale, out, lse, workspace, workspace_bytes, stream, true, true, true);
 }
 
 int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
@@ -1212,19 +1261,19 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
                       const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                       const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
                       int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                      float scale, void* out, float* lse, void* workspace,
+                      int32_t dtype, float scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
-             num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, scale,
-             out, lse, workspace, workspace_bytes, stream, true, false, false);
+             num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
+             scale, out, lse, workspace, workspace_bytes, stream, true, false, false);
 }
 
 int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B, int32_t Hq,
-              int32_t Hkv, int32_t head_dim, void* out, float* lse, void* workspace,
-              size_t workspace_bytes, void* stream) {
+              int32_t Hkv, int32_t head_dim, int32_t dtype, void* out, float* lse,
+              void* workspace, size_t workspace_bytes, void* stream) {
   return run(nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, 0, split_offsets,
-             num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, 1.0f, out, lse, workspace,
-             workspace_bytes, stream, false, true, false);
+             num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, dtype, 1.0f, out, lse,
+             workspace, workspace_bytes, stream, false, true, false);
 }
 
 }  // extern "C"
@@ -1275,7 +1324,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
                            int64_t num_pages, const int32_t* block_table,
                            int32_t max_pages_per_row, const int32_t* seq_lens, int32_t B,
                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                           float scale, int32_t mode, int32_t param, int32_t max_splits,
+                           int32_t dtype, float scale, int32_t mode, int32_t param,
+                           int32_t max_splits,
                            const pkv_policy_params* policy, int32_t num_cus, void* out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   pkv_policy_params pol;
@@ -1319,8 +1369,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   pkv::DecodeArgs da{};
   pkv::MergeArgs ma{};
   st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
-               L.task_cap, offs, L.slot_cap, B, Hq, Hkv, head_dim, page_size, scale, out, lse,
-               workspace, workspace_bytes, true, &da, &ma);
+               L.task_cap, offs, L.slot_cap, B, Hq, Hkv, head_dim, page_size, dtype, scale, out,
+               lse, workspace, workspace_bytes, true, &da, &ma);
   if (st != PKV_OK || B == 0) return st;
   if (num_cus <= 0) {
     st = pkv::num_cus_of_current_device(&num_cus);
@@ -1360,8 +1410,7 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   // every plan is fused, and the merge kernel is not launched at all.
   const int grid = num_cus;
   if (max_splits <= pol.fuse_max_splits && pa.groups_fit) ma.B = 0;
-  return head_dim == 128 ? pkv::launch<128>(da, ma, grid, s, true)
-                         : pkv::launch<64>(da, ma, grid, s, true);
+  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true);
 }
 
 int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,

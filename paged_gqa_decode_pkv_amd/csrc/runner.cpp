@@ -325,13 +325,13 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   if (two) {
     st = pkv_decode_splits(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
                            a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B,
-                           a->Hq, a->Hkv, a->head_dim, a->page_size, a->scale, a->out, a->lse,
-                           a->workspace, a->workspace_bytes, a->stream);
+                           a->Hq, a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale, a->out,
+                           a->lse, a->workspace, a->workspace_bytes, a->stream);
   } else {
     st = pkv_decode(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
                     a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B, a->Hq,
-                    a->Hkv, a->head_dim, a->page_size, a->scale, a->out, a->lse, a->workspace,
-                    a->workspace_bytes, a->stream);
+                    a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale, a->out, a->lse,
+                    a->workspace, a->workspace_bytes, a->stream);
   }
   if (st != PKV_OK) return st;
   if (a->event_after_decode) {
@@ -342,7 +342,7 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
     }
   }
   if (two)
-    st = pkv_merge(offs_d, slots, a->B, a->Hq, a->Hkv, a->head_dim, a->out, a->lse,
+    st = pkv_merge(offs_d, slots, a->B, a->Hq, a->Hkv, a->head_dim, a->dtype, a->out, a->lse,
                    a->workspace, a->workspace_bytes, a->stream);
   // the slot is free once everything enqueued so far has run
   e = hipEventRecord(s.done, stream);

@@ -196,10 +196,12 @@ def build_block_table(cfg: Config, seq_lens: np.ndarray, rng: np.random.Generato
 
 def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan",
                   seq_lens: Optional[Sequence[int]] = None,
-                  pool_pages: Optional[int] = None) -> Workload:
+                  pool_pages: Optional[int] = None, dtype: str = "f16") -> Workload:
     """Draw one batch.  ``seq_lens`` overrides the config's length draw (edge cases).
 
     fill: what unreferenced pool pages and tail slots hold: "nan", "random" or "zero".
+    dtype: "f16", or "bf16" (device workloads only): the same float32 draws
+    rounded to bfloat16 instead of fp16.
     """
     import torch
 
@@ -215,6 +217,10 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
         np.zeros(0, dtype=np.int32)
     pshape = (pool, cfg.Hkv, P, cfg.D)
 
+    if dtype not in ("f16", "bf16"):
+        raise ValueError(dtype)
+    if device == "cpu" and dtype != "f16":
+        raise ValueError("bf16 workloads are drawn on the device only")
     if device == "cpu":
         fill_rng = np.random.default_rng([seed, 1])
         q = rng.standard_normal((len(lens), cfg.Hq, cfg.D), dtype=np.float32).astype(np.float16)
@@ -245,17 +251,18 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
         gen.manual_seed(seed)
         fill_gen = torch.Generator(device=dev)
         fill_gen.manual_seed(seed + 7919)
+        edt = torch.float16 if dtype == "f16" else torch.bfloat16
         q_t = torch.randn((len(lens), cfg.Hq, cfg.D), generator=gen, device=dev,
-                          dtype=torch.float32).half()
+                          dtype=torch.float32).to(edt)
         used_t = torch.from_numpy(used.astype(np.int64)).to(dev)
         pools = []
         for _ in range(2):
             if fill == "nan":
-                arr = torch.full(pshape, float("nan"), dtype=torch.float16, device=dev)
+                arr = torch.full(pshape, float("nan"), dtype=edt, device=dev)
             elif fill == "zero":
-                arr = torch.zeros(pshape, dtype=torch.float16, device=dev)
+                arr = torch.zeros(pshape, dtype=edt, device=dev)
             elif fill == "random":
-                arr = torch.empty(pshape, dtype=torch.float16, device=dev)
+                arr = torch.empty(pshape, dtype=edt, device=dev)
                 _randn_fill(arr, fill_gen)
             else:
                 raise ValueError(fill)
@@ -264,7 +271,7 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
             for i in range(0, len(used), chunk):
                 idx = used_t[i:i + chunk]
                 vals = torch.randn((idx.numel(), cfg.Hkv, P, cfg.D), generator=gen,
-                                   device=dev, dtype=torch.float32).half()
+                                   device=dev, dtype=torch.float32).to(edt)
                 arr.index_copy_(0, idx, vals)
                 del vals
             pools.append(arr)
@@ -290,7 +297,7 @@ def _randn_fill(arr, gen):
     for i in range(0, flat.numel(), step):
         n = min(step, flat.numel() - i)
         flat[i:i + n] = torch.randn(n, generator=gen, device=arr.device,
-                                    dtype=torch.float32).half()
+                                    dtype=torch.float32).to(arr.dtype)
 
 
 def _poison_tails(k, v, bt, lens, P, fill, rng):
@@ -351,7 +358,13 @@ def compact_rows(q, k_pool, v_pool, block_table, seq_lens, rows, page_size=PAGE_
         if isinstance(pool, np.ndarray):
             return pool[uniq]
         idx = torch.from_numpy(uniq.astype(np.int64)).to(pool.device)
-        return pool.index_select(0, idx).cpu().numpy()
+        sel = pool.index_select(0, idx)
+        if sel.dtype == torch.bfloat16:       # numpy has no bfloat16: widen exactly
+            sel = sel.float()
+        return sel.cpu().numpy()
 
-    qn = q.cpu().numpy() if hasattr(q, "cpu") else np.asarray(q)
+    if hasattr(q, "cpu"):
+        qn = (q.float() if q.dtype == torch.bfloat16 else q).cpu().numpy()
+    else:
+        qn = np.asarray(q)
     return qn[rows], take(k_pool), take(v_pool), new_bt, sl
