@@ -25,14 +25,16 @@
  *
  * Conventions
  *   - Every call returns an int status (pkv_status).  No exception crosses
- *     the ABI.  The library allocates no device memory and keeps no per-call
- *     state.  The caller owns every buffer.
+ *     the ABI.  The one-shot entry points allocate no device memory and keep
+ *     no per-call state; the caller owns every buffer.  (A step runner owns
+ *     its plan buffers; see pkv_runner_create.)
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued asynchronously and never synchronised.
- *   - Supported shapes: page_size = 16, head_dim in {64, 128},
- *     G = Hq/Hkv in {1, 2, 4, 8}.  Others return PKV_ERR_UNSUPPORTED.
- *   - Data types: q, K, V and out are IEEE fp16.  lse and the partial states
- *     are fp32.  Indices are int32.
+ *   - Supported shapes: page_size = 16, head_dim in {64, 128, 256},
+ *     G = Hq/Hkv in {1, 2, 4, 8} (at most 4 at head_dim 256).  Others return
+ *     PKV_ERR_UNSUPPORTED.
+ *   - Data types: q, K, V and out are fp16 or bf16 (pkv_dtype), all four the
+ *     same.  lse and the partial states are fp32.  Indices are int32.
  */
 #ifndef PKV_H_
 #define PKV_H_

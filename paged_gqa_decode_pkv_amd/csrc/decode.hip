@@ -172,12 +172,20 @@ __device__ __forceinline__ void load_page(PageRegs<D, E>& r, __amdgpu_buffer_rsr
                                  __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (VW == 8)
+    if constexpr (VW == 16) {
+      const vecE<E, 8> lo = __builtin_bit_cast(
+          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
+      const vecE<E, 8> hi = __builtin_bit_cast(
+          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, 0));
+      r.v[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14,
+                                       15);
+    } else if constexpr (VW == 8) {
       r.v[j] = __builtin_bit_cast(vecE<E, VW>,
                                   __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
-    else
+    } else {
       r.v[j] = __builtin_bit_cast(vecE<E, VW>,
                                   __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, 0));
+    }
   }
 }
 
@@ -376,7 +384,20 @@ __device__ __forceinline__ void write_empty_group(const MergeArgs& a, int b, int
 // Batches up to kRowStage rows get their lengths and split offsets staged in
 // LDS once per workgroup.  Larger batches read them with scalar loads.
 constexpr int kRowStage = 1024;
-constexpr int kRing = 4;   // page tiles in flight per wave (one "round")
+// Page tiles in flight per wave (one "round"): 4 at d <= 128; at d = 256 a
+// tile holds twice the bytes and registers, so 2 keep the same 32 KiB in
+// flight per wave within the register budget.
+template <int D>
+constexpr int ring_depth() {
+  return D == 256 ? 2 : 4;
+}
+
+// Largest GQA group a head dimension supports: the merge gives one float4
+// column of the group to each of its 256 threads (G * D / 4 <= 256).
+template <int D>
+constexpr int max_group() {
+  return D == 256 ? 4 : kMaxG;
+}
 // Split tasks of a workgroup whose arrival is deferred: they are counted in
 // together when the workgroup runs out of tasks or holds kMaxDone of them.
 constexpr int kMaxDone = 64;
@@ -391,7 +412,7 @@ struct Meta {
   int Sb;         // splits of the row
   int o0;         // first partial-state slot of the row
   int64_t slot;   // partial-state slot
-  int rounds;     // >= 1 rounds of kRing positions per wave
+  int rounds;     // >= 1 rounds of R positions per wave
   bool ok;        // a real task whose checks passed
 };
 
@@ -407,7 +428,7 @@ __device__ __forceinline__ int4 load_record(const DecodeArgs& a, const int4* __r
   return tasks[t < a.task_cap ? t : a.task_cap - 1];
 }
 
-template <bool kStaged>
+template <bool kStaged, int R>
 __device__ __forceinline__ Meta decode_meta(const DecodeArgs& a, const int32_t* __restrict__ seq_lens,
                                             const int32_t* __restrict__ offs, const int* s_len,
                                             const int* s_off, int num_tasks, int t, int4 rec) {
@@ -465,17 +486,17 @@ __device__ __forceinline__ Meta decode_meta(const DecodeArgs& a, const int32_t* 
   m.o0 = o0;
   m.slot = slot;
   const int per_wave = (p1 - p0 + kWaves - 1) / kWaves;
-  m.rounds = (per_wave + kRing - 1) / kRing;
+  m.rounds = (per_wave + R - 1) / R;
   m.ok = true;
   return m;
 }
 
-template <bool kStaged>
+template <bool kStaged, int R>
 __device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __restrict__ tasks,
                                           const int32_t* __restrict__ seq_lens,
                                           const int32_t* __restrict__ offs, const int* s_len,
                                           const int* s_off, int num_tasks, int t) {
-  return decode_meta<kStaged>(a, seq_lens, offs, s_len, s_off, num_tasks, t,
+  return decode_meta<kStaged, R>(a, seq_lens, offs, s_len, s_off, num_tasks, t,
                               load_record(a, tasks, t));
 }
 
@@ -509,25 +530,29 @@ __device__ __forceinline__ void flush_done(const DecodeArgs& a, const MergeArgs&
 // page p0 + wave + 16j + 4r.  Positions past the range read a clamped,
 // in-row entry that issue() never uses (it re-checks page < p1).  No select
 // on the loaded values, so the four scalar loads issue back to back.
+template <int R>
 struct Round {
-  int e[kRing];
+  int e[R];
 };
 
-__device__ __forceinline__ Round load_round(const DecodeArgs& a, const int32_t* __restrict__ bt,
-                                            const Meta& m, int wave, int j) {
-  Round r;
+template <int R>
+__device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_t* __restrict__ bt,
+                                               const Meta& m, int wave, int j) {
+  Round<R> r;
   const int32_t* row = bt + static_cast<int64_t>(m.b) * a.max_pages;
   const int last = m.ok ? m.p1 - 1 : 0;
 #pragma unroll
-  for (int i = 0; i < kRing; ++i) {
-    const int page = m.p0 + wave + kWaves * (kRing * j + i);
+  for (int i = 0; i < R; ++i) {
+    const int page = m.p0 + wave + kWaves * (R * j + i);
     r.e[i] = row[page < last ? page : last];
   }
   return r;
 }
 
+// Two workgroups per CU at d <= 128 (256 VGPRs each); one at d = 256, whose
+// larger tiles and accumulators need the AGPR half of the register file.
 template <int D, bool kStaged, class E>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
 pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
                   const int32_t* __restrict__ offs_in) {
@@ -535,6 +560,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   constexpr int VW = D / 16;
   constexpr int LDS_STRIDE = D + 4;
   constexpr uint32_t kTileBytes = static_cast<uint32_t>(kPage * D * 2);
+  constexpr int kRing = ring_depth<D>();
+  constexpr int kGroup = max_group<D>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -548,10 +575,10 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ vecE<E, 8> s_q[2][KK * 64];            // q operand of a task, per lane
   __shared__ float s_m[2][kWaves][16];
   __shared__ float s_l[2][kWaves][16];
-  __shared__ __attribute__((aligned(16))) float s_o[2][kWaves][kMaxG][LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) float s_o[2][kWaves][kGroup][LDS_STRIDE];
   __shared__ int4 s_done[kMaxDone];   // (row, KV head, first slot, splits)
   __shared__ int s_lastf[kMaxDone];
-  static_assert(kWaves * kMaxG * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
+  static_assert(kWaves * kGroup * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
 
   const MergeArgs ma{a.split_offsets, a.num_slots, a.B, a.Hq, a.Hkv, a.G, nullptr,
                      a.part_o, a.part_ml, a.out, a.lse, a.ctrl};
@@ -636,13 +663,14 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   };
 
   // ---- prologue: task 0 = blockIdx.x, task 1 = blockIdx.x + gridDim.x
-  Meta cur = decode_meta<kStaged>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, blockIdx.x,
+  Meta cur = decode_meta<kStaged, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks,
+                                         blockIdx.x,
                                   rec0);
   int t_nxt = blockIdx.x + gridDim.x;
   PageRegs<D, E> ring[kRing];
   bool valid[kRing];
   {
-    const Round r0 = load_round(a, bt_in, cur, wave, 0);
+    const Round<kRing> r0 = load_round<kRing>(a, bt_in, cur, wave, 0);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
     if (wave == 0) {
@@ -659,8 +687,9 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     // next task's metadata, its first round of table entries and its q;
     // the index of the task after it (counter values start at 2*gridDim.x)
     const Meta nxt =
-        load_meta<kStaged>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, num_tasks, t_nxt);
-    const Round nr0 = load_round(a, bt_in, nxt, wave, 0);
+        load_meta<kStaged, kRing>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, num_tasks,
+                                  t_nxt);
+    const Round<kRing> nr0 = load_round<kRing>(a, bt_in, nxt, wave, 0);
     // Wave 0: the index after next and the next task's q, both to LDS.
     // Their loads queue behind this task's first round, which the wave has
     // to wait for next anyway, so the wait costs nothing extra.
@@ -683,7 +712,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
 
     for (int j = 0; j < cur.rounds; ++j) {
       const bool last = (j + 1 == cur.rounds);
-      const Round fr = last ? nr0 : load_round(a, bt_in, cur, wave, j + 1);
+      const Round<kRing> fr = last ? nr0 : load_round<kRing>(a, bt_in, cur, wave, j + 1);
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
         if (valid[r]) {
@@ -1090,9 +1119,12 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
 // caller).
 int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& ma, int grid,
                hipStream_t stream, bool decode) {
-  if (dtype == PKV_DTYPE_BF16)
+  if (dtype == PKV_DTYPE_BF16) {
+    if (head_dim == 256) return launch<256, __bf16>(da, ma, grid, stream, decode);
     return head_dim == 128 ? launch<128, __bf16>(da, ma, grid, stream, decode)
                            : launch<64, __bf16>(da, ma, grid, stream, decode);
+  }
+  if (head_dim == 256) return launch<256, _Float16>(da, ma, grid, stream, decode);
   return head_dim == 128 ? launch<128, _Float16>(da, ma, grid, stream, decode)
                          : launch<64, _Float16>(da, ma, grid, stream, decode);
 }
@@ -1139,11 +1171,12 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 0 || max_pages_per_row < 0 || num_tasks < 0 ||
       num_tasks > INT32_MAX || num_partial_slots < 0 || !(scale == scale))
     return PKV_ERR_INVALID_ARG;
-  if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128) || Hq % Hkv != 0 ||
-      (dtype != PKV_DTYPE_F16 && dtype != PKV_DTYPE_BF16))
+  if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
+      Hq % Hkv != 0 || (dtype != PKV_DTYPE_F16 && dtype != PKV_DTYPE_BF16))
     return PKV_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (head_dim == 256 && G > 4) return PKV_ERR_UNSUPPORTED;   // merge: G * d / 4 <= 256
   if (static_cast<int64_t>(B) * Hq > INT32_MAX) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (!split_offsets || !out || !workspace) return PKV_ERR_INVALID_ARG;
@@ -1229,7 +1262,9 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
     int cus = 0;
     st = pkv::num_cus_of_current_device(&cus);
     if (st != PKV_OK) return st;
-    int64_t g = static_cast<int64_t>(cus) * 2;
+    // as many workgroups as fit at once (persistent: a workgroup that had to
+    // wait for a slot would hold its static tasks until the others finish)
+    int64_t g = static_cast<int64_t>(cus) * (head_dim == 256 ? 1 : 2);
     if (g > num_tasks) g = num_tasks;
     grid = static_cast<int>(g < 1 ? 1 : g);
   } else {

@@ -244,6 +244,8 @@ def test_decode_rejects_bad_scalars_before_touching_the_device():
         return lib.pkv_decode(None, None, None, 0, None, 1, None, None, 0, None, 0, B, Hq, Hkv, D,
                               P, dtype, scale, None, None, None, 0, None)
     assert call(D=96) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(D=256, Hq=8, Hkv=1) == pkv.PKV_ERR_UNSUPPORTED    # G = 8 at d = 256
+    assert call(D=256, Hq=4, Hkv=1) == pkv.PKV_ERR_INVALID_ARG    # supported; null pointers
     assert call(P=32) == pkv.PKV_ERR_UNSUPPORTED
     assert call(Hq=6, Hkv=4) == pkv.PKV_ERR_UNSUPPORTED      # Hq % Hkv
     assert call(Hq=48, Hkv=3) == pkv.PKV_ERR_UNSUPPORTED     # G = 16

@@ -122,3 +122,13 @@ def test_mixed_element_types_rejected():
     with pytest.raises(TypeError):
         dec.set_inputs(wl.q, wl.k_pool.half(), wl.v_pool, wl.block_table, wl.seq_lens,
                        wl.seq_lens_np, cfg.scale, torch.empty_like(wl.q))
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_bf16_head_dim_256(G):
+    cfg = Config("small_bf16_d256", B=0, Hq=G * 2, Hkv=2, D=256, max_pages_per_row=8,
+                 pool_pages=64, lengths=lambda rng: np.zeros(0))
+    lens = [1, 15, 16, 17, 33, 0, 127, 128]
+    for mode, param in [(0, 1), (0, 3), (1, 2)]:
+        wl = make_workload(cfg, 9 + G, device="cuda", seq_lens=lens, dtype="bf16")
+        _parity(wl, mode, param)

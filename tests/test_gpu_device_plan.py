@@ -248,3 +248,12 @@ def _with_lengths(wl, lens):
     import torch
     return dataclasses.replace(wl, seq_lens_np=np.asarray(lens, dtype=np.int32),
                                seq_lens=torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda())
+
+
+def test_device_plan_head_dim_256():
+    cfg = Config("d256_dp", B=8, Hq=16, Hkv=4, D=256, max_pages_per_row=1024,
+                 pool_pages=2 * 8 * 1024, lengths=CONFIGS["b8_bimodal"].lengths)
+    wl = make_workload(cfg, SEED, device="cuda")
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap=256)
+    _check_plan(wl, 256, hdr, tasks, offs, -1, 0)
+    _parity(wl, out, lse)

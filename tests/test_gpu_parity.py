@@ -217,3 +217,24 @@ def test_task_list_readback_bit_exact():
     tasks, offs = dec.plan_arrays()       # the memory the kernels read
     assert np.array_equal(tasks, rt)
     assert np.array_equal(offs, ro)
+
+
+# --------------------------------------------------------------------------- head_dim 256
+
+@pytest.mark.parametrize("two_launch", TWO)
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_head_dim_256_ragged(G, two_launch):
+    """d = 256 runs with a 2-deep page ring and one workgroup per CU."""
+    cfg = _small_cfg(G=G, D=256)
+    lens = [1, 15, 16, 17, 33, 0, 127, 128]
+    for mode, param in [(0, 1), (0, 3), (1, 1), (1, 2)]:
+        wl = make_workload(cfg, 11 + G, device="cuda", seq_lens=lens)
+        _parity(wl, mode, param, two_launch=two_launch)
+
+
+def test_head_dim_256_long_bimodal():
+    cfg = Config("d256_bimodal", B=8, Hq=16, Hkv=4, D=256, max_pages_per_row=1024,
+                 pool_pages=2 * 8 * 1024, lengths=CONFIGS["b8_bimodal"].lengths)
+    wl = make_workload(cfg, SEED, device="cuda")
+    for mode, param in [(None, None), (1, 64), (0, 32)]:
+        _parity(wl, mode, param, two_launch=None)
