@@ -245,7 +245,7 @@ def main():
             "traffic": _traffic({"workload": cfg.name, "seed": args.seed,
                                  "mode": ["split", "workqueue"][mode], "param": param,
                                  "merge": "two-launch" if two_launch else "fused"}),
-            "kernel": "pkv_decode_kernel<128, true>",
+            "kernel": "pkv_decode_kernel<128, true, _Float16>",
             "event_timed_steps": len(events),
             "algorithmic_bytes_per_launch": kv_bytes,
             "extras_bytes_per_launch": extras,
