@@ -257,3 +257,16 @@ def test_device_plan_head_dim_256():
     out, lse, hdr, tasks, offs, _ = _run(wl, cap=256)
     _check_plan(wl, 256, hdr, tasks, offs, -1, 0)
     _parity(wl, out, lse)
+
+
+def test_device_plan_batch_beyond_lds_staging():
+    rng = np.random.default_rng(32)
+    B = 1100
+    lens = rng.integers(0, 300, size=B)
+    cfg = Config("b1100_dp", B=B, Hq=8, Hkv=2, D=64, max_pages_per_row=19,
+                 pool_pages=B * 19 + 64, lengths=None)
+    wl = make_workload(cfg, 32, device="cuda", seq_lens=lens.tolist())
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap=8)
+    _check_plan(wl, 8, hdr, tasks, offs, -1, 0)
+    rows = sorted(rng.choice(B, size=48, replace=False).tolist())
+    _parity(wl, out, lse, rows=rows)

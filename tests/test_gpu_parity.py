@@ -238,3 +238,21 @@ def test_head_dim_256_long_bimodal():
     wl = make_workload(cfg, SEED, device="cuda")
     for mode, param in [(None, None), (1, 64), (0, 32)]:
         _parity(wl, mode, param, two_launch=None)
+
+
+# --------------------------------------------------------------------------- large batches
+
+@pytest.mark.parametrize("two_launch", TWO)
+def test_batch_beyond_lds_staging(two_launch):
+    """B > 1024 rows: the kernel variant that reads row lengths and split
+    offsets with scalar loads instead of staging them in LDS."""
+    rng = np.random.default_rng(31)
+    B = 1100
+    lens = rng.integers(0, 300, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    cfg = Config("b1100", B=0, Hq=8, Hkv=2, D=64, max_pages_per_row=19, pool_pages=B * 19 + 64,
+                 lengths=lambda r: np.zeros(0))
+    wl = make_workload(cfg, 31, device="cuda", seq_lens=lens.tolist())
+    rows = sorted(set(rng.choice(B, size=64, replace=False).tolist()) | {0, B - 1})
+    for mode, param in [(0, 2), (1, 4), (None, None)]:
+        _parity(wl, mode, param, rows=rows, two_launch=two_launch)
