@@ -19,6 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
+PKV_ABI_VERSION = 3               # include/pkv.h; the argument lists below follow it
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = 1
 PKV_ERR_UNSUPPORTED = 2
@@ -145,6 +146,10 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    got = lib.pkv_abi_version()
+    if got != PKV_ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {got}, the binding expects "
+                          f"{PKV_ABI_VERSION}; rebuild with `python -m paged_gqa_decode_pkv_amd.build`")
     _lib = lib
     return lib
 

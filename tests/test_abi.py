@@ -30,7 +30,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert pkv.pkv_abi_version() == 3
+    assert pkv.pkv_abi_version() == pkv.PKV_ABI_VERSION
+    hdr = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    assert re.search(r"#define PKV_ABI_VERSION (\d+)", hdr).group(1) == str(pkv.PKV_ABI_VERSION)
     for code in range(6):
         assert pkv.pkv_status_string(code)
     assert pkv.pkv_status_string(99) == "unknown status"
