@@ -89,7 +89,7 @@ def cpu_baseline(wl, out_gpu, budget_s: float, rows=None):
         "kind": "oracle",
         "sample": (f"{len(rows)} of {len(wl.seq_lens_np)} rows, all {wl.cfg.Hq} heads, "
                    f"{int(sl.sum())} tokens, {reps} pass(es) in {el:.1f} s; float64 numpy, "
-                   f"BLAS limited to 1 thread; fp16 pages copied to host before timing"),
+                   f"BLAS limited to 1 thread; pages copied to host before timing"),
         "gpu_vs_oracle_max_abs_err": err,
         "gpu_vs_oracle_rel_err": rel,
     }
@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="b8_bimodal")
+    ap.add_argument("--kv-dtype", default="f16", choices=("f16", "fp8"),
+                    help="K/V pool element type: fp16, or fp8 E4M3 codes (q and out stay fp16)")
     ap.add_argument("--seed", type=int, default=20260623)
     ap.add_argument("--mode", type=int, default=None, help="0 split / 1 workqueue (default: policy)")
     ap.add_argument("--param", type=int, default=None)
@@ -142,7 +144,8 @@ def main():
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda")
     print(f"[bench] drawing {cfg.name} seed {args.seed}", file=sys.stderr, flush=True)
-    wl = make_workload(cfg, args.seed, device="cuda")
+    wl = make_workload(cfg, args.seed, device="cuda",
+                       dtype="fp8" if args.kv_dtype == "fp8" else "f16")
     B = len(wl.seq_lens_np)
     kv_bytes = wl.kv_bytes
     L = args.layers or max(1, min(16, math.ceil((2 << 30) / max(kv_bytes, 1))))
@@ -222,7 +225,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": cfg.name, "seed": args.seed, "B": B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
-            "head_dim": cfg.D, "page_size": 16, "seq_lens": sl_h.tolist(),
+            "head_dim": cfg.D, "page_size": 16, "kv_dtype": args.kv_dtype,
+            "seq_lens": sl_h.tolist(),
             "kv_bytes_per_step": kv_bytes, "mode": ["split", "workqueue"][mode], "param": param,
             "tasks": T, "layers_rotated": L, "launches_per_step": 2 if two_launch else 1,
             "merge": "separate merge kernel" if two_launch else "fused into the decode kernel",
@@ -243,9 +247,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": _traffic({"workload": cfg.name, "seed": args.seed,
+                                 "kv_dtype": args.kv_dtype,
                                  "mode": ["split", "workqueue"][mode], "param": param,
                                  "merge": "two-launch" if two_launch else "fused"}),
-            "kernel": "pkv_decode_kernel<128, true, _Float16>",
+            "kernel": f"pkv_decode_kernel<{cfg.D}, {'true' if B <= 1024 else 'false'}, _Float16, "
+                      f"{'pkv::Fp8E4M3' if args.kv_dtype == 'fp8' else '_Float16'}>",
             "event_timed_steps": len(events),
             "algorithmic_bytes_per_launch": kv_bytes,
             "extras_bytes_per_launch": extras,

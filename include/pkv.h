@@ -33,8 +33,9 @@
  *   - Supported shapes: page_size = 16, head_dim in {64, 128, 256},
  *     G = Hq/Hkv in {1, 2, 4, 8} (at most 4 at head_dim 256).  Others return
  *     PKV_ERR_UNSUPPORTED.
- *   - Data types: q, K, V and out are fp16 or bf16 (pkv_dtype), all four the
- *     same.  lse and the partial states are fp32.  Indices are int32.
+ *   - Data types: q and out are fp16 or bf16; the K and V pools are the same
+ *     type or fp8 E4M3 with per-tensor dequantisation scales (pkv_dtype).
+ *     lse and the partial states are fp32.  Indices are int32.
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 /* Fixed-size head of every workspace: control words (task counter, exit
  * counter, error word) and the per-(row, KV head) arrival counters of the
@@ -67,11 +68,18 @@ enum pkv_status {
   PKV_ERR_HIP = 5               /* a HIP runtime call failed; see pkv_last_hip_error */
 };
 
-/* Element type of q, K, V and out (scores, softmax state and accumulators
- * are fp32 either way; lse is fp32). */
+/* Element types of q and out (E) and of the K and V pools.  Scores, softmax
+ * state and accumulators are fp32 in every case; lse is fp32.  The fp8 pools
+ * hold OCP 8-bit floating point E4M3 codes ("e4m3fn": bias 7, no
+ * infinities, S.1111.111 is NaN; OCP 8-bit Floating Point Specification
+ * (OFP8)), each exactly representable in E; their dequantised value is
+ * k_scale * code (K) and v_scale * code (V), per-tensor scales that the
+ * decode entry points take. */
 enum pkv_dtype {
-  PKV_DTYPE_F16 = 0,   /* IEEE half */
-  PKV_DTYPE_BF16 = 1   /* bfloat16 */
+  PKV_DTYPE_F16 = 0,          /* q, K, V, out: IEEE half */
+  PKV_DTYPE_BF16 = 1,         /* q, K, V, out: bfloat16 */
+  PKV_DTYPE_F16_KV_FP8 = 2,   /* q, out: IEEE half; K, V: fp8 E4M3 */
+  PKV_DTYPE_BF16_KV_FP8 = 3   /* q, out: bfloat16; K, V: fp8 E4M3 */
 };
 
 /* Scheduling modes of the task list (gist.science explainer, "2. Calibrated
@@ -156,7 +164,8 @@ int pkv_policy_defaults(pkv_policy_params* params);
  *   load = ceil(T / A) pmax              if T <= W   (every task static)
  *        = P / A + alpha pmax            otherwise   (dynamic queue),
  *   tile = 2 * page_size * head_dim * 2 bytes (K and V of one page of one
- *          KV head),
+ *          KV head, 2-byte elements; for fp8 pools the callers here pass
+ *          head_dim / 2, the same bytes),
  *   t = t0_us + t_round_us ceil(T / W) + load tile / (rho 1e3)
  *       + (maxS > fuse_max_splits ? t_two_us + t_two_split_us maxS
  *                                 : t_fused_split_us maxS).
@@ -272,10 +281,11 @@ int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stre
  * call falls back to the two-launch form.
  *
  * All pointers are device pointers.  Tensors are contiguous, row-major; E is
- * the element type `dtype` (pkv_dtype: fp16 or bf16):
+ * the q / out element type of `dtype` (pkv_dtype: fp16 or bf16):
  *   q            E     [B, Hq, head_dim]
- *   k_pool       E     [num_pages, Hkv, page_size, head_dim]
- *   v_pool       E     [num_pages, Hkv, page_size, head_dim]
+ *   k_pool       KV    [num_pages, Hkv, page_size, head_dim]
+ *   v_pool       KV    [num_pages, Hkv, page_size, head_dim]
+ *                (KV = E, or fp8 E4M3 codes for the *_KV_FP8 types)
  *   block_table  int32 [B, max_pages_per_row]
  *   seq_lens     int32 [B]
  *   tasks        int32 [num_tasks][4] and split_offsets int32 [B+1], as
@@ -290,6 +300,9 @@ int pkv_workspace_error_flags(const void* workspace, uint32_t* flags, void* stre
  *                ordered on one stream.  Concurrent calls need separate
  *                workspaces.
  * scale is the softmax scale (1/sqrt(head_dim) for standard attention).
+ * k_scale and v_scale dequantise the pools: attention runs over
+ * k_scale * K and v_scale * V (pass 1 and 1 for fp16 / bf16 pools; with 1
+ * the result is bit for bit the unscaled one).  Both must be finite and > 0.
  * q, k_pool, v_pool and out must be 16-byte aligned.
  *
  * Validation: scalar arguments and the alignment are checked on the host.
@@ -304,8 +317,8 @@ int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t nu
                const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, int32_t dtype,
-               float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-               void* stream);
+               float scale, float k_scale, float v_scale, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_decode_splits -- the first of pkv_decode's two launches: the persistent
@@ -320,8 +333,8 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
                       const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                       const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
                       int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                      int32_t dtype, float scale, void* out, float* lse, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      int32_t dtype, float scale, float k_scale, float v_scale, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_merge -- the second launch: the exact log-sum-exp merge (gist.science
@@ -390,8 +403,9 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
                            int64_t num_pages, const int32_t* block_table,
                            int32_t max_pages_per_row, const int32_t* seq_lens, int32_t B,
                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                           int32_t dtype, float scale, int32_t mode, int32_t param,
-                           int32_t max_splits, const pkv_policy_params* policy, int32_t num_cus,
+                           int32_t dtype, float scale, float k_scale, float v_scale,
+                           int32_t mode, int32_t param, int32_t max_splits,
+                           const pkv_policy_params* policy, int32_t num_cus,
                            void* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -454,8 +468,10 @@ typedef struct pkv_step_args {
   int32_t page_size;
   int32_t dtype;                 /* pkv_dtype of q, the pools and out */
   float scale;
+  float k_scale;                 /* dequantisation scales of the pools (1 for */
+  float v_scale;                 /* fp16 / bf16 pools), as for pkv_decode */
   /* device outputs and scratch */
-  void* out;                     /* fp16 [B, Hq, head_dim] */
+  void* out;                     /* E [B, Hq, head_dim] */
   float* lse;                    /* fp32 [B, Hq] or NULL */
   void* workspace;               /* as for pkv_decode */
   size_t workspace_bytes;

@@ -21,6 +21,10 @@ What it computes is fixed by the PersistentKV pages (arXiv 2606.26666):
     calls it roofline-style.  Here: a roofline-style time model of each
     candidate plan (``predict_us``), fastest candidate wins.
 
+fp8 KV pools (beyond the pages, which use FP16): the values are the OCP E4M3
+codes of the pool times a per-tensor scale (``e4m3_decode``, ``kv_values``),
+decoded from the format's published definition.
+
 Readings taken where the pages are silent (each also listed in the design doc):
   scale = 1/sqrt(d); query head h reads KV head floor(h/G); token t of a row
   lives in page block_table[b, t // 16] at slot t % 16; K and V pools are
@@ -38,6 +42,8 @@ from .ref import (  # noqa: F401
     MODE_WORKQUEUE,
     POLICY_DEFAULTS,
     attend,
+    e4m3_decode,
+    kv_values,
     merge_states,
     partial_state,
     plan_shape,

@@ -30,7 +30,44 @@ def _row_tokens(block_table, b, t0, t1, page_size):
     return block_table[b, t // page_size].astype(np.int64), t % page_size
 
 
-def attend(q, k_pool, v_pool, block_table, seq_lens, scale, page_size=16):
+# ---------------------------------------------------------------------------
+# fp8 KV values
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes):
+    """Value of OCP E4M3 codes ("e4m3fn"), float64.
+
+    Definition: OCP 8-bit Floating Point Specification (OFP8), the E4M3
+    format: 1 sign bit s, 4 exponent bits e with bias 7, 3 mantissa bits m;
+    e > 0 is normal, (-1)^s 2^(e-7) (1 + m/8); e = 0 is subnormal,
+    (-1)^s 2^-6 (m/8); there are no infinities, and e = 15 with m = 7 is
+    NaN (so the largest finite magnitude is 2^8 * 1.75 = 448).
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = sign * np.ldexp(m / 8.0, -6)
+    v = np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+def kv_values(pool, kv_scale=1.0):
+    """Dequantised values of a K or V pool, float64: kv_scale * x.
+
+    A uint8 pool holds E4M3 codes (``e4m3_decode``); any other array holds
+    the values themselves (fp16, or bf16 widened exactly to float32).  The
+    scale is the per-tensor dequantisation factor of an fp8 cache (1 for
+    fp16 / bf16).
+    """
+    a = np.asarray(pool)
+    x = e4m3_decode(a) if a.dtype == np.uint8 else a.astype(np.float64)
+    return x * float(kv_scale) if kv_scale != 1.0 else x
+
+
+def attend(q, k_pool, v_pool, block_table, seq_lens, scale, page_size=16, k_scale=1.0,
+           v_scale=1.0):
     """Single-query GQA attention of every row over its own paged KV.
 
     For row b, query head h, with G = Hq/Hkv and KV head g = floor(h/G)
@@ -40,8 +77,9 @@ def attend(q, k_pool, v_pool, block_table, seq_lens, scale, page_size=16):
         s_t  = scale * <q[b,h], K_t>          t = 0..N_b-1
         out  = sum_t softmax(s)_t * V_t
         lse  = log sum_t exp(s_t)
-    All arithmetic in float64 after exact upcast of the fp16 inputs.
-    N_b = 0 gives out = 0, lse = -inf.
+    All arithmetic in float64 after exact upcast of the inputs; K_t and V_t
+    are the dequantised values k_scale * K and v_scale * V (``kv_values``:
+    uint8 pools are fp8 E4M3 codes).  N_b = 0 gives out = 0, lse = -inf.
 
     Shapes: q [B,Hq,D]; k_pool, v_pool [num_pages, Hkv, page_size, D];
     block_table [B, max_pages]; seq_lens [B].  Returns (out [B,Hq,D],
@@ -53,6 +91,8 @@ def attend(q, k_pool, v_pool, block_table, seq_lens, scale, page_size=16):
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
+    k_pool = kv_values(k_pool, k_scale)
+    v_pool = kv_values(v_pool, v_scale)
     out = np.zeros((B, Hq, D), dtype=np.float64)
     lse = np.full((B, Hq), -np.inf, dtype=np.float64)
     for b in range(B):
@@ -158,19 +198,22 @@ def merge_states(m, l, o):
 
 
 def split_merge(q, k_pool, v_pool, block_table, seq_lens, scale, tasks, split_offsets,
-                page_size=16, extra_neutral=0):
+                page_size=16, extra_neutral=0, k_scale=1.0, v_scale=1.0):
     """Walk a task list, form each task's partial state, merge per (row, head).
 
     Task (b, g, s, c) covers tokens [s*c*P, min((s+1)*c*P, N_b)) of row b for
     KV head g and all G query heads of that group (the v1/v2 abstracts: work
     is mapped by KV-head group so one K/V tile serves the grouped query heads).
-    ``extra_neutral`` appends that many neutral states to every merge.
+    ``extra_neutral`` appends that many neutral states to every merge.  The
+    pools are read as in ``attend`` (``kv_values``).
     Returns (out [B,Hq,D], lse [B,Hq]) float64.
     """
     q = np.asarray(q)
     B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     G = Hq // Hkv
+    k_pool = kv_values(k_pool, k_scale)
+    v_pool = kv_values(v_pool, v_scale)
     nslots = int(split_offsets[-1])
     m = np.full((nslots, Hq), -np.inf)
     l = np.zeros((nslots, Hq))

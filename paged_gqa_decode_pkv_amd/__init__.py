@@ -19,7 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-PKV_ABI_VERSION = 3               # include/pkv.h; the argument lists below follow it
+PKV_ABI_VERSION = 4               # include/pkv.h; the argument lists below follow it
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = 1
 PKV_ERR_UNSUPPORTED = 2
@@ -29,6 +29,8 @@ PKV_ERR_HIP = 5
 
 PKV_DTYPE_F16 = 0
 PKV_DTYPE_BF16 = 1
+PKV_DTYPE_F16_KV_FP8 = 2       # q / out fp16, K / V pools fp8 E4M3 (torch.float8_e4m3fn)
+PKV_DTYPE_BF16_KV_FP8 = 3      # q / out bf16, K / V pools fp8 E4M3
 PKV_MODE_SPLIT = 0
 PKV_MODE_WORKQUEUE = 1
 
@@ -82,7 +84,7 @@ class pkv_step_args(ctypes.Structure):
         ("max_pages_per_row", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
         ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
         ("event_before_decode", ctypes.c_void_p), ("event_after_decode", ctypes.c_void_p),
         ("chosen_mode", ctypes.c_int32), ("chosen_param", ctypes.c_int32),
@@ -122,14 +124,15 @@ def _load():
         "pkv_workspace_init": ([_vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "pkv_workspace_error_flags": ([_vp, ctypes.POINTER(ctypes.c_uint32), _vp], ctypes.c_int),
         "pkv_decode": ([_vp, _vp, _vp, i64, _vp, i32, _vp, _vp, i64, _vp, i64, i32, i32, i32, i32,
-                        i32, i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp],
-                       ctypes.c_int),
+                        i32, i32, ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp,
+                        ctypes.c_size_t, _vp], ctypes.c_int),
         "pkv_merge": ([_vp, i64, i32, i32, i32, i32, i32, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                       ctypes.c_int),
         "pkv_workspace_size_device_plan": ([i32, i32, i32, i32, i32,
                                             ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "pkv_decode_device_plan": ([_vp, _vp, _vp, i64, _vp, i32, _vp, i32, i32, i32, i32, i32,
-                                    i32, ctypes.c_float, i32, i32, i32,
+                                    i32, ctypes.c_float, ctypes.c_float, ctypes.c_float, i32, i32,
+                                    i32,
                                     ctypes.POINTER(pkv_policy_params), i32, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp], ctypes.c_int),
         "pkv_device_plan_read": ([_vp, ctypes.c_size_t, i32, i32, i32, i32, i32, _i32p, _vp, _vp,
@@ -273,6 +276,31 @@ def _elem_dtype(*tensors):
     return codes[dt], dt
 
 
+def _fp8_dtype():
+    import torch
+    return getattr(torch, "float8_e4m3fn", None)
+
+
+def _dtypes(q, k_pool, v_pool, out):
+    """(pkv_dtype code, q / out torch dtype, pool torch dtype).  q and out are
+    float16 or bfloat16; the pools are that same type or float8_e4m3fn."""
+    import torch
+    e = q.dtype
+    if e not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"q must be float16 or bfloat16, got {e}")
+    if out.dtype != e:
+        raise TypeError(f"q and out must share one dtype ({e} vs {out.dtype})")
+    kv = k_pool.dtype
+    if v_pool.dtype != kv:
+        raise TypeError(f"k_pool and v_pool must share one dtype ({kv} vs {v_pool.dtype})")
+    f16 = e == torch.float16
+    if kv == e:
+        return (PKV_DTYPE_F16 if f16 else PKV_DTYPE_BF16), e, kv
+    if kv == _fp8_dtype():
+        return (PKV_DTYPE_F16_KV_FP8 if f16 else PKV_DTYPE_BF16_KV_FP8), e, kv
+    raise TypeError(f"the pools must be {e} or float8_e4m3fn, got {kv}")
+
+
 def _dev(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -300,7 +328,7 @@ def pkv_workspace_error_flags(workspace, stream=None) -> int:
 
 
 def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
-                 num_partial_slots, scale, out, workspace, lse, stream):
+                 num_partial_slots, scale, out, workspace, lse, stream, k_scale=1.0, v_scale=1.0):
     """Checked ctypes argument tuple shared by pkv_decode and pkv_decode_splits.
 
     q [B,Hq,d] fp16, k_pool / v_pool [pages,Hkv,16,d] fp16, block_table
@@ -309,7 +337,7 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
     """
     import torch
     i32 = torch.int32
-    code, f16 = _elem_dtype(q, k_pool, v_pool, out)
+    code, f16, kvt = _dtypes(q, k_pool, v_pool, out)
     B, Hq, D = q.shape
     num_pages, Hkv, P, Dk = k_pool.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
@@ -321,11 +349,11 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
     if lse is not None and tuple(lse.shape) != (B, Hq):
         raise ValueError("lse must be [B, Hq]")
     args = (
-        _dev(q, f16, "q"), _dev(k_pool, f16, "k_pool"), _dev(v_pool, f16, "v_pool"), num_pages,
+        _dev(q, f16, "q"), _dev(k_pool, kvt, "k_pool"), _dev(v_pool, kvt, "v_pool"), num_pages,
         _dev(block_table, i32, "block_table"), block_table.shape[1],
         _dev(seq_lens, i32, "seq_lens"), _dev(tasks, i32, "tasks"), tasks.shape[0],
         _dev(split_offsets, i32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D, P, code,
-        float(scale), _dev(out, f16, "out"),
+        float(scale), float(k_scale), float(v_scale), _dev(out, f16, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream),
     )
@@ -333,18 +361,20 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
 
 
 def pkv_decode(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
-               num_partial_slots: int, scale: float, out, workspace, lse=None, stream=None):
+               num_partial_slots: int, scale: float, out, workspace, lse=None, stream=None,
+               k_scale: float = 1.0, v_scale: float = 1.0):
     """Enqueue decode + merge on ``stream``; see pkv_decode in include/pkv.h."""
     args = _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
-                        num_partial_slots, scale, out, workspace, lse, stream)
+                        num_partial_slots, scale, out, workspace, lse, stream, k_scale, v_scale)
     _check(_load().pkv_decode(*args), "pkv_decode")
 
 
 def pkv_decode_splits(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
-                      num_partial_slots: int, scale: float, out, workspace, lse=None, stream=None):
+                      num_partial_slots: int, scale: float, out, workspace, lse=None, stream=None,
+                      k_scale: float = 1.0, v_scale: float = 1.0):
     """Enqueue the decode kernel only; see pkv_decode_splits in include/pkv.h."""
     args = _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
-                        num_partial_slots, scale, out, workspace, lse, stream)
+                        num_partial_slots, scale, out, workspace, lse, stream, k_scale, v_scale)
     _check(_load().pkv_decode_splits(*args), "pkv_decode_splits")
 
 
@@ -380,12 +410,12 @@ def pkv_workspace_size_device_plan(B: int, Hq: int, Hkv: int, head_dim: int,
 def pkv_decode_device_plan(q, k_pool, v_pool, block_table, seq_lens, scale: float, out,
                            workspace, max_splits: int, lse=None, mode: int = -1, param: int = 0,
                            params: Optional[pkv_policy_params] = None, num_cus: int = 0,
-                           stream=None):
+                           stream=None, k_scale: float = 1.0, v_scale: float = 1.0):
     """One step planned on the device; see pkv_decode_device_plan in include/pkv.h.
     seq_lens is a device tensor: nothing is read on the host."""
     import torch
     i32 = torch.int32
-    code, f16 = _elem_dtype(q, k_pool, v_pool, out)
+    code, f16, kvt = _dtypes(q, k_pool, v_pool, out)
     B, Hq, D = q.shape
     num_pages, Hkv, P, Dk = k_pool.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (B, Hq, D):
@@ -396,9 +426,10 @@ def pkv_decode_device_plan(q, k_pool, v_pool, block_table, seq_lens, scale: floa
         raise ValueError("lse must be [B, Hq]")
     pp = ctypes.byref(params) if params is not None else None
     _check(_load().pkv_decode_device_plan(
-        _dev(q, f16, "q"), _dev(k_pool, f16, "k_pool"), _dev(v_pool, f16, "v_pool"), num_pages,
+        _dev(q, f16, "q"), _dev(k_pool, kvt, "k_pool"), _dev(v_pool, kvt, "v_pool"), num_pages,
         _dev(block_table, i32, "block_table"), block_table.shape[1], _dev(seq_lens, i32, "seq_lens"),
-        B, Hq, Hkv, D, P, code, float(scale), mode, param, max_splits, pp, num_cus,
+        B, Hq, Hkv, D, P, code, float(scale), float(k_scale), float(v_scale), mode, param,
+        max_splits, pp, num_cus,
         _dev(out, f16, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream)),
         "pkv_decode_device_plan")
@@ -499,7 +530,7 @@ class PagedDecoder:
             pass
 
     def set_inputs(self, q, k_pool, v_pool, block_table, seq_lens, seq_lens_h, scale: float,
-                   out, lse=None):
+                   out, lse=None, k_scale: float = 1.0, v_scale: float = 1.0):
         """Bind the tensors of the next steps (checked once here)."""
         import torch
         B, Hq, D = q.shape
@@ -512,17 +543,19 @@ class PagedDecoder:
         if lse is not None and tuple(lse.shape) != (B, Hq):
             raise ValueError("lse must be [B, Hq]")
         a = self.args
-        code, edt = _elem_dtype(q, k_pool, v_pool, out)
+        code, edt, kvt = _dtypes(q, k_pool, v_pool, out)
         a.dtype = code
         a.q = _dev(q, edt, "q").value
-        a.k_pool = _dev(k_pool, edt, "k_pool").value
-        a.v_pool = _dev(v_pool, edt, "v_pool").value
+        a.k_pool = _dev(k_pool, kvt, "k_pool").value
+        a.v_pool = _dev(v_pool, kvt, "v_pool").value
         a.num_pages = k_pool.shape[0]
         a.block_table = _dev(block_table, torch.int32, "block_table").value
         a.seq_lens = _dev(seq_lens, torch.int32, "seq_lens").value
         a.out = _dev(out, edt, "out").value
         a.lse = _dev(lse, torch.float32, "lse").value if lse is not None else None
         a.scale = float(scale)
+        a.k_scale = float(k_scale)
+        a.v_scale = float(v_scale)
         self._seq_host = np.ascontiguousarray(seq_lens_h, dtype=np.int32)
         a.seq_lens_host = self._seq_host.ctypes.data
         a.B = B

@@ -41,6 +41,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -92,6 +93,56 @@ struct Mfma<__bf16> {
   }
 };
 
+// KV pool element types.  A 2-byte pool holds E itself.  An fp8 pool holds
+// OCP E4M3 codes ("e4m3fn": sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; no infinities; S.1111.111 is NaN), which every E represents exactly,
+// so the kernel converts them to E in registers and keeps E's MFMA path.
+struct Fp8E4M3 {};
+template <class KV>
+constexpr int kv_bytes() {
+  return 2;
+}
+template <>
+constexpr int kv_bytes<Fp8E4M3>() {
+  return 1;
+}
+
+typedef unsigned uint4x __attribute__((ext_vector_type(4)));
+
+// Two codes (bytes 2*kHi, 2*kHi+1 of w) to E, exact: the hardware converter
+// with a unit scale.
+template <class E, bool kHi>
+__device__ __forceinline__ vecE<E, 2> fp8x2(uint32_t w);
+template <>
+__device__ __forceinline__ vecE<_Float16, 2> fp8x2<_Float16, false>(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+template <>
+__device__ __forceinline__ vecE<_Float16, 2> fp8x2<_Float16, true>(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+template <>
+__device__ __forceinline__ vecE<__bf16, 2> fp8x2<__bf16, false>(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+template <>
+__device__ __forceinline__ vecE<__bf16, 2> fp8x2<__bf16, true>(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+// Four codes (the bytes of w, lowest first) to E.
+template <class E>
+__device__ __forceinline__ vecE<E, 4> fp8x4(uint32_t w) {
+  const vecE<E, 2> lo = fp8x2<E, false>(w);
+  const vecE<E, 2> hi = fp8x2<E, true>(w);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+template <class E>
+__device__ __forceinline__ vecE<E, 8> fp8x8(uint2x w) {
+  const vecE<E, 4> a = fp8x4<E>(w[0]);
+  const vecE<E, 4> b = fp8x4<E>(w[1]);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 constexpr int kPage = 16;
 constexpr int kWaves = 4;             // waves per workgroup (one task at a time)
 constexpr int kThreads = 64 * kWaves;
@@ -113,7 +164,8 @@ struct DecodeArgs {
   const int32_t* split_offsets;
   int64_t num_slots;
   int32_t B, Hq, Hkv, G;
-  float scale_log2;   // softmax scale * log2(e)
+  float scale_log2;   // softmax scale * K's dequantisation scale * log2(e)
+  float v_scale;      // V's dequantisation scale
   void* out;          // E [B, Hq, D]
   float* lse;
   uint32_t* ctrl;     // [0] task counter, [1] exit counter, [2] error word
@@ -130,13 +182,52 @@ __device__ __forceinline__ void flag_error(uint32_t* ctrl, uint32_t bits) {
 }
 
 // Per-page registers of one wave: the K operand and the raw V rows.
-template <int D, class E>
+template <int D, class E, class KV>
 struct PageRegs {
   static constexpr int KK = D / 32;
   static constexpr int VW = D / 16;
   vecE<E, 8> k[KK];
   vecE<E, VW> v[4];
 };
+
+// N fp8 codes in one, two or four dwords.
+template <int N>
+struct CodeVec;
+template <>
+struct CodeVec<4> {
+  using T = uint32_t;
+};
+template <>
+struct CodeVec<8> {
+  using T = uint2x;
+};
+template <>
+struct CodeVec<16> {
+  using T = uint4x;
+};
+
+// An fp8 pool keeps the codes as loaded (half the registers of a 2-byte
+// page); process_page converts them.
+template <int D, class E>
+struct PageRegs<D, E, Fp8E4M3> {
+  static constexpr int KK = D / 32;
+  static constexpr int VW = D / 16;
+  uint2x k[KK];                    // the 8 codes of the K operand of chunk kk
+  typename CodeVec<VW>::T v[4];    // VW codes of token row 4*grp + j
+};
+
+template <class E, int N>
+__device__ __forceinline__ vecE<E, N> fp8_row(typename CodeVec<N>::T c) {
+  if constexpr (N == 4) {
+    return fp8x4<E>(c);
+  } else if constexpr (N == 8) {
+    return fp8x8<E>(c);
+  } else {
+    const vecE<E, 8> a = fp8x8<E>(uint2x{c[0], c[1]});
+    const vecE<E, 8> b = fp8x8<E>(uint2x{c[2], c[3]});
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  }
+}
 
 // Buffer resource for raw buffer loads (gfx9 dword3).  Loads at offsets
 // >= num_records return zero without touching memory.  This gives the
@@ -161,30 +252,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // voff = 2*(4*grp*D + VW*col)).  Each K instruction reads 16 runs of 64
 // contiguous bytes, and each V instruction reads 4 whole 2*D-byte rows of
 // the contiguous page tile.
-template <int D, class E>
-__device__ __forceinline__ void load_page(PageRegs<D, E>& r, __amdgpu_buffer_rsrc_t kr,
+template <int D, class E, class KV>
+__device__ __forceinline__ void load_page(PageRegs<D, E, KV>& r, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, int koff, int voff) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
+  if constexpr (kv_bytes<KV>() == 1) {
+    // the same lanes and rows, at one byte per element
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    r.k[kk] = __builtin_bit_cast(vecE<E, 8>,
-                                 __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
+    for (int kk = 0; kk < KK; ++kk)
+      r.k[kk] = __builtin_bit_cast(
+          uint2x, __builtin_amdgcn_raw_buffer_load_b64(kr, koff + 32 * kk, 0, 0));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (VW == 16) {
-      const vecE<E, 8> lo = __builtin_bit_cast(
-          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
-      const vecE<E, 8> hi = __builtin_bit_cast(
-          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, 0));
-      r.v[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14,
-                                       15);
-    } else if constexpr (VW == 8) {
-      r.v[j] = __builtin_bit_cast(vecE<E, VW>,
-                                  __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
-    } else {
-      r.v[j] = __builtin_bit_cast(vecE<E, VW>,
-                                  __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, 0));
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (VW == 16)
+        r.v[j] = __builtin_bit_cast(uint4x,
+                                    __builtin_amdgcn_raw_buffer_load_b128(vr, voff + D * j, 0, 0));
+      else if constexpr (VW == 8)
+        r.v[j] = __builtin_bit_cast(uint2x,
+                                    __builtin_amdgcn_raw_buffer_load_b64(vr, voff + D * j, 0, 0));
+      else
+        r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff + D * j, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      r.k[kk] = __builtin_bit_cast(
+          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (VW == 16) {
+        const vecE<E, 8> lo = __builtin_bit_cast(
+            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
+        const vecE<E, 8> hi = __builtin_bit_cast(
+            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, 0));
+        r.v[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
+                                         14, 15);
+      } else if constexpr (VW == 8) {
+        r.v[j] = __builtin_bit_cast(
+            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
+      } else {
+        r.v[j] = __builtin_bit_cast(
+            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, 0));
+      }
     }
   }
 }
@@ -207,19 +317,26 @@ struct WaveState {
   floatx4 acc[VW];      // O^T block e: lane holds O[head col][VW*(4*grp+j)+e]
 };
 
-template <int D, class E>
-__device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D, E>& pg,
+template <int D, class E, class KV>
+__device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D, E, KV>& pg,
                                              const vecE<E, 8>* __restrict__ qf_lds, int nvalid,
                                              float scale_log2, int lane) {
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
+  constexpr bool kFp8 = kv_bytes<KV>() == 1;
   const int grp = lane >> 4;
   // S^T = K . Q^T: lane holds the raw scores of tokens 4*grp+j for head col.
   // The q operand is re-read from LDS for each page (saves 16 VGPRs).
   floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    sacc = Mfma<E>::k32(pg.k[kk], qf_lds[kk * 64 + lane], sacc);
+  for (int kk = 0; kk < KK; ++kk) {
+    vecE<E, 8> kop;
+    if constexpr (kFp8)
+      kop = fp8x8<E>(pg.k[kk]);
+    else
+      kop = pg.k[kk];
+    sacc = Mfma<E>::k32(kop, qf_lds[kk * 64 + lane], sacc);
+  }
   float sc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) sc[j] = sacc[j] * scale_log2;
@@ -228,7 +345,7 @@ __device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D, E>& p
     for (int j = 0; j < 4; ++j) {
       const bool live = 4 * grp + j < nvalid;
       sc[j] = live ? sc[j] : -INFINITY;
-      if (!live) pg.v[j] = vecE<E, VW>{};
+      if (!live) pg.v[j] = {};   // E zeros, or fp8 code 0 (+0)
     }
   }
   const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -248,10 +365,19 @@ __device__ __forceinline__ void process_page(WaveState<D>& st, PageRegs<D, E>& p
   for (int j = 0; j < 4; ++j) pb[j] = static_cast<E>(fast_exp2(sc[j] - st.m));
   st.l += (static_cast<float>(pb[0]) + static_cast<float>(pb[1])) +
           (static_cast<float>(pb[2]) + static_cast<float>(pb[3]));
+  // V rows in E (converted from the codes for an fp8 pool)
+  vecE<E, VW> vr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (kFp8)
+      vr[j] = fp8_row<E, VW>(pg.v[j]);
+    else
+      vr[j] = pg.v[j];
+  }
   // O^T += V^T . P^T, one 16x16x16 MFMA per 16 output columns
 #pragma unroll
   for (int e = 0; e < VW; ++e) {
-    const vecE<E, 4> av = {pg.v[0][e], pg.v[1][e], pg.v[2][e], pg.v[3][e]};
+    const vecE<E, 4> av = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
     st.acc[e] = Mfma<E>::k16(av, pb, st.acc[e]);
   }
 }
@@ -386,10 +512,11 @@ __device__ __forceinline__ void write_empty_group(const MergeArgs& a, int b, int
 constexpr int kRowStage = 1024;
 // Page tiles in flight per wave (one "round"): 4 at d <= 128; at d = 256 a
 // tile holds twice the bytes and registers, so 2 keep the same 32 KiB in
-// flight per wave within the register budget.
-template <int D>
+// flight per wave within the register budget.  An fp8 tile holds half the
+// bytes of a 2-byte one, so twice as many keep the same bytes in flight.
+template <int D, class KV>
 constexpr int ring_depth() {
-  return D == 256 ? 2 : 4;
+  return (D == 256 ? 2 : 4) * (2 / kv_bytes<KV>());
 }
 
 // Largest GQA group a head dimension supports: the merge gives one float4
@@ -551,7 +678,7 @@ __device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_
 
 // Two workgroups per CU at d <= 128 (256 VGPRs each); one at d = 256, whose
 // larger tiles and accumulators need the AGPR half of the register file.
-template <int D, bool kStaged, class E>
+template <int D, bool kStaged, class E, class KV>
 __global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
 pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
@@ -559,8 +686,9 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   constexpr int KK = D / 32;
   constexpr int VW = D / 16;
   constexpr int LDS_STRIDE = D + 4;
-  constexpr uint32_t kTileBytes = static_cast<uint32_t>(kPage * D * 2);
-  constexpr int kRing = ring_depth<D>();
+  constexpr int kKvb = kv_bytes<KV>();
+  constexpr uint32_t kTileBytes = static_cast<uint32_t>(kPage * D * kKvb);
+  constexpr int kRing = ring_depth<D, KV>();
   constexpr int kGroup = max_group<D>();
 
   const int tid = threadIdx.x;
@@ -624,25 +752,26 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
 
   const int G = a.G;
   const int64_t tile_elems = static_cast<int64_t>(kPage) * D;
-  const int64_t stride_bytes = static_cast<int64_t>(a.Hkv) * tile_elems * 2;
-  const int koff = 2 * (col * D + 8 * grp);
-  const int voff = 2 * (4 * grp * D + VW * col);
+  const int64_t stride_bytes = static_cast<int64_t>(a.Hkv) * tile_elems * kKvb;
+  const int koff = kKvb * (col * D + 8 * grp);
+  const int voff = kKvb * (4 * grp * D + VW * col);
   const char* kpool = reinterpret_cast<const char*>(a.k);
   const char* vpool = reinterpret_cast<const char*>(a.v);
 
   // Load the page at position `pos` of task m (entry e) into `r`.  A
   // position past the range, an invalid task or an out-of-pool entry loads
   // nothing (num_records = 0) and returns false.
-  auto issue = [&](const Meta& m, int pos, int e, PageRegs<D, E>& r) -> bool {
+  auto issue = [&](const Meta& m, int pos, int e, PageRegs<D, E, KV>& r) -> bool {
     const int page = m.p0 + wave + kWaves * pos;
     const bool want = m.ok && page < m.p1;
     const bool inr = e >= 0 && static_cast<int64_t>(e) < a.num_pages;
     if (want && !inr && lane == 0) flag_error(a.ctrl, PKV_DEVERR_PAGE);
     const bool live = want && inr;
-    const int64_t off = static_cast<int64_t>(m.g) * tile_elems * 2 +
+    const int64_t off = static_cast<int64_t>(m.g) * tile_elems * kKvb +
                         (live ? static_cast<int64_t>(e) * stride_bytes : 0);
     const uint32_t bytes = live ? kTileBytes : 0u;
-    load_page<D, E>(r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff, voff);
+    load_page<D, E, KV>(r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff,
+                        voff);
     return live;
   };
   // q of task m (B operand of the score MFMA, column = head within the
@@ -667,7 +796,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                                          blockIdx.x,
                                   rec0);
   int t_nxt = blockIdx.x + gridDim.x;
-  PageRegs<D, E> ring[kRing];
+  PageRegs<D, E, KV> ring[kRing];
   bool valid[kRing];
   {
     const Round<kRing> r0 = load_round<kRing>(a, bt_in, cur, wave, 0);
@@ -717,7 +846,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       for (int r = 0; r < kRing; ++r) {
         if (valid[r]) {
           const int page = cur.p0 + wave + kWaves * (kRing * j + r);
-          process_page<D, E>(st, ring[r], s_q[par], cur.N - page * kPage, a.scale_log2, lane);
+          process_page<D, E, KV>(st, ring[r], s_q[par], cur.N - page * kPage, a.scale_log2,
+                                 lane);
         }
         // refill the slot with the position one round ahead
         if (last)
@@ -759,6 +889,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
           L += wt * s_l[par][w][h];
           O += wt * s_o[par][w][h][d];
         }
+        O *= a.v_scale;   // V's dequantisation scale (exact for 1)
         const int64_t hq = static_cast<int64_t>(cur.g) * G + h;
         if (direct) {
           static_cast<E*>(a.out)[(static_cast<int64_t>(cur.b) * a.Hq + hq) * D + d] =
@@ -1086,17 +1217,17 @@ int num_cus_of_current_device(int* cus) {
   return PKV_OK;
 }
 
-template <int D, class E>
+template <int D, class E, class KV>
 int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
            bool decode) {
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     if (da.B <= kRowStage)
-      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E>), dim3(grid), dim3(kThreads), 0, stream, da,
-                         tasks, da.block_table, da.seq_lens, da.split_offsets);
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV>), dim3(grid), dim3(kThreads), 0,
+                         stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
     else
-      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E>), dim3(grid), dim3(kThreads), 0, stream, da,
-                         tasks, da.block_table, da.seq_lens, da.split_offsets);
+      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV>), dim3(grid), dim3(kThreads), 0,
+                         stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       set_hip_error(static_cast<int>(e));
@@ -1115,18 +1246,28 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
   return PKV_OK;
 }
 
-// The kernels of one head dimension and element type (both checked by the
-// caller).
+template <class E, class KV>
+int launch_d(int head_dim, const DecodeArgs& da, const MergeArgs& ma, int grid,
+             hipStream_t stream, bool decode) {
+  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode);
+  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode)
+                         : launch<64, E, KV>(da, ma, grid, stream, decode);
+}
+
+// The kernels of one head dimension and element-type pair (both checked by
+// the caller).
 int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& ma, int grid,
                hipStream_t stream, bool decode) {
-  if (dtype == PKV_DTYPE_BF16) {
-    if (head_dim == 256) return launch<256, __bf16>(da, ma, grid, stream, decode);
-    return head_dim == 128 ? launch<128, __bf16>(da, ma, grid, stream, decode)
-                           : launch<64, __bf16>(da, ma, grid, stream, decode);
+  switch (dtype) {
+    case PKV_DTYPE_BF16:
+      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode);
+    case PKV_DTYPE_F16_KV_FP8:
+      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode);
+    case PKV_DTYPE_BF16_KV_FP8:
+      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode);
+    default:
+      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode);
   }
-  if (head_dim == 256) return launch<256, _Float16>(da, ma, grid, stream, decode);
-  return head_dim == 128 ? launch<128, _Float16>(da, ma, grid, stream, decode)
-                         : launch<64, _Float16>(da, ma, grid, stream, decode);
 }
 
 }  // namespace pkv
@@ -1166,13 +1307,15 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
             const int32_t* block_table, int32_t max_pages_per_row, const int32_t* seq_lens,
             const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,
             int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
-            int32_t page_size, int32_t dtype, float scale, void* out, float* lse, void* workspace,
-            size_t workspace_bytes, bool need_decode, pkv::DecodeArgs* da, pkv::MergeArgs* ma) {
+            int32_t page_size, int32_t dtype, float scale, float k_scale, float v_scale,
+            void* out, float* lse, void* workspace, size_t workspace_bytes, bool need_decode,
+            pkv::DecodeArgs* da, pkv::MergeArgs* ma) {
   if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 0 || max_pages_per_row < 0 || num_tasks < 0 ||
-      num_tasks > INT32_MAX || num_partial_slots < 0 || !(scale == scale))
+      num_tasks > INT32_MAX || num_partial_slots < 0 || !(scale == scale) ||
+      !(k_scale > 0.f && k_scale <= FLT_MAX) || !(v_scale > 0.f && v_scale <= FLT_MAX))
     return PKV_ERR_INVALID_ARG;
   if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
-      Hq % Hkv != 0 || (dtype != PKV_DTYPE_F16 && dtype != PKV_DTYPE_BF16))
+      Hq % Hkv != 0 || dtype < PKV_DTYPE_F16 || dtype > PKV_DTYPE_BF16_KV_FP8)
     return PKV_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
@@ -1215,7 +1358,8 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   da->Hq = Hq;
   da->Hkv = Hkv;
   da->G = G;
-  da->scale_log2 = scale * 1.44269504088896340736f;
+  da->scale_log2 = scale * k_scale * 1.44269504088896340736f;
+  da->v_scale = v_scale;
   da->out = out;
   da->lse = lse;
   da->ctrl = ctrl;
@@ -1242,13 +1386,15 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
         const int32_t* block_table, int32_t max_pages_per_row, const int32_t* seq_lens,
         const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,
         int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
-        int32_t page_size, int32_t dtype, float scale, void* out, float* lse, void* workspace,
-        size_t workspace_bytes, void* stream, bool do_decode, bool do_merge, bool fused) {
+        int32_t page_size, int32_t dtype, float scale, float k_scale, float v_scale, void* out,
+        float* lse, void* workspace, size_t workspace_bytes, void* stream, bool do_decode,
+        bool do_merge, bool fused) {
   pkv::DecodeArgs da{};
   pkv::MergeArgs ma{};
   int st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
                    num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size,
-                   dtype, scale, out, lse, workspace, workspace_bytes, do_decode, &da, &ma);
+                   dtype, scale, k_scale, v_scale, out, lse, workspace, workspace_bytes, do_decode,
+                   &da, &ma);
   if (st != PKV_OK || B == 0) return st;
   // Fused single launch when the arrival counters fit and there is work for
   // the decode kernel; otherwise the two-launch form.
@@ -1284,11 +1430,12 @@ int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t nu
                const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, int32_t dtype,
-               float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               float scale, float k_scale, float v_scale, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
              num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
-             scale, out, lse, workspace, workspace_bytes, stream, true, true, true);
+             scale, k_scale, v_scale, out, lse, workspace, workspace_bytes, stream, true, true,
+             true);
 }
 
 int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
@@ -1296,19 +1443,20 @@ int pkv_decode_splits(const void* q, const void* k_pool, const void* v_pool, int
                       const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
                       const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
                       int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                      int32_t dtype, float scale, void* out, float* lse, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int32_t dtype, float scale, float k_scale, float v_scale, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
              num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
-             scale, out, lse, workspace, workspace_bytes, stream, true, false, false);
+             scale, k_scale, v_scale, out, lse, workspace, workspace_bytes, stream, true, false,
+             false);
 }
 
 int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B, int32_t Hq,
               int32_t Hkv, int32_t head_dim, int32_t dtype, void* out, float* lse,
               void* workspace, size_t workspace_bytes, void* stream) {
   return run(nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, 0, split_offsets,
-             num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, dtype, 1.0f, out, lse,
-             workspace, workspace_bytes, stream, false, true, false);
+             num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, dtype, 1.0f, 1.0f, 1.0f, out,
+             lse, workspace, workspace_bytes, stream, false, true, false);
 }
 
 }  // extern "C"
@@ -1359,8 +1507,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
                            int64_t num_pages, const int32_t* block_table,
                            int32_t max_pages_per_row, const int32_t* seq_lens, int32_t B,
                            int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
-                           int32_t dtype, float scale, int32_t mode, int32_t param,
-                           int32_t max_splits,
+                           int32_t dtype, float scale, float k_scale, float v_scale,
+                           int32_t mode, int32_t param, int32_t max_splits,
                            const pkv_policy_params* policy, int32_t num_cus, void* out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   pkv_policy_params pol;
@@ -1404,8 +1552,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   pkv::DecodeArgs da{};
   pkv::MergeArgs ma{};
   st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
-               L.task_cap, offs, L.slot_cap, B, Hq, Hkv, head_dim, page_size, dtype, scale, out,
-               lse, workspace, workspace_bytes, true, &da, &ma);
+               L.task_cap, offs, L.slot_cap, B, Hq, Hkv, head_dim, page_size, dtype, scale,
+               k_scale, v_scale, out, lse, workspace, workspace_bytes, true, &da, &ma);
   if (st != PKV_OK || B == 0) return st;
   if (num_cus <= 0) {
     st = pkv::num_cus_of_current_device(&num_cus);
@@ -1415,7 +1563,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   pa.seq_lens = seq_lens;
   pa.B = B;
   pa.Hkv = Hkv;
-  pa.head_dim = head_dim;
+  // the model's tile bytes assume 2-byte elements: an fp8 pool moves half
+  pa.head_dim = pkv::policy_head_dim(head_dim, dtype);
   pa.page_size = page_size;
   pa.num_cus = num_cus;
   pa.max_pages = max_pages_per_row;

@@ -218,8 +218,8 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   // policy ("2. Calibrated Adaptive Policy")
   int32_t mode = a->mode, param = a->param;
   if (mode < 0) {
-    int st = pkv_policy(a->seq_lens_host, a->B, a->Hkv, a->head_dim, a->page_size, r->num_cus,
-                        &r->params, &mode, &param);
+    int st = pkv_policy(a->seq_lens_host, a->B, a->Hkv, pkv::policy_head_dim(a->head_dim, a->dtype),
+                        a->page_size, r->num_cus, &r->params, &mode, &param);
     if (st != PKV_OK) return st;
   }
   a->chosen_mode = mode;
@@ -325,13 +325,14 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   if (two) {
     st = pkv_decode_splits(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
                            a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B,
-                           a->Hq, a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale, a->out,
-                           a->lse, a->workspace, a->workspace_bytes, a->stream);
+                           a->Hq, a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale,
+                           a->k_scale, a->v_scale, a->out, a->lse, a->workspace,
+                           a->workspace_bytes, a->stream);
   } else {
     st = pkv_decode(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
                     a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B, a->Hq,
-                    a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale, a->out, a->lse,
-                    a->workspace, a->workspace_bytes, a->stream);
+                    a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale, a->k_scale,
+                    a->v_scale, a->out, a->lse, a->workspace, a->workspace_bytes, a->stream);
   }
   if (st != PKV_OK) return st;
   if (a->event_after_decode) {

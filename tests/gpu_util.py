@@ -44,9 +44,10 @@ def check_lse(got, ref, atol=LSE_ATOL):
         assert err <= atol, f"lse: max abs err {err:.3e}"
 
 
-def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1, two_launch=None):
+def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1, two_launch=None,
+            k_scale=1.0, v_scale=1.0):
     """Plan + decode through the C ABI (fused single launch, or the two-launch
-    decode + merge form).  Returns (out fp16 tensor, lse tensor|None, decoder)."""
+    decode + merge form).  Returns (out tensor, lse tensor|None, decoder)."""
     import torch
     import paged_gqa_decode_pkv_amd as pkv
 
@@ -61,17 +62,17 @@ def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1, two_la
     pkv.pkv_plan(wl.seq_lens_np, cfg.Hkv, wl.block_table_np.shape[1], 0, 1,
                  block_table=wl.block_table_np, num_pages=wl.k_pool.shape[0])
     decoder.set_inputs(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, wl.seq_lens_np,
-                       cfg.scale, out, lse_t)
+                       cfg.scale, out, lse_t, k_scale=k_scale, v_scale=v_scale)
     for _ in range(repeats):
         decoder.run(mode, param, two_launch=two_launch)
     torch.cuda.synchronize()
     return out, lse_t, decoder
 
 
-def oracle_rows(wl, rows=None):
+def oracle_rows(wl, rows=None, k_scale=1.0, v_scale=1.0):
     """Float64 oracle on the given rows (all rows by default), pages copied
-    from wherever the workload lives."""
+    from wherever the workload lives (fp8 pools as their E4M3 codes)."""
     if rows is None:
         rows = range(len(wl.seq_lens_np))
     q, k, v, bt, sl = compact_rows(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, rows)
-    return oracle.attend(q, k, v, bt, sl, wl.cfg.scale)
+    return oracle.attend(q, k, v, bt, sl, wl.cfg.scale, k_scale=k_scale, v_scale=v_scale)

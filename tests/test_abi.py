@@ -242,17 +242,21 @@ def test_workspace_size():
 def test_decode_rejects_bad_scalars_before_touching_the_device():
     lib = pkv._load()
     common = dict(q=None, k=None, v=None)
-    def call(B=1, Hq=4, Hkv=1, D=64, P=16, scale=0.125, dtype=pkv.PKV_DTYPE_F16):
+    def call(B=1, Hq=4, Hkv=1, D=64, P=16, scale=0.125, dtype=pkv.PKV_DTYPE_F16, ks=1.0, vs=1.0):
         return lib.pkv_decode(None, None, None, 0, None, 1, None, None, 0, None, 0, B, Hq, Hkv, D,
-                              P, dtype, scale, None, None, None, 0, None)
+                              P, dtype, scale, ks, vs, None, None, None, 0, None)
     assert call(D=96) == pkv.PKV_ERR_UNSUPPORTED
     assert call(D=256, Hq=8, Hkv=1) == pkv.PKV_ERR_UNSUPPORTED    # G = 8 at d = 256
     assert call(D=256, Hq=4, Hkv=1) == pkv.PKV_ERR_INVALID_ARG    # supported; null pointers
     assert call(P=32) == pkv.PKV_ERR_UNSUPPORTED
     assert call(Hq=6, Hkv=4) == pkv.PKV_ERR_UNSUPPORTED      # Hq % Hkv
     assert call(Hq=48, Hkv=3) == pkv.PKV_ERR_UNSUPPORTED     # G = 16
-    assert call(dtype=2) == pkv.PKV_ERR_UNSUPPORTED          # no such element type
-    assert call(dtype=pkv.PKV_DTYPE_BF16) == pkv.PKV_ERR_INVALID_ARG   # bf16 ok, null pointers
+    assert call(dtype=4) == pkv.PKV_ERR_UNSUPPORTED          # no such element type
+    assert call(dtype=-1) == pkv.PKV_ERR_UNSUPPORTED
+    for dt in (pkv.PKV_DTYPE_BF16, pkv.PKV_DTYPE_F16_KV_FP8, pkv.PKV_DTYPE_BF16_KV_FP8):
+        assert call(dtype=dt) == pkv.PKV_ERR_INVALID_ARG     # supported, null pointers
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        assert call(ks=ks, vs=vs) == pkv.PKV_ERR_INVALID_ARG   # scales finite and > 0
     assert call(B=-1) == pkv.PKV_ERR_INVALID_ARG
     assert call(scale=float("nan")) == pkv.PKV_ERR_INVALID_ARG
     assert call(B=0) == pkv.PKV_OK                           # nothing to do
@@ -274,8 +278,8 @@ def test_device_plan_workspace_size_and_host_checks():
 
     def call(mode, param, max_splits, B=2, maxp=1024):
         return lib.pkv_decode_device_plan(None, None, None, 0, None, maxp, None, B, 32, 8, 128, 16,
-                                          pkv.PKV_DTYPE_F16, 0.1, mode, param, max_splits, None,
-                                          256, None, None, None, 0, None)
+                                          pkv.PKV_DTYPE_F16, 0.1, 1.0, 1.0, mode, param,
+                                          max_splits, None, 256, None, None, None, 0, None)
     assert call(-1, 0, 8, B=0) == pkv.PKV_OK                   # nothing to do
     assert call(2, 1, 8) == pkv.PKV_ERR_INVALID_ARG            # unknown mode
     assert call(-1, 0, 0) == pkv.PKV_ERR_INVALID_ARG           # no capacity

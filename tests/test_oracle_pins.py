@@ -188,3 +188,89 @@ def test_policy_structure():
     m, p = oracle.policy([100, 0], 8, 16, 256)
     T, _, _, _ = oracle.plan_shape([100, 0], 8, 16, m, p)
     assert 8 <= T <= 8 * 7
+
+
+# --------------------------------------------------------------------------- fp8 KV values
+
+def test_e4m3_decode_spec_values():
+    """Values the OCP 8-bit Floating Point Specification (OFP8) states for
+    E4M3: largest normal 448 (S.1111.110), smallest normal 2^-6 (S.0001.000),
+    largest subnormal 0.875 * 2^-6 (S.0000.111), smallest subnormal 2^-9
+    (S.0000.001), zeros of both signs, NaN at S.1111.111 and no infinity."""
+    d = oracle.e4m3_decode
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x08) == 2.0 ** -6
+    assert d(0x07) == 0.875 * 2.0 ** -6
+    assert d(0x01) == 2.0 ** -9
+    assert d(0x00) == 0.0 and not math.copysign(1.0, d(0x00)) < 0
+    assert d(0x80) == 0.0 and math.copysign(1.0, d(0x80)) < 0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+    assert d(0x38) == 1.0 and d(0xC0) == -2.0 and d(0x3C) == 1.5
+    vals = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert not np.isinf(vals).any()
+    assert np.isnan(vals).sum() == 2
+
+
+def test_e4m3_decode_matches_torch():
+    """Library special case: torch's float8_e4m3fn holds the same format."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_e4m3_decode_monotone_and_symmetric():
+    """Positive codes 0x00..0x7E increase strictly; the sign bit negates."""
+    pos = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    neg = oracle.e4m3_decode(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(neg[1:], -pos[1:])
+
+
+def test_attend_k_scale_is_a_softmax_scale():
+    """Scaling K by c is scaling the scores by c: attend(k_scale=c) equals
+    attend with softmax scale * c (an invariance, to float64 rounding)."""
+    rng = np.random.default_rng(5)
+    c = pins.rand_case(rng, B=2, Hq=4, Hkv=2, D=8, page_size=4, lens=[7, 30])
+    args = (c["q"], c["k_pool"], c["v_pool"], c["block_table"], c["seq_lens"])
+    for ks in (0.25, 3.0):
+        o1, l1 = oracle.attend(*args, c["scale"], page_size=4, k_scale=ks)
+        o2, l2 = oracle.attend(*args, c["scale"] * ks, page_size=4)
+        assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12
+
+
+def test_attend_v_scale_scales_the_output_only():
+    """out is linear in V and lse does not depend on V."""
+    rng = np.random.default_rng(6)
+    c = pins.rand_case(rng, B=2, Hq=4, Hkv=1, D=8, page_size=4, lens=[0, 13])
+    args = (c["q"], c["k_pool"], c["v_pool"], c["block_table"], c["seq_lens"], c["scale"])
+    o1, l1 = oracle.attend(*args, page_size=4)
+    o2, l2 = oracle.attend(*args, page_size=4, v_scale=2.5)
+    assert np.max(np.abs(o2 - 2.5 * o1)) < 1e-12
+    assert np.array_equal(np.isneginf(l1), np.isneginf(l2))
+    fin = ~np.isneginf(l1)
+    assert np.max(np.abs(l1[fin] - l2[fin])) < 1e-15
+
+
+def test_attend_on_codes_is_attend_on_their_values():
+    """A uint8 pool is read as E4M3 codes: the result equals attention over
+    the codes' values times the scales."""
+    rng = np.random.default_rng(7)
+    c = pins.rand_case(rng, B=2, Hq=4, Hkv=2, D=8, page_size=4, lens=[5, 18])
+    codes_k = rng.integers(0, 256, size=c["k_pool"].shape).astype(np.uint8)
+    codes_v = rng.integers(0, 256, size=c["v_pool"].shape).astype(np.uint8)
+    # keep the referenced tokens finite: NaN codes only where the rows never read
+    nan_k = (codes_k & 0x7F) == 0x7F
+    nan_v = (codes_v & 0x7F) == 0x7F
+    codes_k[nan_k] = 0x38
+    codes_v[nan_v] = 0x38
+    vals_k = oracle.e4m3_decode(codes_k)
+    vals_v = oracle.e4m3_decode(codes_v)
+    args = (c["block_table"], c["seq_lens"], c["scale"])
+    o1, l1 = oracle.attend(c["q"], codes_k, codes_v, *args, page_size=4, k_scale=0.5,
+                           v_scale=2.0)
+    o2, l2 = oracle.attend(c["q"], vals_k * 0.5, vals_v * 2.0, *args, page_size=4)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -167,8 +167,10 @@ class Workload:
 
     @property
     def kv_bytes(self) -> int:
-        """Bytes of K and V the batch attends over (fp16): sum_b N_b*Hkv*D*2*2."""
-        return int(self.seq_lens_np.astype(np.int64).sum()) * self.cfg.Hkv * self.cfg.D * 4
+        """Bytes of K and V the batch attends over: sum_b N_b*Hkv*D*2*e, with e
+        the bytes of one pool element (2 for fp16 / bf16, 1 for fp8)."""
+        e = self.k_pool.element_size() if hasattr(self.k_pool, "element_size") else 2
+        return int(self.seq_lens_np.astype(np.int64).sum()) * self.cfg.Hkv * self.cfg.D * 2 * e
 
 
 def make_lengths(cfg: Config, seed: int) -> np.ndarray:
@@ -200,8 +202,11 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
     """Draw one batch.  ``seq_lens`` overrides the config's length draw (edge cases).
 
     fill: what unreferenced pool pages and tail slots hold: "nan", "random" or "zero".
-    dtype: "f16", or "bf16" (device workloads only): the same float32 draws
-    rounded to bfloat16 instead of fp16.
+    dtype: "f16", or (device workloads only) "bf16": the same float32 draws
+    rounded to bfloat16 instead of fp16; "fp8": q fp16 and K / V pools of fp8
+    E4M3 codes (torch.float8_e4m3fn), the float32 draws rounded to E4M3;
+    "bf16_fp8": the same with q in bfloat16.  Poison fills of fp8 pools use
+    the NaN code 0x7F.
     """
     import torch
 
@@ -217,10 +222,10 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
         np.zeros(0, dtype=np.int32)
     pshape = (pool, cfg.Hkv, P, cfg.D)
 
-    if dtype not in ("f16", "bf16"):
+    if dtype not in ("f16", "bf16", "fp8", "bf16_fp8"):
         raise ValueError(dtype)
     if device == "cpu" and dtype != "f16":
-        raise ValueError("bf16 workloads are drawn on the device only")
+        raise ValueError("bf16 and fp8 workloads are drawn on the device only")
     if device == "cpu":
         fill_rng = np.random.default_rng([seed, 1])
         q = rng.standard_normal((len(lens), cfg.Hq, cfg.D), dtype=np.float32).astype(np.float16)
@@ -251,53 +256,65 @@ def make_workload(name_or_cfg, seed: int, device: str = "cpu", fill: str = "nan"
         gen.manual_seed(seed)
         fill_gen = torch.Generator(device=dev)
         fill_gen.manual_seed(seed + 7919)
-        edt = torch.float16 if dtype == "f16" else torch.bfloat16
+        edt = torch.bfloat16 if dtype in ("bf16", "bf16_fp8") else torch.float16
+        fp8 = dtype in ("fp8", "bf16_fp8")
+        # pools of fp8 codes are built as uint8 (fills, copies) and viewed as
+        # float8_e4m3fn at the end; the draws are rounded by torch's conversion
+        pdt = torch.uint8 if fp8 else edt
+
+        def to_pool(x):
+            return x.to(torch.float8_e4m3fn).view(torch.uint8) if fp8 else x.to(edt)
+
         q_t = torch.randn((len(lens), cfg.Hq, cfg.D), generator=gen, device=dev,
                           dtype=torch.float32).to(edt)
         used_t = torch.from_numpy(used.astype(np.int64)).to(dev)
         pools = []
+        nan_val = 0x7F if fp8 else float("nan")
         for _ in range(2):
             if fill == "nan":
-                arr = torch.full(pshape, float("nan"), dtype=edt, device=dev)
+                arr = torch.full(pshape, nan_val, dtype=pdt, device=dev)
             elif fill == "zero":
-                arr = torch.zeros(pshape, dtype=edt, device=dev)
+                arr = torch.zeros(pshape, dtype=pdt, device=dev)
             elif fill == "random":
-                arr = torch.empty(pshape, dtype=edt, device=dev)
-                _randn_fill(arr, fill_gen)
+                arr = torch.empty(pshape, dtype=pdt, device=dev)
+                _randn_fill(arr, fill_gen, to_pool)
             else:
                 raise ValueError(fill)
             # referenced pages, generated in chunks to bound the fp32 temporary
             chunk = max(1, (1 << 28) // (cfg.Hkv * P * cfg.D))
             for i in range(0, len(used), chunk):
                 idx = used_t[i:i + chunk]
-                vals = torch.randn((idx.numel(), cfg.Hkv, P, cfg.D), generator=gen,
-                                   device=dev, dtype=torch.float32).to(edt)
+                vals = to_pool(torch.randn((idx.numel(), cfg.Hkv, P, cfg.D), generator=gen,
+                                           device=dev, dtype=torch.float32))
                 arr.index_copy_(0, idx, vals)
                 del vals
             pools.append(arr)
         k_t, v_t = pools
         if fill != "random":
-            tail_val = float("nan") if fill == "nan" else 0.0
+            tail_val = nan_val if fill == "nan" else 0
             for b, n in enumerate(lens):
                 r = int(n) % P
                 if n > 0 and r:
                     last = int(bt[b, (int(n) - 1) // P])
                     k_t[last, :, r:, :] = tail_val
                     v_t[last, :, r:, :] = tail_val
+        if fp8:
+            k_t = k_t.view(torch.float8_e4m3fn)
+            v_t = v_t.view(torch.float8_e4m3fn)
         bt_t = torch.from_numpy(bt.copy()).to(dev)
         sl_t = torch.from_numpy(lens.copy()).to(dev)
     return Workload(cfg=cfg, seed=seed, seq_lens_np=lens, block_table_np=bt, q=q_t,
                     k_pool=k_t, v_pool=v_t, block_table=bt_t, seq_lens=sl_t)
 
 
-def _randn_fill(arr, gen):
+def _randn_fill(arr, gen, convert=None):
     import torch
     flat = arr.view(-1)
     step = 1 << 28
     for i in range(0, flat.numel(), step):
         n = min(step, flat.numel() - i)
-        flat[i:i + n] = torch.randn(n, generator=gen, device=arr.device,
-                                    dtype=torch.float32).to(arr.dtype)
+        x = torch.randn(n, generator=gen, device=arr.device, dtype=torch.float32)
+        flat[i:i + n] = convert(x) if convert is not None else x.to(arr.dtype)
 
 
 def _poison_tails(k, v, bt, lens, P, fill, rng):
@@ -358,6 +375,8 @@ def compact_rows(q, k_pool, v_pool, block_table, seq_lens, rows, page_size=PAGE_
         if isinstance(pool, np.ndarray):
             return pool[uniq]
         idx = torch.from_numpy(uniq.astype(np.int64)).to(pool.device)
+        if pool.dtype == torch.float8_e4m3fn:   # E4M3 codes, decoded by the reader
+            return pool.view(torch.uint8).index_select(0, idx).cpu().numpy()
         sel = pool.index_select(0, idx)
         if sel.dtype == torch.bfloat16:       # numpy has no bfloat16: widen exactly
             sel = sel.float()
