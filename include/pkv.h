@@ -31,7 +31,7 @@
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued asynchronously and never synchronised.
  *   - Supported shapes: page_size = 16, head_dim in {64, 128, 256},
- *     G = Hq/Hkv in {1, 2, 4, 8} (at most 4 at head_dim 256).  Others return
+ *     G = Hq/Hkv in {1, 2, 4, 8, 16}.  Others return
  *     PKV_ERR_UNSUPPORTED.
  *   - Data types: q and out are fp16 or bf16; the K and V pools are the same
  *     type or fp8 E4M3 with per-tensor dequantisation scales (pkv_dtype).

@@ -146,7 +146,7 @@ __device__ __forceinline__ vecE<E, 8> fp8x8(uint2x w) {
 constexpr int kPage = 16;
 constexpr int kWaves = 4;             // waves per workgroup (one task at a time)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxG = 8;
+constexpr int kMaxG = 16;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct DecodeArgs {
@@ -400,12 +400,14 @@ struct MergeArgs {
 //   out = sum_s w_s o_s / sum_s w_s l_s,  lse = (M + log2 sum_s w_s l_s) ln 2.
 // One workgroup merges the G heads of one (row, KV head), whose partial
 // outputs are contiguous (G*D floats per slot), over slots o0 .. o0+S-1.
-// Thread t owns float4 column t % C of the group (C = G*D/4) and the slots
-// r, r+R, r+2R, ... with r = t / C and R = 256 / C.  It folds its slots into
-// a running (max, sum, vector) state kB slots at a time, so kB loads per
-// thread are in flight together; the R states of a column are then combined
-// in LDS.  The result is the same maximum and the same sums as the two-pass
-// form, up to the order of the additions.
+// A float4 column of the group (C = G*D/4 of them) folds slots r, r+R,
+// r+2R, ... into a running (max, sum, vector) state kB slots at a time, so
+// kB loads per thread are in flight together (fold_column).  With C <= 256,
+// thread t owns column t % C and r = t / C, R = 256 / C, and the R states of
+// a column are combined in LDS.  A wider group (G * D > 1024) takes
+// ceil(C / 256) passes of one column per thread over all the slots (R = 1).
+// The result is the same maximum and the same sums as the two-pass form, up
+// to the order of the additions.
 // Slots in flight per thread in the merge.  Every merge (fused or not) uses
 // the same value, so both forms add the states in the same order.
 constexpr int kMergeBatch = 8;
@@ -415,62 +417,92 @@ constexpr int merge_lds_floats() {
   return kThreads * 6;
 }
 
+template <int D, int kB>
+__device__ __forceinline__ void fold_column(__amdgpu_buffer_rsrc_t ml_rsrc,
+                                            __amdgpu_buffer_rsrc_t o_rsrc, int Hq, int ml_off,
+                                            int o_off, int r, int R, int S, float& M, float& L,
+                                            floatx4& O) {
+  M = -INFINITY;
+  L = 0.f;
+  O = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int base = r; base < S; base += R * kB) {
+    float2 ml[kB];
+    floatx4 o[kB];
+    // Slot indices are clamped so every load is unconditional; clamped
+    // slots get weight 0 below.
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int sl = min(base + R * k, S - 1);
+      ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+          ml_rsrc, 8 * sl * Hq + ml_off, 0, kCoherent));
+      o[k] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+          o_rsrc, 4 * sl * Hq * D + o_off, 0, kCoherent));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all 2*kB loads issue before the first wait
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (base + R * k < S) Mn = fmaxf(Mn, ml[k].x);
+    const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    O *= f;
+    L *= f;
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const bool live = base + R * k < S && ml[k].x != -INFINITY;
+      const float w = live ? fast_exp2(ml[k].x - Mn) : 0.f;
+      O += w * o[k];
+      L += w * ml[k].y;
+    }
+    M = Mn;
+  }
+}
+
 template <int D, int kB, class E>
 __device__ void merge_group(const MergeArgs& a, int b, int g, int o0, int S, float* lds) {
   const int tid = threadIdx.x;
   const int G = a.G;
-  const int cols = G * (D / 4);          // <= kThreads, since G <= kMaxG
-  const int R = kThreads / cols;
-  const int r = tid / cols;
-  const int c = tid - r * cols;
-  const int h = (4 * c) / D;
+  const int cols = G * (D / 4);
   const int64_t head0 = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G;
-  float* s_M = lds;
-  float* s_L = lds + kThreads;
-  floatx4* s_O = reinterpret_cast<floatx4*>(lds + 2 * kThreads);
-
   // Coherent (L2-bypassing) loads: the states may come from other XCDs.
   const __amdgpu_buffer_rsrc_t ml_rsrc = make_rsrc(
       a.part_ml + static_cast<int64_t>(o0) * a.Hq, static_cast<uint32_t>(S) * a.Hq * 8u);
   const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
       a.part_o + static_cast<int64_t>(o0) * a.Hq * D, static_cast<uint32_t>(S) * a.Hq * D * 4u);
-  const int ml_off = 8 * (g * G + h);
-  const int o_off = 4 * (g * G * D + 4 * c);
+  auto write = [&](int c, float Mt, float Lt, floatx4 Ot) {
+    const int h = (4 * c) / D;
+    const float inv = 1.f / Lt;
+    E* dst = static_cast<E*>(a.out) + head0 * D + 4 * c;
+    dst[0] = static_cast<E>(Ot[0] * inv);
+    dst[1] = static_cast<E>(Ot[1] * inv);
+    dst[2] = static_cast<E>(Ot[2] * inv);
+    dst[3] = static_cast<E>(Ot[3] * inv);
+    if ((4 * c) % D == 0 && a.lse) a.lse[head0 + h] = (Mt + __log2f(Lt)) * kLn2;
+  };
 
+  if (cols > kThreads) {
+    for (int c = tid; c < cols; c += kThreads) {
+      const int h = (4 * c) / D;
+      float M, L;
+      floatx4 O;
+      fold_column<D, kB>(ml_rsrc, o_rsrc, a.Hq, 8 * (g * G + h), 4 * (g * G * D + 4 * c), 0, 1,
+                         S, M, L, O);
+      write(c, M, L, O);
+    }
+    return;
+  }
+
+  const int R = kThreads / cols;
+  const int r = tid / cols;
+  const int c = tid - r * cols;
+  const int h = (4 * c) / D;
+  float* s_M = lds;
+  float* s_L = lds + kThreads;
+  floatx4* s_O = reinterpret_cast<floatx4*>(lds + 2 * kThreads);
   float M = -INFINITY, L = 0.f;
   floatx4 O = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (r < R) {
-    for (int base = r; base < S; base += R * kB) {
-      float2 ml[kB];
-      floatx4 o[kB];
-      // Slot indices are clamped so every load is unconditional; clamped
-      // slots get weight 0 below.
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const int sl = min(base + R * k, S - 1);
-        ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-            ml_rsrc, 8 * sl * a.Hq + ml_off, 0, kCoherent));
-        o[k] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-            o_rsrc, 4 * sl * a.Hq * D + o_off, 0, kCoherent));
-      }
-      __builtin_amdgcn_sched_barrier(0);   // all 2*kB loads issue before the first wait
-      float Mn = M;
-#pragma unroll
-      for (int k = 0; k < kB; ++k)
-        if (base + R * k < S) Mn = fmaxf(Mn, ml[k].x);
-      const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
-      O *= f;
-      L *= f;
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const bool live = base + R * k < S && ml[k].x != -INFINITY;
-        const float w = live ? fast_exp2(ml[k].x - Mn) : 0.f;
-        O += w * o[k];
-        L += w * ml[k].y;
-      }
-      M = Mn;
-    }
-  }
+  if (r < R)
+    fold_column<D, kB>(ml_rsrc, o_rsrc, a.Hq, 8 * (g * G + h), 4 * (g * G * D + 4 * c), r, R, S,
+                       M, L, O);
   s_M[tid] = M;
   s_L[tid] = L;
   s_O[tid] = O;
@@ -487,13 +519,7 @@ __device__ void merge_group(const MergeArgs& a, int b, int g, int o0, int S, flo
       Lt += w * s_L[tid + j * cols];
       Ot += w * s_O[tid + j * cols];
     }
-    const float inv = 1.f / Lt;
-    E* dst = static_cast<E*>(a.out) + head0 * D + 4 * c;
-    dst[0] = static_cast<E>(Ot[0] * inv);
-    dst[1] = static_cast<E>(Ot[1] * inv);
-    dst[2] = static_cast<E>(Ot[2] * inv);
-    dst[3] = static_cast<E>(Ot[3] * inv);
-    if ((4 * c) % D == 0 && a.lse) a.lse[head0 + h] = (Mt + __log2f(Lt)) * kLn2;
+    write(tid, Mt, Lt, Ot);
   }
 }
 
@@ -520,12 +546,6 @@ constexpr int ring_depth() {
   return D == 256 ? 2 : 4;
 }
 
-// Largest GQA group a head dimension supports: the merge gives one float4
-// column of the group to each of its 256 threads (G * D / 4 <= 256).
-template <int D>
-constexpr int max_group() {
-  return D == 256 ? 4 : kMaxG;
-}
 // Split tasks of a workgroup whose arrival is deferred: they are counted in
 // together when the workgroup runs out of tasks or holds kMaxDone of them.
 constexpr int kMaxDone = 64;
@@ -690,7 +710,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   constexpr int kKvb = kv_bytes<KV>();
   constexpr uint32_t kTileBytes = static_cast<uint32_t>(kPage * D * kKvb);
   constexpr int kRing = ring_depth<D>();
-  constexpr int kGroup = max_group<D>();
+  constexpr int kGroup = kMaxG;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -704,7 +724,9 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ vecE<E, 8> s_q[2][KK * 64];            // q operand of a task, per lane
   __shared__ float s_m[2][kWaves][16];
   __shared__ float s_l[2][kWaves][16];
-  __shared__ __attribute__((aligned(16))) float s_o[2][kWaves][kGroup][LDS_STRIDE];
+  // The waves' accumulators, single-buffered (room for G = 16 heads): a
+  // barrier after the combine keeps the next task's writes behind its reads.
+  __shared__ __attribute__((aligned(16))) float s_o[kWaves][kGroup][LDS_STRIDE];
   __shared__ int4 s_done[kMaxDone];   // (row, KV head, first slot, splits)
   __shared__ int s_lastf[kMaxDone];
   static_assert(kWaves * kGroup * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
@@ -869,7 +891,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < VW; ++e) s_o[par][wave][col][VW * (4 * grp + j) + e] = st.acc[e][j];
+        for (int e = 0; e < VW; ++e) s_o[wave][col][VW * (4 * grp + j) + e] = st.acc[e][j];
     }
     __syncthreads();
 
@@ -888,7 +910,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
           const float mw = s_m[par][w][h];
           const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
           L += wt * s_l[par][w][h];
-          O += wt * s_o[par][w][h][d];
+          O += wt * s_o[w][h][d];
         }
         O *= a.v_scale;   // V's dequantisation scale (exact for 1)
         const int64_t hq = static_cast<int64_t>(cur.g) * G + h;
@@ -918,16 +940,17 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
         // behind it.
         if (tid == 0) s_done[n_done] = int4{cur.b, cur.g, cur.o0, cur.Sb};
         if (++n_done == kMaxDone) {
-          flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[par][0][0][0]);
+          flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0]);
           n_done = 0;
         }
       }
     }
+    __syncthreads();   // every read of s_o above precedes the next task's writes
     t_nxt = __builtin_amdgcn_readfirstlane(s_next[par]);
     cur = nxt;
   }
 
-  if (n_done > 0) flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0][0]);
+  if (n_done > 0) flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0]);
 
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
@@ -1318,9 +1341,8 @@ int prepare(const void* q, const void* k_pool, const void* v_pool, int64_t num_p
   if (page_size != pkv::kPage || (head_dim != 64 && head_dim != 128 && head_dim != 256) ||
       Hq % Hkv != 0 || dtype < PKV_DTYPE_F16 || dtype > PKV_DTYPE_BF16_KV_FP8)
     return PKV_ERR_UNSUPPORTED;
-  const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
-  if (head_dim == 256 && G > 4) return PKV_ERR_UNSUPPORTED;   // merge: G * d / 4 <= 256
+  const int G = Hq / Hkv;   // one MFMA column per query head of the group
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * Hq > INT32_MAX) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (!split_offsets || !out || !workspace) return PKV_ERR_INVALID_ARG;

@@ -246,11 +246,13 @@ def test_decode_rejects_bad_scalars_before_touching_the_device():
         return lib.pkv_decode(None, None, None, 0, None, 1, None, None, 0, None, 0, B, Hq, Hkv, D,
                               P, dtype, scale, ks, vs, None, None, None, 0, None)
     assert call(D=96) == pkv.PKV_ERR_UNSUPPORTED
-    assert call(D=256, Hq=8, Hkv=1) == pkv.PKV_ERR_UNSUPPORTED    # G = 8 at d = 256
+    assert call(D=256, Hq=16, Hkv=1) == pkv.PKV_ERR_INVALID_ARG   # G = 16 at d = 256; null pointers
     assert call(D=256, Hq=4, Hkv=1) == pkv.PKV_ERR_INVALID_ARG    # supported; null pointers
+    assert call(Hq=32, Hkv=1) == pkv.PKV_ERR_UNSUPPORTED     # G = 32
     assert call(P=32) == pkv.PKV_ERR_UNSUPPORTED
     assert call(Hq=6, Hkv=4) == pkv.PKV_ERR_UNSUPPORTED      # Hq % Hkv
-    assert call(Hq=48, Hkv=3) == pkv.PKV_ERR_UNSUPPORTED     # G = 16
+    assert call(Hq=48, Hkv=3) == pkv.PKV_ERR_INVALID_ARG     # G = 16, supported; null pointers
+    assert call(Hq=36, Hkv=3) == pkv.PKV_ERR_UNSUPPORTED     # G = 12
     assert call(dtype=4) == pkv.PKV_ERR_UNSUPPORTED          # no such element type
     assert call(dtype=-1) == pkv.PKV_ERR_UNSUPPORTED
     for dt in (pkv.PKV_DTYPE_BF16, pkv.PKV_DTYPE_F16_KV_FP8, pkv.PKV_DTYPE_BF16_KV_FP8):

@@ -68,7 +68,7 @@ def test_bf16_workloads(name, mode, param, two_launch):
     _parity(wl, mode, param, two_launch)
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("D", [64, 128])
 def test_bf16_ragged_gqa_ratios_and_head_dims(G, D):
     cfg = Config("small_bf16", B=0, Hq=G * 2, Hkv=2, D=D, max_pages_per_row=8, pool_pages=64,
@@ -124,7 +124,7 @@ def test_mixed_element_types_rejected():
                        wl.seq_lens_np, cfg.scale, torch.empty_like(wl.q))
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_bf16_head_dim_256(G):
     cfg = Config("small_bf16_d256", B=0, Hq=G * 2, Hkv=2, D=256, max_pages_per_row=8,
                  pool_pages=64, lengths=lambda rng: np.zeros(0))

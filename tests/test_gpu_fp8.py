@@ -61,7 +61,7 @@ def test_fp8_workloads(name, mode, param, two_launch):
     _parity(wl, mode, param, two_launch)
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("D", [64, 128])
 def test_fp8_ragged_gqa_ratios_and_head_dims(G, D):
     cfg = Config("small_fp8", B=0, Hq=G * 2, Hkv=2, D=D, max_pages_per_row=8, pool_pages=64,
@@ -72,7 +72,7 @@ def test_fp8_ragged_gqa_ratios_and_head_dims(G, D):
         _parity(wl, mode, param)
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_fp8_head_dim_256(G):
     cfg = Config("small_fp8_d256", B=0, Hq=G * 2, Hkv=2, D=256, max_pages_per_row=8,
                  pool_pages=64, lengths=lambda rng: np.zeros(0))

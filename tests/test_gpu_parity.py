@@ -94,7 +94,7 @@ def _small_cfg(G=4, D=128, Hkv=2, maxp=8, pool=64):
 
 
 @pytest.mark.parametrize("two_launch", TWO)
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("D", [64, 128])
 def test_ragged_gqa_ratios_and_head_dims(G, D, two_launch):
     cfg = _small_cfg(G=G, D=D)
@@ -222,7 +222,7 @@ def test_task_list_readback_bit_exact():
 # --------------------------------------------------------------------------- head_dim 256
 
 @pytest.mark.parametrize("two_launch", TWO)
-@pytest.mark.parametrize("G", [1, 2, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 def test_head_dim_256_ragged(G, two_launch):
     """d = 256 runs with a 2-deep page ring and one workgroup per CU."""
     cfg = _small_cfg(G=G, D=256)
@@ -238,6 +238,17 @@ def test_head_dim_256_long_bimodal():
     wl = make_workload(cfg, SEED, device="cuda")
     for mode, param in [(None, None), (1, 64), (0, 32)]:
         _parity(wl, mode, param, two_launch=None)
+
+
+@pytest.mark.parametrize("D,Hkv", [(128, 4), (256, 2), (64, 8)])
+def test_gqa_16_long_bimodal(D, Hkv):
+    """G = 16: every MFMA column is a live head, and at G * d > 1024 the merge
+    takes several column passes (d = 128 and 256)."""
+    cfg = Config(f"g16_d{D}", B=8, Hq=16 * Hkv, Hkv=Hkv, D=D, max_pages_per_row=1024,
+                 pool_pages=2 * 8 * 1024, lengths=CONFIGS["b8_bimodal"].lengths)
+    wl = make_workload(cfg, SEED, device="cuda")
+    for mode, param, two in [(None, None, None), (1, 64, False), (1, 64, True), (0, 32, True)]:
+        _parity(wl, mode, param, two_launch=two)
 
 
 # --------------------------------------------------------------------------- large batches
