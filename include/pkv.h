@@ -476,10 +476,12 @@ typedef struct pkv_step_args {
   void* workspace;               /* as for pkv_decode */
   size_t workspace_bytes;
   void* stream;                  /* hipStream_t */
-  void* event_before_decode;     /* optional hipEvent_t, recorded on `stream`
-                                    just before the decode kernel */
-  void* event_after_decode;      /* optional hipEvent_t, recorded just after it
-                                    (before the merge kernel in two-launch form) */
+  void* event_before_decode;     /* optional hipEvent_t pair (created by the caller)
+                                    that takes the decode kernel's own start ... */
+  void* event_after_decode;      /* ... and end timestamps (hipExtLaunchKernel); in
+                                    the two-launch form the merge kernel comes after
+                                    the end.  A step without tasks records both where
+                                    the kernel would have run. */
   /* outputs */
   int32_t chosen_mode;
   int32_t chosen_param;

@@ -39,6 +39,7 @@
 // nearest even.  Tokens past the row's length are masked with selects, never
 // multiplies, so NaN in unused page slots cannot leak.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -1241,17 +1242,37 @@ int num_cus_of_current_device(int* cus) {
   return PKV_OK;
 }
 
+// ev0 / ev1 (optional): events that take the decode kernel's own start and
+// end timestamps (hipExtLaunchKernel), for timing it without the queue time
+// of separately recorded events.
 template <int D, class E, class KV>
 int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
-           bool decode) {
+           bool decode, hipEvent_t ev0, hipEvent_t ev1) {
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
-    if (da.B <= kRowStage)
+    const bool staged = da.B <= kRowStage;
+    if (ev0 || ev1) {
+      if (staged)
+        hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV>), dim3(grid), dim3(kThreads), 0,
+                              stream, ev0, ev1, 0, da, tasks, da.block_table, da.seq_lens,
+                              da.split_offsets);
+      else
+        hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV>), dim3(grid), dim3(kThreads),
+                              0, stream, ev0, ev1, 0, da, tasks, da.block_table, da.seq_lens,
+                              da.split_offsets);
+    } else if (staged) {
       hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV>), dim3(grid), dim3(kThreads), 0,
                          stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
-    else
+    } else {
       hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV>), dim3(grid), dim3(kThreads), 0,
                          stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
+    }
+  } else {
+    // no decode kernel (no tasks): the events still mark this point of the stream
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PKV_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return PKV_ERR_HIP;
+  }
+  if (decode) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       set_hip_error(static_cast<int>(e));
@@ -1272,25 +1293,26 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
 
 template <class E, class KV>
 int launch_d(int head_dim, const DecodeArgs& da, const MergeArgs& ma, int grid,
-             hipStream_t stream, bool decode) {
-  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode);
-  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode)
-                         : launch<64, E, KV>(da, ma, grid, stream, decode);
+             hipStream_t stream, bool decode, hipEvent_t ev0, hipEvent_t ev1) {
+  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode, ev0, ev1);
+  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode, ev0, ev1)
+                         : launch<64, E, KV>(da, ma, grid, stream, decode, ev0, ev1);
 }
 
 // The kernels of one head dimension and element-type pair (both checked by
 // the caller).
 int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& ma, int grid,
-               hipStream_t stream, bool decode) {
+               hipStream_t stream, bool decode, hipEvent_t ev0 = nullptr,
+               hipEvent_t ev1 = nullptr) {
   switch (dtype) {
     case PKV_DTYPE_BF16:
-      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode);
+      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
     case PKV_DTYPE_F16_KV_FP8:
-      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode);
+      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
     case PKV_DTYPE_BF16_KV_FP8:
-      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode);
+      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
     default:
-      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode);
+      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
   }
 }
 
@@ -1411,7 +1433,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
         int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
         int32_t page_size, int32_t dtype, float scale, float k_scale, float v_scale, void* out,
         float* lse, void* workspace, size_t workspace_bytes, void* stream, bool do_decode,
-        bool do_merge, bool fused) {
+        bool do_merge, bool fused, void* ev0 = nullptr, void* ev1 = nullptr) {
   pkv::DecodeArgs da{};
   pkv::MergeArgs ma{};
   int st = prepare(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
@@ -1443,10 +1465,28 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool decode = da.num_tasks > 0;
   da.task_cap = da.num_tasks > 0 ? da.num_tasks : 1;
-  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode);
+  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode, static_cast<hipEvent_t>(ev0),
+                         static_cast<hipEvent_t>(ev1));
 }
 
 }  // namespace
+
+extern "C++" {   // internal, C++ linkage, inside the extern "C" block
+namespace pkv {
+int decode_timed(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
+                 const int32_t* block_table, int32_t max_pages_per_row, const int32_t* seq_lens,
+                 const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,
+                 int64_t num_partial_slots, int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                 int32_t page_size, int32_t dtype, float scale, float k_scale, float v_scale,
+                 void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                 bool fused, void* ev0, void* ev1) {
+  return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
+             num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
+             scale, k_scale, v_scale, out, lse, workspace, workspace_bytes, stream, true, fused,
+             fused, ev0, ev1);
+}
+}  // namespace pkv
+}
 
 int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
                const int32_t* block_table, int32_t max_pages_per_row,

@@ -314,34 +314,15 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
     }
   }
 
-  // the decode kernel (merge fused in), or decode then merge kernel
-  if (a->event_before_decode) {
-    e = hipEventRecord(static_cast<hipEvent_t>(a->event_before_decode), stream);
-    if (e != hipSuccess) {
-      pkv::set_hip_error(static_cast<int>(e));
-      return PKV_ERR_HIP;
-    }
-  }
-  if (two) {
-    st = pkv_decode_splits(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
-                           a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B,
-                           a->Hq, a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale,
-                           a->k_scale, a->v_scale, a->out, a->lse, a->workspace,
-                           a->workspace_bytes, a->stream);
-  } else {
-    st = pkv_decode(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
-                    a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B, a->Hq,
-                    a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale, a->k_scale,
-                    a->v_scale, a->out, a->lse, a->workspace, a->workspace_bytes, a->stream);
-  }
+  // the decode kernel (merge fused in), or decode then merge kernel; the
+  // events, if any, take the decode kernel's own start and end timestamps
+  st = pkv::decode_timed(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
+                         a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B,
+                         a->Hq, a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale,
+                         a->k_scale, a->v_scale, a->out, a->lse, a->workspace,
+                         a->workspace_bytes, a->stream, !two, a->event_before_decode,
+                         a->event_after_decode);
   if (st != PKV_OK) return st;
-  if (a->event_after_decode) {
-    e = hipEventRecord(static_cast<hipEvent_t>(a->event_after_decode), stream);
-    if (e != hipSuccess) {
-      pkv::set_hip_error(static_cast<int>(e));
-      return PKV_ERR_HIP;
-    }
-  }
   if (two)
     st = pkv_merge(offs_d, slots, a->B, a->Hq, a->Hkv, a->head_dim, a->dtype, a->out, a->lse,
                    a->workspace, a->workspace_bytes, a->stream);
