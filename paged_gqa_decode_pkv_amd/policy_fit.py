@@ -13,6 +13,8 @@ thresholds fixed on a calibration seed and then evaluated on held-out seeds
            its measured time, the best measured schedule, and the regret
            (picked / best); also the regret of a fixed reference rule
 
+``python -m paged_gqa_decode_pkv_amd.policy_fit --revalidate RUNS.jsonl`` judges the
+committed constants on fresh runs instead (``calibration/mi355x_revalidation.json``).
 ``python -m paged_gqa_decode_pkv_amd.policy_fit RUNS.jsonl`` writes
 ``calibration/mi355x_runs.json`` (the runs, compacted) and
 ``calibration/mi355x_fit.json`` (constants + evaluation) and prints the table.
@@ -115,27 +117,33 @@ def compact_runs(jsonl_path):
         key = r["config"]
         d = runs[key].setdefault(str(r["seed"]), {"lens": r["lens"], "runs": [], "rule": None})
         row = [r["mode"], r["param"], int(r["two_launch"]), r["num_tasks"], r["max_splits"],
-               r["gpu_us"], r["wall_us"]]
+               r["step_us"]]
         if r["requested"] is None:
             d["rule"] = row
         else:
             d["runs"].append(row)
     return {"device": "1x MI355X (gfx950), 256 CUs", "Hkv": 8, "head_dim": 128, "cus": 256,
-            "columns": ["mode", "param", "two_launch", "num_tasks", "max_splits", "gpu_us",
-                        "wall_us"],
+            "columns": ["mode", "param", "two_launch", "num_tasks", "max_splits", "step_us"],
             "command": "python -m paged_gqa_decode_pkv_amd.calibrate --out RUNS.jsonl",
             "traces": runs}
 
 
 def records(data):
+    """One record per measured candidate.  The time is the "step_us" column
+    (steady-state time per step), or "gpu_us" in runs taken before it existed
+    (HIP events from the decode kernel to the end of the step)."""
+    cols = data["columns"]
+    ti = cols.index("step_us") if "step_us" in cols else cols.index("gpu_us")
     out = []
     for cfg, seeds in data["traces"].items():
         for seed, d in seeds.items():
-            for mode, param, two, T, maxS, gpu, wall in d["runs"]:
+            for row in d["runs"]:
+                mode, param, two, T, maxS = row[:5]
+                step = row[ti]
                 Tf, P, pmax, mS = plan_features(d["lens"], data["Hkv"], mode, param)
                 assert (Tf, mS) == (T, maxS), (cfg, seed, mode, param)
                 out.append(dict(cfg=cfg, seed=int(seed), mode=mode, param=param, two=bool(two),
-                                T=T, P=P, pmax=pmax, maxS=maxS, gpu=gpu, wall=wall))
+                                T=T, P=P, pmax=pmax, maxS=maxS, step=step))
     return out
 
 
@@ -145,7 +153,7 @@ def fit(recs, cus, head_dim):
 
     def resid(x):
         return np.array([math.log(predict(x, r["T"], r["P"], r["pmax"], r["maxS"], r["two"],
-                                          cus, head_dim)) - math.log(r["gpu"]) for r in cal])
+                                          cus, head_dim)) - math.log(r["step"]) for r in cal])
     x0 = [10.0, 5.0, 0.5, 40.0, 6000.0, 5.0, 0.01, 0.3]
     lb = [0.0, 0.0, 0.0, 1.0, 500.0, 0.0, 0.0, 0.0]
     ub = [200.0, 100.0, 4.0, 1000.0, 20000.0, 100.0, 10.0, 20.0]
@@ -157,6 +165,8 @@ def fit(recs, cus, head_dim):
 
 def judge(x, data, recs):
     cus, head_dim, Hkv = data["cus"], data["head_dim"], data["Hkv"]
+    cols = data["columns"]
+    ti = cols.index("step_us") if "step_us" in cols else cols.index("gpu_us")
     by = defaultdict(dict)
     for r in recs:
         by[(r["cfg"], r["seed"])][(r["mode"], r["param"], r["two"])] = r
@@ -166,23 +176,60 @@ def judge(x, data, recs):
             runs = by[(cfg, int(seed))]
             mode, param, two = pick(x, d["lens"], Hkv, cus, head_dim)
             got = runs[(mode, param, two)]
-            best = min(runs.values(), key=lambda r: r["gpu"])
+            best = min(runs.values(), key=lambda r: r["step"])
             rule = d["rule"]
+            rule_t = rule[ti] if rule else None
             rows.append({
                 "trace": cfg, "seed": int(seed), "pick": [mode, param, int(two)],
-                "pick_us": got["gpu"], "best": [best["mode"], best["param"], int(best["two"])],
-                "best_us": best["gpu"], "regret": round(got["gpu"] / best["gpu"], 4),
+                "pick_us": got["step"], "best": [best["mode"], best["param"], int(best["two"])],
+                "best_us": best["step"], "regret": round(got["step"] / best["step"], 4),
                 "rule": rule[:3] if rule else None,
-                "rule_regret": round(rule[5] / best["gpu"], 4) if rule else None,
+                "rule_regret": round(rule_t / best["step"], 4) if rule else None,
             })
     return rows
+
+
+def revalidate(jsonl, out_name="mi355x_revalidation.json"):
+    """Judge the committed constants (no new fit) on fresh runs of calibrate.py,
+    e.g. after a kernel change: for every (trace, seed), the committed policy's
+    pick, its measured time and the regret against the best measured schedule;
+    the constants a fit on the fresh calibration seed would give, and theirs."""
+    data = compact_runs(jsonl)
+    recs = records(data)
+    committed = json.load(open(os.path.join(CAL_DIR, "mi355x_fit.json")))["params"]
+    x = [committed[k] for k in PARAM_NAMES]
+    rows = judge(x, data, recs)
+    refit, rms = fit(recs, data["cus"], data["head_dim"])
+    rows_refit = judge(refit, data, recs)
+    held = [r["regret"] for r in rows if r["seed"] != CALIBRATION_SEED]
+    held_refit = [r["regret"] for r in rows_refit if r["seed"] != CALIBRATION_SEED]
+    summary = {
+        "what": "committed constants judged on fresh runs (no refit); a refit shown beside them",
+        "params": committed,
+        "held_out_regret_mean": round(float(np.mean(held)), 4),
+        "held_out_regret_max": round(float(np.max(held)), 4),
+        "refit_params": dict(zip(PARAM_NAMES, refit)),
+        "refit_held_out_regret_mean": round(float(np.mean(held_refit)), 4),
+        "refit_held_out_regret_max": round(float(np.max(held_refit)), 4),
+        "runs": data,
+        "rows": rows,
+    }
+    with open(os.path.join(CAL_DIR, out_name), "w") as f:
+        json.dump(summary, f, separators=(",", ":"))
+    return summary
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("jsonl", nargs="?", help="output of calibrate.py")
     ap.add_argument("--runs", help="compacted runs (calibration/mi355x_runs.json)")
+    ap.add_argument("--revalidate", action="store_true",
+                    help="judge the committed constants on the runs in JSONL (no new fit)")
     args = ap.parse_args(argv)
+    if args.revalidate:
+        s = revalidate(args.jsonl)
+        print({k: v for k, v in s.items() if k not in ("rows", "runs")})
+        return 0
     if args.jsonl:
         data = compact_runs(args.jsonl)
         os.makedirs(CAL_DIR, exist_ok=True)
