@@ -251,7 +251,7 @@ def main():
                                  "mode": ["split", "workqueue"][mode], "param": param,
                                  "merge": "two-launch" if two_launch else "fused"}),
             "kernel": f"pkv_decode_kernel<{cfg.D}, {'true' if B <= 1024 else 'false'}, _Float16, "
-                      f"{'pkv::Fp8E4M3' if args.kv_dtype == 'fp8' else '_Float16'}>",
+                      f"{'pkv::Fp8E4M3' if args.kv_dtype == 'fp8' else '_Float16'}, false>",
             "event_timed_steps": len(events),
             "algorithmic_bytes_per_launch": kv_bytes,
             "extras_bytes_per_launch": extras,

@@ -45,6 +45,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pkv.h"
 #include "policy_model.h"
@@ -174,6 +175,16 @@ struct DecodeArgs {
   int32_t fuse;       // 1: the last split of a (row, KV head) merges it
   float* part_o;      // [slots][Hq][D]
   float2* part_ml;    // [slots][Hq] (max in log2 units, sum)
+  // Self-planned step (pkv_decode_device_plan, B <= kRowStage): every
+  // workgroup derives the plan from the staged lengths; workgroup 0 writes
+  // the header and the offsets, each task's record is written by the
+  // workgroup that runs it.
+  int32_t plan_mode, plan_param;   // mode < 0: the policy chooses
+  int32_t plan_num_cus, plan_head_dim, plan_groups_fit;
+  pkv_policy_params plan_pol;      // candidate sets limited to the capacity
+  int32_t* plan_out;               // header [kPlanHdrInts]; NULL: not self-planned
+  int32_t* plan_offs_out;          // [B + 1]
+  int4* plan_tasks_out;            // [tasks]
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -551,6 +562,145 @@ constexpr int ring_depth() {
 // together when the workgroup runs out of tasks or holds kMaxDone of them.
 constexpr int kMaxDone = 64;
 
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t B, Hkv, head_dim, page_size, num_cus;
+  int32_t max_pages;
+  int32_t mode, param;      // mode < 0: the policy chooses
+  int32_t groups_fit;       // B * Hkv fits the fused merge's arrival counters
+  pkv_policy_params pol;    // candidate sets already limited to the capacity
+  int32_t* hdr;             // [kPlanHdrInts]
+  int32_t* offs;            // [B + 1]
+  int4* tasks;              // capacity Hkv * B * max_splits
+  uint32_t* ctrl;
+};
+
+constexpr int kPlanHdrInts = 16;
+constexpr int kPlanStage = 4096;   // rows whose page counts the planner keeps in LDS
+constexpr int kCandBatch = 16;     // policy candidates evaluated together
+constexpr int kCandGroups = kThreads / kCandBatch;
+
+__device__ __forceinline__ uint32_t cdiv32(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+// Pages of row b, or -1 for a row to flag (N_b < 0 or more than max_pages
+// pages).  Read from global memory; the planner stages the first kPlanStage.
+__device__ __forceinline__ int32_t plan_row_pages_global(const PlanArgs& a, int b) {
+  const int32_t N = a.seq_lens[b];
+  if (N < 0) return -1;
+  const int64_t n = (static_cast<int64_t>(N) + a.page_size - 1) / a.page_size;
+  return n > a.max_pages ? -1 : static_cast<int32_t>(n);
+}
+
+// Add one row of n pages to the plan shape (mode, param): the arithmetic of
+// shape_add_row in 32 bits (n, c, S fit) with 64-bit sums.
+__device__ __forceinline__ void plan_shape_add(PlanShape& f, int32_t n, int32_t Hkv, int m,
+                                               uint32_t v) {
+  if (n <= 0) return;
+  const uint32_t un = static_cast<uint32_t>(n);
+  const uint32_t c = m == PKV_MODE_SPLIT ? cdiv32(un, v) : v;
+  const uint32_t S = cdiv32(un, c);
+  f.T += static_cast<int64_t>(Hkv) * S;
+  f.P += static_cast<int64_t>(Hkv) * un;
+  const int64_t largest = c < un ? c : un;
+  if (largest > f.pmax) f.pmax = largest;
+  if (static_cast<int64_t>(S) > f.maxS) f.maxS = S;
+}
+
+__device__ __forceinline__ int64_t wave_max64(int64_t v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// LDS of the policy's candidate search.
+struct CandLds {
+  int64_t T[kCandGroups][kCandBatch];
+  int64_t P[kCandGroups][kCandBatch];
+  int64_t pmax[kCandGroups][kCandBatch];
+  int64_t maxS[kCandGroups][kCandBatch];
+  double t[kCandBatch];
+  int64_t pages;
+  int pick[2];
+};
+
+// "2. Calibrated Adaptive Policy" on the device: the candidates of pkv_policy
+// in its order, each timed by the same model (policy_model.h), the earliest
+// fastest kept.  Candidates go 16 at a time: thread (candidate j, group r)
+// folds rows r, r+16, ... into a plan shape; 16 threads sum the groups and
+// evaluate the model; thread 0 keeps the first fastest.  row_n(b): pages of
+// row b (0 for an empty or flagged row).  All threads call it and all get
+// the choice.
+template <class RowN>
+__device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_cus,
+                            int head_dim, int page_size, RowN row_n, CandLds& L, int& mode,
+                            int& param) {
+  const int tid = threadIdx.x;
+  int nsplit = 0;
+  for (int64_t S = 1; S <= p.split_max; S *= 2) ++nsplit;
+  int nchunk = 0;
+  for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) ++nchunk;
+  const int ncand = nsplit + nchunk;
+  const int j = tid % kCandBatch;
+  const int grp = tid / kCandBatch;
+  double best_t = 0.0;
+  int best_i = -1;
+  int64_t total_pages = 0;
+  for (int cb = 0; cb < ncand; cb += kCandBatch) {
+    const int i = cb + j;
+    PlanShape f;
+    if (i < ncand) {
+      const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
+      const uint32_t v = i < nsplit ? (1u << i)
+                                    : static_cast<uint32_t>(p.chunk_min) << (i - nsplit);
+      for (int b = grp; b < B; b += kCandGroups) plan_shape_add(f, row_n(b), Hkv, m, v);
+    }
+    L.T[grp][j] = f.T;
+    L.P[grp][j] = f.P;
+    L.pmax[grp][j] = f.pmax;
+    L.maxS[grp][j] = f.maxS;
+    __syncthreads();
+    if (tid < kCandBatch && i < ncand) {
+      PlanShape F;
+      for (int r = 0; r < kCandGroups; ++r) {
+        F.T += L.T[r][j];
+        F.P += L.P[r][j];
+        F.pmax = L.pmax[r][j] > F.pmax ? L.pmax[r][j] : F.pmax;
+        F.maxS = L.maxS[r][j] > F.maxS ? L.maxS[r][j] : F.maxS;
+      }
+      L.t[j] = model_us(p, F, num_cus, head_dim, page_size, F.maxS > p.fuse_max_splits);
+      if (j == 0) L.pages = F.P;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      total_pages = L.pages;
+      for (int k = 0; k < kCandBatch && cb + k < ncand; ++k) {
+        if (best_i < 0 || L.t[k] < best_t) {
+          best_t = L.t[k];
+          best_i = cb + k;
+        }
+      }
+    }
+    __syncthreads();   // the shapes are rewritten by the next batch
+  }
+  if (tid == 0) {
+    if (total_pages == 0 || best_i < 0) {
+      L.pick[0] = PKV_MODE_SPLIT;
+      L.pick[1] = 1;
+    } else if (best_i < nsplit) {
+      L.pick[0] = PKV_MODE_SPLIT;
+      L.pick[1] = 1 << best_i;
+    } else {
+      L.pick[0] = PKV_MODE_WORKQUEUE;
+      L.pick[1] = p.chunk_min << (best_i - nsplit);
+    }
+  }
+  __syncthreads();
+  mode = L.pick[0];
+  param = L.pick[1];
+}
+
 // Everything the workgroup needs to know about one task.  All fields are
 // wave-uniform and live in SGPRs.
 struct Meta {
@@ -700,7 +850,7 @@ __device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_
 
 // Two workgroups per CU at d <= 128 (256 VGPRs each); one at d = 256, whose
 // larger tiles and accumulators need the AGPR half of the register file.
-template <int D, bool kStaged, class E, class KV>
+template <int D, bool kStaged, class E, class KV, bool kSelfPlan = false>
 __global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
 pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
@@ -730,7 +880,11 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ __attribute__((aligned(16))) float s_o[kWaves][kGroup][LDS_STRIDE];
   __shared__ int4 s_done[kMaxDone];   // (row, KV head, first slot, splits)
   __shared__ int s_lastf[kMaxDone];
+  // self-planned step only: the policy's candidate search and the row scan
+  __shared__ typename std::conditional<kSelfPlan, CandLds, char>::type s_cand;
+  __shared__ int s_plan[kSelfPlan ? 2 * kWaves + 2 : 1];
   static_assert(kWaves * kGroup * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
+  static_assert(!kSelfPlan || kStaged, "a self-planned step stages its rows");
 
   const MergeArgs ma{a.split_offsets, a.num_slots, a.B, a.Hq, a.Hkv, a.G, nullptr,
                      a.part_o, a.part_ml, a.out, a.lse, a.ctrl};
@@ -742,10 +896,130 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     num_tasks = __builtin_amdgcn_readfirstlane(a.plan_hdr[0]);
     fuse = __builtin_amdgcn_readfirstlane(a.plan_hdr[1]);
   }
+  // Self-planned step: "Row-Local Bounds" / "Compact Workqueue" from the
+  // staged lengths, as the planner kernel builds them (same policy, same
+  // offsets, same records in the same order).
+  int plan_mode = 0, plan_param = 1;
+  if constexpr (kSelfPlan) {
+    constexpr int kPer = (kRowStage + kThreads) / kThreads;
+    constexpr int kRows = kRowStage / kThreads;   // rows per thread in the scan
+    int lv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      lv[k] = i < a.B ? seq_lens_in[i] : 0;
+    }
+    // A row with N < 0 or more than max_pages pages is flagged and planned
+    // empty (its length staged as 0).
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < a.B) {
+        const int N = lv[k];
+        const bool ok = N >= 0 && (static_cast<int64_t>(N) + kPage - 1) / kPage <= a.max_pages;
+        bad |= ok ? 0 : 1;
+        s_len[i] = ok ? N : 0;
+      }
+    }
+    const int any_bad = __syncthreads_or(bad);
+    auto row_n = [&](int b) -> int32_t { return (s_len[b] + kPage - 1) / kPage; };
+    plan_mode = a.plan_mode;
+    plan_param = a.plan_param;
+    if (plan_mode < 0)
+      choose_plan(a.plan_pol, a.B, a.Hkv, a.plan_num_cus, a.plan_head_dim, kPage, row_n, s_cand,
+                  plan_mode, plan_param);
+    // splits per row, then their exclusive prefix: thread t takes rows
+    // kRows*t .. kRows*t + kRows-1
+    int sv[kRows];
+    int sum = 0, mx = 0;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int b = kRows * tid + k;
+      int S = 0;
+      if (b < a.B) {
+        const uint32_t n = static_cast<uint32_t>(row_n(b));
+        if (n > 0) {
+          const uint32_t c = plan_mode == PKV_MODE_SPLIT ? cdiv32(n, plan_param)
+                                                         : static_cast<uint32_t>(plan_param);
+          S = static_cast<int>(cdiv32(n, c));
+        }
+      }
+      sv[k] = S;
+      sum += S;
+      mx = S > mx ? S : mx;
+    }
+    int incl = sum;   // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const int wmax = static_cast<int>(wave_max64(mx));
+    if (lane == 63) s_plan[wave] = incl;
+    if (lane == 0) s_plan[kWaves + wave] = wmax;
+    __syncthreads();
+    int base = incl - sum;
+    int total = 0, maxS = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) base += s_plan[w];
+      total += s_plan[w];
+      maxS = s_plan[kWaves + w] > maxS ? s_plan[kWaves + w] : maxS;
+    }
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int b = kRows * tid + k;
+      if (b < a.B) s_off[b] = base;
+      base += sv[k];
+    }
+    if (tid == 0) s_off[a.B] = total;
+    num_tasks = a.Hkv * total;
+    fuse = (num_tasks == 0 || (maxS <= a.plan_pol.fuse_max_splits && a.plan_groups_fit)) ? 1 : 0;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int b = tid; b <= a.B; b += kThreads) a.plan_offs_out[b] = s_off[b];
+      if (tid == 0) {
+        a.plan_out[0] = num_tasks;
+        a.plan_out[1] = fuse;
+        a.plan_out[2] = plan_mode;
+        a.plan_out[3] = plan_param;
+        a.plan_out[4] = total;
+        a.plan_out[5] = maxS;
+        a.plan_out[6] = any_bad ? 1 : 0;
+        if (any_bad) flag_error(a.ctrl, PKV_DEVERR_ROW);
+      }
+    }
+  }
+  // Record of task t of a self-planned step, from the offsets in LDS: the
+  // row is the last one whose first task is <= t (rows without tasks share
+  // the next row's offset and come before it).  Written out for read-back
+  // by the workgroup that takes the task.
+  auto self_record = [&](int t) -> int4 {
+    if (t >= num_tasks) return int4{0, 0, 0, 1};
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.Hkv * s_off[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    const int b = lo;
+    const int S = s_off[b + 1] - s_off[b];
+    const int r = t - a.Hkv * s_off[b];
+    const int g = r / S;
+    const uint32_t n = static_cast<uint32_t>((s_len[b] + kPage - 1) / kPage);
+    const int c = plan_mode == PKV_MODE_SPLIT ? static_cast<int>(cdiv32(n, plan_param))
+                                              : plan_param;
+    const int4 rec = int4{b, g, r - g * S, c};
+    if (tid == 0) a.plan_tasks_out[t] = rec;
+    return rec;
+  };
   // Staging loads first (vector), then the first task record (scalar), then
   // the LDS stores: the two load latencies overlap instead of adding up.
   int4 rec0;
-  if constexpr (kStaged) {
+  if constexpr (kSelfPlan) {
+    rec0 = self_record(blockIdx.x);
+  } else if constexpr (kStaged) {
     constexpr int kPer = (kRowStage + kThreads) / kThreads;   // covers B+1 <= kRowStage+1
     int lv[kPer], ov[kPer];
 #pragma unroll
@@ -839,9 +1113,13 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const int par = it & 1;
     // next task's metadata, its first round of table entries and its q;
     // the index of the task after it (counter values start at 2*gridDim.x)
-    const Meta nxt =
-        load_meta<kStaged, kRing>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off, num_tasks,
-                                  t_nxt);
+    Meta nxt;
+    if constexpr (kSelfPlan)
+      nxt = decode_meta<kStaged, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, t_nxt,
+                                        self_record(t_nxt));
+    else
+      nxt = load_meta<kStaged, kRing>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off,
+                                      num_tasks, t_nxt);
     const Round<kRing> nr0 = load_round<kRing>(a, bt_in, nxt, wave, 0);
     // Wave 0: the index after next and the next task's q, both to LDS.
     // Their loads queue behind this task's first round, which the wave has
@@ -998,71 +1276,13 @@ __global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
 // A row with N_b < 0 or more than max_pages pages is flagged
 // (PKV_DEVERR_ROW) and planned as empty.
 
-struct PlanArgs {
-  const int32_t* seq_lens;
-  int32_t B, Hkv, head_dim, page_size, num_cus;
-  int32_t max_pages;
-  int32_t mode, param;      // mode < 0: the policy chooses
-  int32_t groups_fit;       // B * Hkv fits the fused merge's arrival counters
-  pkv_policy_params pol;    // candidate sets already limited to the capacity
-  int32_t* hdr;             // [kPlanHdrInts]
-  int32_t* offs;            // [B + 1]
-  int4* tasks;              // capacity Hkv * B * max_splits
-  uint32_t* ctrl;
-};
-
-constexpr int kPlanHdrInts = 16;
-constexpr int kPlanStage = 4096;   // rows whose page counts the planner keeps in LDS
-constexpr int kCandBatch = 16;     // policy candidates evaluated together
-constexpr int kCandGroups = kThreads / kCandBatch;
-
-__device__ __forceinline__ uint32_t cdiv32(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
-
-// Pages of row b, or -1 for a row to flag (N_b < 0 or more than max_pages
-// pages).  Read from global memory; the planner stages the first kPlanStage.
-__device__ __forceinline__ int32_t plan_row_pages_global(const PlanArgs& a, int b) {
-  const int32_t N = a.seq_lens[b];
-  if (N < 0) return -1;
-  const int64_t n = (static_cast<int64_t>(N) + a.page_size - 1) / a.page_size;
-  return n > a.max_pages ? -1 : static_cast<int32_t>(n);
-}
-
-// Add one row of n pages to the plan shape (mode, param): the arithmetic of
-// shape_add_row in 32 bits (n, c, S fit) with 64-bit sums.
-__device__ __forceinline__ void plan_shape_add(PlanShape& f, int32_t n, int32_t Hkv, int m,
-                                               uint32_t v) {
-  if (n <= 0) return;
-  const uint32_t un = static_cast<uint32_t>(n);
-  const uint32_t c = m == PKV_MODE_SPLIT ? cdiv32(un, v) : v;
-  const uint32_t S = cdiv32(un, c);
-  f.T += static_cast<int64_t>(Hkv) * S;
-  f.P += static_cast<int64_t>(Hkv) * un;
-  const int64_t largest = c < un ? c : un;
-  if (largest > f.pmax) f.pmax = largest;
-  if (static_cast<int64_t>(S) > f.maxS) f.maxS = S;
-}
-
-__device__ __forceinline__ int64_t wave_max64(int64_t v) {
-  for (int off = 32; off >= 1; off >>= 1) {
-    const int64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   __shared__ int32_t s_n[kPlanStage];
-  __shared__ int64_t s_cT[kCandGroups][kCandBatch];
-  __shared__ int64_t s_cP[kCandGroups][kCandBatch];
-  __shared__ int64_t s_cpmax[kCandGroups][kCandBatch];
-  __shared__ int64_t s_cmaxS[kCandGroups][kCandBatch];
-  __shared__ double s_ct[kCandBatch];
-  __shared__ int64_t s_cpages;
+  __shared__ CandLds s_cand;
   __shared__ int s_best_i[kWaves];
   __shared__ int s_scan[kThreads];
   __shared__ int s_S[kThreads];
   __shared__ int s_c[kThreads];
-  __shared__ int s_pick[2];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1086,75 +1306,11 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
     return n < 0 ? 0 : n;
   };
 
-  // ---- 1. policy: candidates in batches of 16; thread (candidate j, group
-  // r) folds rows r, r+16, ... into a plan shape; 16 threads then sum the
-  // groups, evaluate the model, and thread 0 keeps the first fastest.
+  // ---- 1. policy
   int mode = a.mode, param = a.param;
-  if (mode < 0) {
-    const pkv_policy_params& p = a.pol;
-    int nsplit = 0;
-    for (int64_t S = 1; S <= p.split_max; S *= 2) ++nsplit;
-    int nchunk = 0;
-    for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) ++nchunk;
-    const int ncand = nsplit + nchunk;
-    const int j = tid % kCandBatch;
-    const int grp = tid / kCandBatch;
-    double best_t = 0.0;
-    int best_i = -1;
-    int64_t total_pages = 0;
-    for (int cb = 0; cb < ncand; cb += kCandBatch) {
-      const int i = cb + j;
-      PlanShape f;
-      if (i < ncand) {
-        const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
-        const uint32_t v = i < nsplit ? (1u << i)
-                                      : static_cast<uint32_t>(p.chunk_min) << (i - nsplit);
-        for (int b = grp; b < a.B; b += kCandGroups) plan_shape_add(f, row_n(b), a.Hkv, m, v);
-      }
-      s_cT[grp][j] = f.T;
-      s_cP[grp][j] = f.P;
-      s_cpmax[grp][j] = f.pmax;
-      s_cmaxS[grp][j] = f.maxS;
-      __syncthreads();
-      if (tid < kCandBatch && i < ncand) {
-        PlanShape F;
-        for (int r = 0; r < kCandGroups; ++r) {
-          F.T += s_cT[r][j];
-          F.P += s_cP[r][j];
-          F.pmax = s_cpmax[r][j] > F.pmax ? s_cpmax[r][j] : F.pmax;
-          F.maxS = s_cmaxS[r][j] > F.maxS ? s_cmaxS[r][j] : F.maxS;
-        }
-        s_ct[j] = model_us(p, F, a.num_cus, a.head_dim, a.page_size, F.maxS > p.fuse_max_splits);
-        if (j == 0) s_cpages = F.P;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        total_pages = s_cpages;
-        for (int k = 0; k < kCandBatch && cb + k < ncand; ++k) {
-          if (best_i < 0 || s_ct[k] < best_t) {
-            best_t = s_ct[k];
-            best_i = cb + k;
-          }
-        }
-      }
-      __syncthreads();   // s_c* are rewritten by the next batch
-    }
-    if (tid == 0) {
-      if (total_pages == 0 || best_i < 0) {
-        s_pick[0] = PKV_MODE_SPLIT;
-        s_pick[1] = 1;
-      } else if (best_i < nsplit) {
-        s_pick[0] = PKV_MODE_SPLIT;
-        s_pick[1] = 1 << best_i;
-      } else {
-        s_pick[0] = PKV_MODE_WORKQUEUE;
-        s_pick[1] = p.chunk_min << (best_i - nsplit);
-      }
-    }
-    __syncthreads();
-    mode = s_pick[0];
-    param = s_pick[1];
-  }
+  if (mode < 0)
+    choose_plan(a.pol, a.B, a.Hkv, a.num_cus, a.head_dim, a.page_size, row_n, s_cand, mode,
+                param);
 
   // ---- 2. split offsets and records, 256 rows at a time
   int carry = 0;
@@ -1251,7 +1407,10 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     const bool staged = da.B <= kRowStage;
-    if (ev0 || ev1) {
+    if (da.plan_out) {   // self-planned step (staged rows only; checked by the caller)
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true>), dim3(grid), dim3(kThreads), 0,
+                         stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
+    } else if (ev0 || ev1) {
       if (staged)
         hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV>), dim3(grid), dim3(kThreads), 0,
                               stream, ev0, ev1, 0, da, tasks, da.block_table, da.seq_lens,
@@ -1639,16 +1798,30 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   pa.offs = offs;
   pa.tasks = reinterpret_cast<int4*>(tasks);
   pa.ctrl = da.ctrl;
-  da.plan_hdr = hdr;
   da.task_cap = static_cast<int32_t>(L.task_cap > 0 ? L.task_cap : 1);
   da.num_tasks = 0;
   ma.plan_hdr = hdr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(pkv::pkv_plan_kernel, dim3(1), dim3(pkv::kThreads), 0, s, pa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    pkv::set_hip_error(static_cast<int>(e));
-    return PKV_ERR_HIP;
+  if (B <= pkv::kRowStage) {
+    // One launch: every decode workgroup plans from the lengths it stages
+    // anyway (the same policy and plan as the planner kernel).
+    da.plan_mode = mode;
+    da.plan_param = param;
+    da.plan_num_cus = num_cus;
+    da.plan_head_dim = pa.head_dim;
+    da.plan_groups_fit = pa.groups_fit;
+    da.plan_pol = pol;
+    da.plan_out = hdr;
+    da.plan_offs_out = offs;
+    da.plan_tasks_out = reinterpret_cast<int4*>(tasks);
+  } else {
+    da.plan_hdr = hdr;
+    hipLaunchKernelGGL(pkv::pkv_plan_kernel, dim3(1), dim3(pkv::kThreads), 0, s, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      pkv::set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
   }
   // The task count is known only on the device: one workgroup per CU (as
   // fast as two per CU on the measured workloads, and with no pair of
