@@ -253,18 +253,44 @@ constexpr int kRsrcDword3 = 0x00020000;
 // write back or invalidate a whole L2.
 constexpr int kCoherent = 17;   // sc0 | sc1
 
+// Cache policy of the page loads.  A step reads every K/V tile exactly once.
+// With the nt (non-temporal, streaming) bit, a grid that keeps every CU busy
+// streams the pools faster (B64 at d = 128: 5.8 -> 6.4 TB/s with fp16, 5.6 ->
+// 5.9 TB/s with fp8), but one workgroup alone on its CU streams slower (about
+// 28 instead of 34 GB/s), so a plan with fewer tasks than about 7/8 of the
+// CUs keeps the default policy.  The loads must be wide: fp8 K rows read in
+// 8-byte pieces streamed far slower with the bit (B64: 833 -> 1066 us), hence
+// the 16-byte K loads of load_page.
+constexpr int kStream = 2;   // nt
+constexpr int kDefault = 0;
+
+// num_tasks < 0: not known on the host (a self-planned step).
+inline bool streaming_loads(int64_t num_tasks, int num_cus) {
+  return num_tasks < 0 || 8 * num_tasks >= 7 * static_cast<int64_t>(num_cus);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), kRsrcDword3);
 }
 
-// K operand of the score MFMA: token row `col`, 8 halves at d-chunk 4*kk+grp
-// (byte offset koff + 64*kk with koff = 2*(col*D + 8*grp)).  V: token rows
-// 4*grp + j, VW halves at d = VW*col (byte offset voff + 2*D*j with
-// voff = 2*(4*grp*D + VW*col)).  Each K instruction reads 16 runs of 64
-// contiguous bytes, and each V instruction reads 4 whole 2*D-byte rows of
-// the contiguous page tile.
-template <int D, class E, class KV>
+// d-chunk (8 elements) of the score MFMA's step kk for lane group grp.
+template <class KV>
+__device__ __forceinline__ constexpr int k_chunk(int kk, int grp) {
+  return kv_bytes<KV>() == 1 ? 8 * (kk >> 1) + 2 * grp + (kk & 1) : 4 * kk + grp;
+}
+
+// K operand of the score MFMA: token row `col`, 8 elements at d-chunk
+// k_chunk(kk, grp) (8 elements per chunk).  2-byte pools: chunk 4*kk+grp,
+// byte offset koff + 64*kk with koff = 2*(col*D + 8*grp); fp8 pools: chunks
+// 8*(kk/2) + 2*grp + kk%2, so one 16-byte load at koff + 64*(kk/2) with
+// koff = col*D + 16*grp brings the codes of kk and kk+1.  Either way each K
+// instruction reads 16 runs of 64 contiguous bytes; q takes the same chunk
+// map, and the score sums over all chunks.  V: token rows 4*grp + j, VW
+// elements at d = VW*col (byte offset voff + e*D*j with voff =
+// e*(4*grp*D + VW*col), e bytes per element): each V instruction reads 4
+// whole rows of the contiguous page tile.
+template <int D, class E, class KV, int kCpol>
 __device__ __forceinline__ void load_page(PageRegs<D, E, KV>& r, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, int koff, int voff) {
   constexpr int KK = D / 32;
@@ -272,40 +298,44 @@ __device__ __forceinline__ void load_page(PageRegs<D, E, KV>& r, __amdgpu_buffer
   if constexpr (kv_bytes<KV>() == 1) {
     // the same lanes and rows, at one byte per element
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      r.k[kk] = __builtin_bit_cast(
-          uint2x, __builtin_amdgcn_raw_buffer_load_b64(kr, koff + 32 * kk, 0, 0));
+    for (int kk = 0; kk < KK; kk += 2) {
+      const uint4x w = __builtin_bit_cast(
+          uint4x, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 32 * kk, 0, kCpol));
+      r.k[kk] = uint2x{w[0], w[1]};
+      r.k[kk + 1] = uint2x{w[2], w[3]};
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (VW == 16)
-        r.v[j] = __builtin_bit_cast(uint4x,
-                                    __builtin_amdgcn_raw_buffer_load_b128(vr, voff + D * j, 0, 0));
+        r.v[j] = __builtin_bit_cast(
+            uint4x, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + D * j, 0, kCpol));
       else if constexpr (VW == 8)
-        r.v[j] = __builtin_bit_cast(uint2x,
-                                    __builtin_amdgcn_raw_buffer_load_b64(vr, voff + D * j, 0, 0));
+        r.v[j] = __builtin_bit_cast(
+            uint2x, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + D * j, 0, kCpol));
       else
-        r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff + D * j, 0, 0);
+        r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff + D * j, 0, kCpol);
     }
   } else {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       r.k[kk] = __builtin_bit_cast(
-          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, 0));
+          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, kCpol));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (VW == 16) {
         const vecE<E, 8> lo = __builtin_bit_cast(
-            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
+            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, kCpol));
         const vecE<E, 8> hi = __builtin_bit_cast(
-            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, 0));
+            vecE<E, 8>,
+            __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, kCpol));
         r.v[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
                                          14, 15);
       } else if constexpr (VW == 8) {
         r.v[j] = __builtin_bit_cast(
-            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, 0));
+            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, kCpol));
       } else {
         r.v[j] = __builtin_bit_cast(
-            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, 0));
+            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, kCpol));
       }
     }
   }
@@ -850,7 +880,7 @@ __device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_
 
 // Two workgroups per CU at d <= 128 (256 VGPRs each); one at d = 256, whose
 // larger tiles and accumulators need the AGPR half of the register file.
-template <int D, bool kStaged, class E, class KV, bool kSelfPlan = false>
+template <int D, bool kStaged, class E, class KV, bool kSelfPlan, bool kNt>
 __global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
 pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
@@ -1051,7 +1081,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   const int G = a.G;
   const int64_t tile_elems = static_cast<int64_t>(kPage) * D;
   const int64_t stride_bytes = static_cast<int64_t>(a.Hkv) * tile_elems * kKvb;
-  const int koff = kKvb * (col * D + 8 * grp);
+  const int koff = kKvb == 1 ? col * D + 16 * grp : kKvb * (col * D + 8 * grp);
   const int voff = kKvb * (4 * grp * D + VW * col);
   const char* kpool = reinterpret_cast<const char*>(a.k);
   const char* vpool = reinterpret_cast<const char*>(a.v);
@@ -1068,8 +1098,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const int64_t off = static_cast<int64_t>(m.g) * tile_elems * kKvb +
                         (live ? static_cast<int64_t>(e) * stride_bytes : 0);
     const uint32_t bytes = live ? kTileBytes : 0u;
-    load_page<D, E, KV>(r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff,
-                        voff);
+    load_page<D, E, KV, kNt ? kStream : kDefault>(r, make_rsrc(kpool + off, bytes),
+                                                  make_rsrc(vpool + off, bytes), koff, voff);
     return live;
   };
   // q of task m (B operand of the score MFMA, column = head within the
@@ -1081,7 +1111,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                                 static_cast<int64_t>(m.g) * G + (live ? col : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = *reinterpret_cast<const vecE<E, 8>*>(qp + 8 * (4 * kk + grp));
+      qf[kk] = *reinterpret_cast<const vecE<E, 8>*>(qp + 8 * k_chunk<KV>(kk, grp));
   };
   auto store_q = [&](const Meta& m, const vecE<E, 8> (&qf)[KK], vecE<E, 8>* dst) {
     const bool live = m.ok && col < G;
@@ -1401,30 +1431,34 @@ int num_cus_of_current_device(int* cus) {
 // ev0 / ev1 (optional): events that take the decode kernel's own start and
 // end timestamps (hipExtLaunchKernel), for timing it without the queue time
 // of separately recorded events.
-template <int D, class E, class KV>
-int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
-           bool decode, hipEvent_t ev0, hipEvent_t ev1) {
+// kNt: page loads with the streaming cache policy (streaming_loads).
+template <int D, class E, class KV, bool kNt>
+int launch_nt(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
+              bool decode, hipEvent_t ev0, hipEvent_t ev1) {
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     const bool staged = da.B <= kRowStage;
     if (da.plan_out) {   // self-planned step (staged rows only; checked by the caller)
-      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true>), dim3(grid), dim3(kThreads), 0,
-                         stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true, kNt>), dim3(grid),
+                         dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
+                         da.split_offsets);
     } else if (ev0 || ev1) {
       if (staged)
-        hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV>), dim3(grid), dim3(kThreads), 0,
-                              stream, ev0, ev1, 0, da, tasks, da.block_table, da.seq_lens,
-                              da.split_offsets);
+        hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kNt>), dim3(grid),
+                              dim3(kThreads), 0, stream, ev0, ev1, 0, da, tasks, da.block_table,
+                              da.seq_lens, da.split_offsets);
       else
-        hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV>), dim3(grid), dim3(kThreads),
-                              0, stream, ev0, ev1, 0, da, tasks, da.block_table, da.seq_lens,
-                              da.split_offsets);
+        hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kNt>), dim3(grid),
+                              dim3(kThreads), 0, stream, ev0, ev1, 0, da, tasks, da.block_table,
+                              da.seq_lens, da.split_offsets);
     } else if (staged) {
-      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV>), dim3(grid), dim3(kThreads), 0,
-                         stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kNt>), dim3(grid),
+                         dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
+                         da.split_offsets);
     } else {
-      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV>), dim3(grid), dim3(kThreads), 0,
-                         stream, da, tasks, da.block_table, da.seq_lens, da.split_offsets);
+      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kNt>), dim3(grid),
+                         dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
+                         da.split_offsets);
     }
   } else {
     // no decode kernel (no tasks): the events still mark this point of the stream
@@ -1450,28 +1484,35 @@ int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stre
   return PKV_OK;
 }
 
+template <int D, class E, class KV>
+int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream, bool decode,
+           bool nt, hipEvent_t ev0, hipEvent_t ev1) {
+  return nt ? launch_nt<D, E, KV, true>(da, ma, grid, stream, decode, ev0, ev1)
+            : launch_nt<D, E, KV, false>(da, ma, grid, stream, decode, ev0, ev1);
+}
+
 template <class E, class KV>
 int launch_d(int head_dim, const DecodeArgs& da, const MergeArgs& ma, int grid,
-             hipStream_t stream, bool decode, hipEvent_t ev0, hipEvent_t ev1) {
-  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode, ev0, ev1);
-  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode, ev0, ev1)
-                         : launch<64, E, KV>(da, ma, grid, stream, decode, ev0, ev1);
+             hipStream_t stream, bool decode, bool nt, hipEvent_t ev0, hipEvent_t ev1) {
+  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode, nt, ev0, ev1);
+  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode, nt, ev0, ev1)
+                         : launch<64, E, KV>(da, ma, grid, stream, decode, nt, ev0, ev1);
 }
 
 // The kernels of one head dimension and element-type pair (both checked by
 // the caller).
 int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& ma, int grid,
-               hipStream_t stream, bool decode, hipEvent_t ev0 = nullptr,
+               hipStream_t stream, bool decode, bool nt, hipEvent_t ev0 = nullptr,
                hipEvent_t ev1 = nullptr) {
   switch (dtype) {
     case PKV_DTYPE_BF16:
-      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
+      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
     case PKV_DTYPE_F16_KV_FP8:
-      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
+      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
     case PKV_DTYPE_BF16_KV_FP8:
-      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
+      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
     default:
-      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode, ev0, ev1);
+      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
   }
 }
 
@@ -1608,10 +1649,12 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
     do_merge = false;
   }
   int grid = 1;
+  bool nt = false;
   if (do_decode) {
     int cus = 0;
     st = pkv::num_cus_of_current_device(&cus);
     if (st != PKV_OK) return st;
+    nt = pkv::streaming_loads(num_tasks, cus);
     // as many workgroups as fit at once (persistent: a workgroup that had to
     // wait for a slot would hold its static tasks until the others finish)
     int64_t g = static_cast<int64_t>(cus) * (head_dim == 256 ? 1 : 2);
@@ -1624,8 +1667,8 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool decode = da.num_tasks > 0;
   da.task_cap = da.num_tasks > 0 ? da.num_tasks : 1;
-  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode, static_cast<hipEvent_t>(ev0),
-                         static_cast<hipEvent_t>(ev1));
+  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode, nt,
+                         static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1));
 }
 
 }  // namespace
@@ -1830,7 +1873,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   // every plan is fused, and the merge kernel is not launched at all.
   const int grid = num_cus;
   if (max_splits <= pol.fuse_max_splits && pa.groups_fit) ma.B = 0;
-  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true);
+  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true,
+                         pkv::streaming_loads(-1, num_cus));
 }
 
 int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,

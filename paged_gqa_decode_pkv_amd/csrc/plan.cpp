@@ -53,14 +53,14 @@ int pkv_policy_defaults(pkv_policy_params* p) {
   p->fuse_max_splits = 16;
   // Fitted on the calibration seed (paged_gqa_decode_pkv_amd/calibration/
   // mi355x_fit.json, written by policy_fit.py from calibrate.py's runs).
-  p->t0_us = 10.01;
-  p->t_round_us = 5.849;
-  p->alpha = 1.056;
-  p->cu_gbps = 45.71;
-  p->hbm_gbps = 8113.0;
-  p->t_two_us = 5.69;
-  p->t_two_split_us = 0.01229;
-  p->t_fused_split_us = 0.2748;
+  p->t0_us = 0.2777;
+  p->t_round_us = 5.491;
+  p->alpha = 0.8341;
+  p->cu_gbps = 45.85;
+  p->hbm_gbps = 8292.0;
+  p->t_two_us = 6.975;
+  p->t_two_split_us = 0.0218;
+  p->t_fused_split_us = 0.2892;
   return PKV_OK;
 }
 

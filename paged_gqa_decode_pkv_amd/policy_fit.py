@@ -11,7 +11,8 @@ thresholds fixed on a calibration seed and then evaluated on held-out seeds
            documented at ``pkv_policy`` in include/pkv.h
   judge    for every (trace, seed): the schedule the fitted policy picks,
            its measured time, the best measured schedule, and the regret
-           (picked / best); also the regret of a fixed reference rule
+           (picked / best); also the regret of the runner's own pick during the
+           runs (the policy the library held when they were taken)
 
 ``python -m paged_gqa_decode_pkv_amd.policy_fit --revalidate RUNS.jsonl`` judges the
 committed constants on fresh runs instead (``calibration/mi355x_revalidation.json``).
@@ -158,8 +159,9 @@ def fit(recs, cus, head_dim):
     lb = [0.0, 0.0, 0.0, 1.0, 500.0, 0.0, 0.0, 0.0]
     ub = [200.0, 100.0, 4.0, 1000.0, 20000.0, 100.0, 10.0, 20.0]
     sol = least_squares(resid, x0, bounds=(lb, ub))
-    # round to 4 significant digits: these are the published defaults
-    x = [float(f"{v:.4g}") for v in sol.x]
+    # round to 4 significant digits: these are the published defaults (a
+    # constant that the fit drives onto its lower bound of 0 is published as 0)
+    x = [0.0 if abs(v) < 1e-9 else float(f"{v:.4g}") for v in sol.x]
     return x, float(np.sqrt(np.mean(resid(x) ** 2)))
 
 
@@ -247,15 +249,15 @@ def main(argv=None):
         "fit_rms_log_error_calibration_seed": round(rms, 4),
         "held_out_regret_mean": round(float(np.mean(held)), 4),
         "held_out_regret_max": round(float(np.max(held)), 4),
-        "reference_rule_held_out_regret_mean": round(float(np.mean(held_rule)), 4) if held_rule else None,
-        "reference_rule_held_out_regret_max": round(float(np.max(held_rule)), 4) if held_rule else None,
+        "runner_pick_held_out_regret_mean": round(float(np.mean(held_rule)), 4) if held_rule else None,
+        "runner_pick_held_out_regret_max": round(float(np.max(held_rule)), 4) if held_rule else None,
         "rows": rows,
     }
     with open(os.path.join(CAL_DIR, "mi355x_fit.json"), "w") as f:
         json.dump(summary, f, indent=1)
     name = lambda m: f"{'S' if m[0] == 0 else 'c'}={m[1]}{'/2L' if m[2] else ''}"
     print("params:", json.dumps(summary["params"]))
-    print(f"{'trace':12s} {'seed':8s} {'pick':10s} {'us':>8s} {'best':10s} {'us':>8s} {'regret':>7s} {'rule regret':>11s}")
+    print(f"{'trace':12s} {'seed':8s} {'pick':10s} {'us':>8s} {'best':10s} {'us':>8s} {'regret':>7s} {'runner pick':>11s}")
     for r in rows:
         print(f"{r['trace']:12s} {r['seed']} {name(r['pick']):10s} {r['pick_us']:8.1f} "
               f"{name(r['best']):10s} {r['best_us']:8.1f} {r['regret']:7.3f} "
