@@ -270,3 +270,26 @@ def test_device_plan_batch_beyond_lds_staging():
     _check_plan(wl, 8, hdr, tasks, offs, -1, 0)
     rows = sorted(rng.choice(B, size=48, replace=False).tolist())
     _parity(wl, out, lse, rows=rows)
+
+
+@pytest.mark.parametrize("name,dtype,mode,param", [
+    ("b8_zipf", "f16", 1, 256),      # 208 tasks: the host step keeps the default cache policy
+    ("b1", "f16", 0, 16),            # 128 tasks: likewise
+    ("b8_bimodal", "f16", 1, 128),   # 256 tasks: both stream with nt
+    ("b8_zipf", "fp8", 1, 256),
+    ("b8_bimodal", "fp8", 1, 128),
+])
+def test_device_step_equals_host_step_bit_for_bit(name, dtype, mode, param):
+    """The same plan computes the same bits whichever way it was planned and
+    whatever cache policy its page loads carry: the device-planned step always
+    streams with nt, the host-planned step only when the plan has at least 7/8
+    as many tasks as the GPU has CUs."""
+    from tests.gpu_util import run_hip
+    wl = make_workload(name, SEED, device="cuda", dtype=dtype)
+    log_case("device vs host step", name, dtype, mode, param)
+    host_out, host_lse, dec = run_hip(wl, mode, param)
+    assert dec.last[:2] == (mode, param) and not dec.last[5]
+    out, lse, hdr, _, _, _ = _run(wl, 256, mode, param)
+    assert hdr["fused"] == 1
+    assert np.array_equal(out.float().cpu().numpy(), host_out.float().cpu().numpy())
+    assert np.array_equal(lse.cpu().numpy(), host_lse.cpu().numpy())
