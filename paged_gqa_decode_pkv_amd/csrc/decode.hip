@@ -7,34 +7,44 @@
 // KV-head group so K/V tiles are reused across the grouped query heads.
 //
 // Kernel 1, pkv_decode_kernel (persistent workqueue):
-//   A grid of (CUs x 2) workgroups of 4 waves.  A workgroup takes task
-//   indices from a device-scope atomic counter.  The next index is fetched
-//   while the current task runs.  A task is (row b, KV head g, split s,
-//   chunk c).  The 4 waves interleave over the task's pages.  Each wave
-//   keeps an online-softmax state for the G query heads.  At task end the
-//   4 states are combined in LDS.  The result is written as the final fp16
-//   output (rows with one split) or as an fp32 partial state.
+//   min(T, 2 x CUs) workgroups of 4 waves (one per CU at d = 256).  A
+//   workgroup's first two tasks are static (blockIdx.x, blockIdx.x +
+//   gridDim.x); later indices come from a device-scope atomic counter, fetched
+//   two tasks ahead.  A task is (row b, KV head g, split s, chunk c).  The 4
+//   waves interleave over the task's pages, each keeping an online-softmax
+//   state for the G query heads; at task end the 4 states are combined in LDS
+//   and written as the final output (rows with one split) or as an fp32
+//   partial state.  In the fused form the workgroup that brings a group's
+//   arrival count to its split count merges the group (merge_group).  The
+//   kSelfPlan instance plans the step itself from the row lengths (policy,
+//   split offsets, task records), for the device-planned step.
 //
 // Kernel 2, pkv_merge_kernel: the exact log-sum-exp combination of a row's
-//   partial states, one workgroup per (row, query head).
+//   partial states in the two-launch form, one workgroup per (row, KV head)
+//   for the G heads of the group.
 //
-// One page tile = 16 tokens x head_dim fp16 of one KV head (4 KiB at
-// d=128), contiguous in the pool.  Per page and wave:
+// Kernel 3, pkv_plan_kernel: the device-planned step's plan for batches too
+//   large to stage in LDS (one workgroup).
+//
+// One page tile = 16 tokens x head_dim elements of one KV head (4 KiB at
+// d=128 in fp16), contiguous in the pool.  Per page and wave:
 //   S^T[16 tok x 16 head] = K[16 tok x d] . Q^T[d x 16 head]
-//       d/32 MFMA 16x16x32 f16.  A = K rows straight from memory, B = q of
-//       the G heads (columns >= G are zero).
+//       d/32 MFMA 16x16x32 (f16 or bf16).  A = K rows straight from memory
+//       (fp8 codes converted in registers), B = q of the G heads (columns
+//       >= G are zero).
 //   online softmax in fp32, base 2.  scale*log2(e) is folded into the scores.
 //   O^T[d x 16 head] += V^T[d x 16 tok] . P^T[16 tok x 16 head]
-//       d/16 MFMA 16x16x16 f16.  The C layout of the score MFMA (lane l holds
+//       d/16 MFMA 16x16x16.  The C layout of the score MFMA (lane l holds
 //       rows 4*(l/16)+j, column l%16) is exactly the B layout that the
 //       16x16x16 MFMA wants, so P feeds straight through in registers.  The
-//       A operand gathers 4 tokens of one d column per lane.  Lane l loads
-//       16 bytes of each token row 4*(l/16)+j, so each load instruction
-//       covers 4 whole rows of 256 B, and the gather is a byte permute.
+//       A operand gathers 4 tokens of one d column per lane: lane l loads
+//       its slice of each token row 4*(l/16)+j, so each load instruction
+//       covers 4 whole rows, and the gather is a byte permute.
 //
-// Numerics: fp16 inputs, fp32 scores / max / sums / accumulators.  The
-// probabilities p = 2^(s - m) lie in (0, 1] (unnormalised) and are rounded to
-// fp16 for the PV MFMA.  The row sum uses the same rounded values, so the
+// Numerics: fp16 / bf16 inputs (fp8 E4M3 pools decode exactly into q's
+// type), fp32 scores / max / sums / accumulators.  The probabilities
+// p = 2^(s - m) lie in (0, 2^8] (lazy maximum) and are rounded to q's type
+// for the PV MFMA.  The row sum uses the same rounded values, so the
 // normalisation is consistent.  Final division in fp32, output rounded to
 // nearest even.  Tokens past the row's length are masked with selects, never
 // multiplies, so NaN in unused page slots cannot leak.
@@ -53,13 +63,8 @@
 
 namespace pkv {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned uint2x __attribute__((ext_vector_type(2)));
-
-template <int N>
-using halfN = _Float16 __attribute__((ext_vector_type(N)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 // Vectors of the element type E of q, K, V and out: _Float16 or __bf16.
@@ -224,7 +229,7 @@ template <int D, class E>
 struct PageRegs<D, E, Fp8E4M3> {
   static constexpr int KK = D / 32;
   static constexpr int VW = D / 16;
-  uint2x k[KK];                    // the 8 codes of the K operand of chunk kk
+  uint2x k[KK];                    // the 8 codes of the K operand of MFMA step kk
   typename CodeVec<VW>::T v[4];    // VW codes of token row 4*grp + j
 };
 
