@@ -201,6 +201,7 @@ def main():
     dec_ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
     mode, param, T, nslots = dec.last[:4]
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nt_loads = 8 * T >= 7 * num_cus and (cfg.D != 256 or args.kv_dtype == "fp8")
     two_launch = bool(dec.last[5])
     avg_dec_s = float(dec_ms.mean()) * 1e-3
     achieved = kv_bytes / avg_dec_s / 1e9
@@ -252,10 +253,11 @@ def main():
                                  "mode": ["split", "workqueue"][mode], "param": param,
                                  "merge": "two-launch" if two_launch else "fused"}),
             # the library streams the pages with the nt cache policy when the
-            # plan has at least 7/8 as many tasks as the GPU has CUs
+            # plan has at least 7/8 as many tasks as the GPU has CUs (2-byte
+            # pools at d = 256 excepted)
             "kernel": f"pkv_decode_kernel<{cfg.D}, {'true' if B <= 1024 else 'false'}, _Float16, "
                       f"{'pkv::Fp8E4M3' if args.kv_dtype == 'fp8' else '_Float16'}, false, "
-                      f"{'true' if 8 * T >= 7 * num_cus else 'false'}>",
+                      f"{'true' if nt_loads else 'false'}>",
             "event_timed_steps": len(events),
             "algorithmic_bytes_per_launch": kv_bytes,
             "extras_bytes_per_launch": extras,

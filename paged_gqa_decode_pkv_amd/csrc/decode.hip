@@ -263,14 +263,18 @@ constexpr int kCoherent = 17;   // sc0 | sc1
 // streams the pools faster (B64 at d = 128: 5.8 -> 6.4 TB/s with fp16, 5.6 ->
 // 5.9 TB/s with fp8), but one workgroup alone on its CU streams slower (about
 // 28 instead of 34 GB/s), so a plan with fewer tasks than about 7/8 of the
-// CUs keeps the default policy.  The loads must be wide: fp8 K rows read in
-// 8-byte pieces streamed far slower with the bit (B64: 833 -> 1066 us), hence
-// the 16-byte K loads of load_page.
+// CUs keeps the default policy, and so do 2-byte pools at d = 256 (one
+// workgroup per CU, 8 KiB tiles: about 7% slower with the bit, while fp8
+// pools at d = 256 gain about 6%).  The loads must be wide: fp8 K rows read
+// in 8-byte pieces streamed far slower with the bit (B64: 833 -> 1066 us),
+// hence the 16-byte K loads of load_page.
 constexpr int kStream = 2;   // nt
 constexpr int kDefault = 0;
 
 // num_tasks < 0: not known on the host (a self-planned step).
-inline bool streaming_loads(int64_t num_tasks, int num_cus) {
+inline bool streaming_loads(int head_dim, int dtype, int64_t num_tasks, int num_cus) {
+  const bool fp8 = dtype == PKV_DTYPE_F16_KV_FP8 || dtype == PKV_DTYPE_BF16_KV_FP8;
+  if (head_dim == 256 && !fp8) return false;
   return num_tasks < 0 || 8 * num_tasks >= 7 * static_cast<int64_t>(num_cus);
 }
 
@@ -763,7 +767,8 @@ __device__ __forceinline__ int4 load_record(const DecodeArgs& a, const int4* __r
 }
 
 template <bool kStaged, int R>
-__device__ __forceinline__ Meta decode_meta(const DecodeArgs& a, const int32_t* __restrict__ seq_lens,
+__device__ __forceinline__ Meta decode_meta(const DecodeArgs& a,
+                                            const int32_t* __restrict__ seq_lens,
                                             const int32_t* __restrict__ offs, const int* s_len,
                                             const int* s_off, int num_tasks, int t, int4 rec) {
   Meta m;
@@ -1659,7 +1664,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
     int cus = 0;
     st = pkv::num_cus_of_current_device(&cus);
     if (st != PKV_OK) return st;
-    nt = pkv::streaming_loads(num_tasks, cus);
+    nt = pkv::streaming_loads(head_dim, dtype, num_tasks, cus);
     // as many workgroups as fit at once (persistent: a workgroup that had to
     // wait for a slot would hold its static tasks until the others finish)
     int64_t g = static_cast<int64_t>(cus) * (head_dim == 256 ? 1 : 2);
@@ -1879,7 +1884,7 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   const int grid = num_cus;
   if (max_splits <= pol.fuse_max_splits && pa.groups_fit) ma.B = 0;
   return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true,
-                         pkv::streaming_loads(-1, num_cus));
+                         pkv::streaming_loads(head_dim, dtype, -1, num_cus));
 }
 
 int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
