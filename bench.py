@@ -197,6 +197,16 @@ def main():
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
     dec = decs[0]
 
+    # Outside the timed region: one step at a time, each waited for, as the
+    # pages time a step (host policy and plan, launches, synchronisation).
+    synced = []
+    for i in range(min(K, 50)):
+        s0 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        synced.append((time.perf_counter() - s0) * 1e6)
+    synced = np.array(synced)
+
     wall = t1 - t0
     dec_ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
     mode, param, T, nslots = dec.last[:4]
@@ -237,6 +247,13 @@ def main():
                     "+ decode kernel (+ merge kernel in the two-launch form)",
         },
         "kv_gbps_step": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "synced_step_us": {
+            "median": round(float(np.median(synced)), 2),
+            "p10": round(float(np.percentile(synced, 10)), 2),
+            "p90": round(float(np.percentile(synced, 90)), 2),
+            "note": "one step at a time, each followed by a synchronisation (outside the timed "
+                    "region): the latency of a lone step, host policy and plan included",
+        },
         "gpu_us": {
             "decode_mean": round(float(dec_ms.mean()) * 1e3, 2),
             "decode_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
