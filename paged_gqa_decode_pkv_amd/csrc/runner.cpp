@@ -1,6 +1,7 @@
 // Native step runner: one call runs the whole hot path of a decode step.
-// It chooses the policy, plans on the host, uploads the plan in one async
-// copy, and enqueues the decode and merge kernels.
+// It chooses the policy, plans on the host, hands the plan to the kernels
+// (pinned memory for a new plan, a device copy for a repeated one), and
+// enqueues the decode kernel (and the merge kernel in the two-launch form).
 //
 // Source: PersistentKV (arXiv 2606.26666), gist.science explainer,
 // "Technische Samenvatting" > "2. Calibrated Adaptive Policy" and
