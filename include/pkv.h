@@ -478,10 +478,10 @@ typedef struct pkv_step_args {
   void* stream;                  /* hipStream_t */
   void* event_before_decode;     /* optional hipEvent_t pair (created by the caller)
                                     that takes the decode kernel's own start ... */
-  void* event_after_decode;      /* ... and end timestamps (hipExtLaunchKernel); in
-                                    the two-launch form the merge kernel comes after
-                                    the end.  A step without tasks records both where
-                                    the kernel would have run. */
+  void* event_after_decode;      /* ... and end timestamps (hipExtLaunchKernel); either
+                                    may be NULL.  In the two-launch form the merge
+                                    kernel comes after the end.  A step without tasks
+                                    records them where the kernel would have run. */
   /* outputs */
   int32_t chosen_mode;
   int32_t chosen_param;

@@ -564,9 +564,10 @@ class PagedDecoder:
     def run(self, mode: Optional[int] = None, param: Optional[int] = None, stream=None,
             events=None, two_launch: Optional[bool] = None):
         """Enqueue one step on the bound inputs.  ``events`` = (before, after)
-        torch.cuda.Event pair recorded around the decode kernel, or None.
-        ``two_launch``: True = separate merge kernel, False = fused single
-        launch, None = the policy's choice (fuse_max_splits)."""
+        torch.cuda.Event pair that takes the decode kernel's start and end
+        timestamps (either may be None), or None.  ``two_launch``: True =
+        separate merge kernel, False = fused single launch, None = the
+        policy's choice (fuse_max_splits)."""
         import torch
         a = self.args
         a.two_launch = -1 if two_launch is None else (1 if two_launch else 0)
@@ -574,8 +575,8 @@ class PagedDecoder:
         a.param = 0 if param is None else param
         a.stream = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
         if events is not None:
-            a.event_before_decode = events[0].cuda_event
-            a.event_after_decode = events[1].cuda_event
+            a.event_before_decode = None if events[0] is None else events[0].cuda_event
+            a.event_after_decode = None if events[1] is None else events[1].cuda_event
         else:
             a.event_before_decode = None
             a.event_after_decode = None
