@@ -228,7 +228,13 @@ def main():
     dec_ms = np.array([e0.elapsed_time(e1) / win for e0, e1 in events])
     mode, param, T, nslots = dec.last[:4]
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
-    nt_loads = 8 * T >= 7 * num_cus and (cfg.D != 256 or args.kv_dtype == "fp8")
+    # the page loads' cache policy the library picks for this plan (0: default,
+    # 1: nt on V, 2: nt on K and V)
+    fp8 = args.kv_dtype == "fp8"
+    if (cfg.D == 256 and not fp8) or 8 * T < 7 * num_cus:
+        load_mode = 0
+    else:
+        load_mode = 2 if (not fp8 and T > 2 * num_cus) else 1
     two_launch = bool(dec.last[5])
     avg_dec_s = float(dec_ms.mean()) * 1e-3
     achieved = kv_bytes / avg_dec_s / 1e9
@@ -289,12 +295,8 @@ def main():
                                  "kv_dtype": args.kv_dtype,
                                  "mode": ["split", "workqueue"][mode], "param": param,
                                  "merge": "two-launch" if two_launch else "fused"}),
-            # the library streams the pages with the nt cache policy when the
-            # plan has at least 7/8 as many tasks as the GPU has CUs (2-byte
-            # pools at d = 256 excepted)
             "kernel": f"pkv_decode_kernel<{cfg.D}, {'true' if B <= 1024 else 'false'}, _Float16, "
-                      f"{'pkv::Fp8E4M3' if args.kv_dtype == 'fp8' else '_Float16'}, false, "
-                      f"{'true' if nt_loads else 'false'}>",
+                      f"{'pkv::Fp8E4M3' if fp8 else '_Float16'}, false, {load_mode}>",
             "event_windows": len(events),
             "launches_per_event_window": win,
             "algorithmic_bytes_per_launch": kv_bytes,

@@ -260,22 +260,29 @@ constexpr int kCoherent = 17;   // sc0 | sc1
 
 // Cache policy of the page loads.  A step reads every K/V tile exactly once.
 // With the nt (non-temporal, streaming) bit, a grid that keeps every CU busy
-// streams the pools faster (B64 at d = 128: 5.8 -> 6.4 TB/s with fp16, 5.6 ->
-// 5.9 TB/s with fp8), but one workgroup alone on its CU streams slower (about
-// 28 instead of 34 GB/s), so a plan with fewer tasks than about 7/8 of the
-// CUs keeps the default policy, and so do 2-byte pools at d = 256 (one
-// workgroup per CU, 8 KiB tiles: about 7% slower with the bit, while fp8
-// pools at d = 256 gain about 6%).  The loads must be wide: fp8 K rows read
-// in 8-byte pieces streamed far slower with the bit (B64: 833 -> 1066 us),
-// hence the 16-byte K loads of load_page.
+// streams the pools faster, but one workgroup alone on its CU streams slower
+// (about 28 instead of 34 GB/s).  Measured at the best plan of each workload,
+// the modes (kLoadMode) are:
+//   0  default policy for K and V: plans with fewer tasks than about 7/8 of
+//      the CUs, and 2-byte pools at d = 256 (one workgroup per CU, 8 KiB
+//      tiles: about 7% slower with the bit);
+//   1  nt on the V loads only: every other plan, except
+//   2  nt on K and V: 2-byte pools whose plan runs more than two tasks per
+//      CU (fp16 B32: 408 against 428 us with V alone).
+// With V alone, B8 bimodal at d = 128 takes 47.5 instead of 48.5 us (both)
+// and 51 us (neither), and B8 uniform 77 instead of 82 us (both).  The loads
+// must be wide: fp8 K rows read in 8-byte pieces streamed far slower with the
+// bit (B64: 833 -> 1066 us), hence the 16-byte K loads of load_page.
 constexpr int kStream = 2;   // nt
 constexpr int kDefault = 0;
 
 // num_tasks < 0: not known on the host (a self-planned step).
-inline bool streaming_loads(int head_dim, int dtype, int64_t num_tasks, int num_cus) {
+inline int load_mode(int head_dim, int dtype, int64_t num_tasks, int num_cus) {
   const bool fp8 = dtype == PKV_DTYPE_F16_KV_FP8 || dtype == PKV_DTYPE_BF16_KV_FP8;
-  if (head_dim == 256 && !fp8) return false;
-  return num_tasks < 0 || 8 * num_tasks >= 7 * static_cast<int64_t>(num_cus);
+  if (head_dim == 256 && !fp8) return 0;
+  if (num_tasks < 0) return 1;
+  if (8 * num_tasks < 7 * static_cast<int64_t>(num_cus)) return 0;
+  return (!fp8 && num_tasks > 2 * static_cast<int64_t>(num_cus)) ? 2 : 1;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -299,7 +306,7 @@ __device__ __forceinline__ constexpr int k_chunk(int kk, int grp) {
 // elements at d = VW*col (byte offset voff + e*D*j with voff =
 // e*(4*grp*D + VW*col), e bytes per element): each V instruction reads 4
 // whole rows of the contiguous page tile.
-template <int D, class E, class KV, int kCpol>
+template <int D, class E, class KV, int kKCpol, int kVCpol>
 __device__ __forceinline__ void load_page(PageRegs<D, E, KV>& r, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, int koff, int voff) {
   constexpr int KK = D / 32;
@@ -309,7 +316,7 @@ __device__ __forceinline__ void load_page(PageRegs<D, E, KV>& r, __amdgpu_buffer
 #pragma unroll
     for (int kk = 0; kk < KK; kk += 2) {
       const uint4x w = __builtin_bit_cast(
-          uint4x, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 32 * kk, 0, kCpol));
+          uint4x, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 32 * kk, 0, kKCpol));
       r.k[kk] = uint2x{w[0], w[1]};
       r.k[kk + 1] = uint2x{w[2], w[3]};
     }
@@ -317,34 +324,34 @@ __device__ __forceinline__ void load_page(PageRegs<D, E, KV>& r, __amdgpu_buffer
     for (int j = 0; j < 4; ++j) {
       if constexpr (VW == 16)
         r.v[j] = __builtin_bit_cast(
-            uint4x, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + D * j, 0, kCpol));
+            uint4x, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + D * j, 0, kVCpol));
       else if constexpr (VW == 8)
         r.v[j] = __builtin_bit_cast(
-            uint2x, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + D * j, 0, kCpol));
+            uint2x, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + D * j, 0, kVCpol));
       else
-        r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff + D * j, 0, kCpol);
+        r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff + D * j, 0, kVCpol);
     }
   } else {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       r.k[kk] = __builtin_bit_cast(
-          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, kCpol));
+          vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kk, 0, kKCpol));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (VW == 16) {
         const vecE<E, 8> lo = __builtin_bit_cast(
-            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, kCpol));
+            vecE<E, 8>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, kVCpol));
         const vecE<E, 8> hi = __builtin_bit_cast(
             vecE<E, 8>,
-            __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, kCpol));
+            __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j + 16, 0, kVCpol));
         r.v[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
                                          14, 15);
       } else if constexpr (VW == 8) {
         r.v[j] = __builtin_bit_cast(
-            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, kCpol));
+            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 2 * D * j, 0, kVCpol));
       } else {
         r.v[j] = __builtin_bit_cast(
-            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, kCpol));
+            vecE<E, VW>, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 2 * D * j, 0, kVCpol));
       }
     }
   }
@@ -890,7 +897,7 @@ __device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_
 
 // Two workgroups per CU at d <= 128 (256 VGPRs each); one at d = 256, whose
 // larger tiles and accumulators need the AGPR half of the register file.
-template <int D, bool kStaged, class E, class KV, bool kSelfPlan, bool kNt>
+template <int D, bool kStaged, class E, class KV, bool kSelfPlan, int kLoadMode>
 __global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
 pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
@@ -1108,8 +1115,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const int64_t off = static_cast<int64_t>(m.g) * tile_elems * kKvb +
                         (live ? static_cast<int64_t>(e) * stride_bytes : 0);
     const uint32_t bytes = live ? kTileBytes : 0u;
-    load_page<D, E, KV, kNt ? kStream : kDefault>(r, make_rsrc(kpool + off, bytes),
-                                                  make_rsrc(vpool + off, bytes), koff, voff);
+    load_page<D, E, KV, kLoadMode == 2 ? kStream : kDefault, kLoadMode >= 1 ? kStream : kDefault>(
+        r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff, voff);
     return live;
   };
   // q of task m (B operand of the score MFMA, column = head within the
@@ -1441,32 +1448,33 @@ int num_cus_of_current_device(int* cus) {
 // ev0 / ev1 (optional): events that take the decode kernel's own start and
 // end timestamps (hipExtLaunchKernel), for timing it without the queue time
 // of separately recorded events.
-// kNt: page loads with the streaming cache policy (streaming_loads).
-template <int D, class E, class KV, bool kNt>
-int launch_nt(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
+// kMode: cache policy of the page loads (load_mode).
+template <int D, class E, class KV, int kMode>
+int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
               bool decode, hipEvent_t ev0, hipEvent_t ev1) {
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     const bool staged = da.B <= kRowStage;
     if (da.plan_out) {   // self-planned step (staged rows only; checked by the caller)
-      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true, kNt>), dim3(grid),
-                         dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
-                         da.split_offsets);
+      // (load_mode never gives mode 2 to a self-planned step)
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true, kMode == 2 ? 1 : kMode>),
+                         dim3(grid), dim3(kThreads), 0, stream, da, tasks, da.block_table,
+                         da.seq_lens, da.split_offsets);
     } else if (ev0 || ev1) {
       if (staged)
-        hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kNt>), dim3(grid),
+        hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
                               dim3(kThreads), 0, stream, ev0, ev1, 0, da, tasks, da.block_table,
                               da.seq_lens, da.split_offsets);
       else
-        hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kNt>), dim3(grid),
+        hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kMode>), dim3(grid),
                               dim3(kThreads), 0, stream, ev0, ev1, 0, da, tasks, da.block_table,
                               da.seq_lens, da.split_offsets);
     } else if (staged) {
-      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kNt>), dim3(grid),
+      hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
                          dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
                          da.split_offsets);
     } else {
-      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kNt>), dim3(grid),
+      hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kMode>), dim3(grid),
                          dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
                          da.split_offsets);
     }
@@ -1496,33 +1504,42 @@ int launch_nt(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t s
 
 template <int D, class E, class KV>
 int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream, bool decode,
-           bool nt, hipEvent_t ev0, hipEvent_t ev1) {
-  return nt ? launch_nt<D, E, KV, true>(da, ma, grid, stream, decode, ev0, ev1)
-            : launch_nt<D, E, KV, false>(da, ma, grid, stream, decode, ev0, ev1);
+           int mode, hipEvent_t ev0, hipEvent_t ev1) {
+  // Only the modes load_mode can give this pool type and head dimension are
+  // compiled: mode 0 alone for 2-byte pools at d = 256, no mode 2 for fp8.
+  constexpr bool kFp8 = kv_bytes<KV>() == 1;
+  if constexpr (D == 256 && !kFp8) {
+    return launch_mode<D, E, KV, 0>(da, ma, grid, stream, decode, ev0, ev1);
+  } else {
+    if (!kFp8 && mode == 2)
+      return launch_mode<D, E, KV, kFp8 ? 1 : 2>(da, ma, grid, stream, decode, ev0, ev1);
+    return mode >= 1 ? launch_mode<D, E, KV, 1>(da, ma, grid, stream, decode, ev0, ev1)
+                     : launch_mode<D, E, KV, 0>(da, ma, grid, stream, decode, ev0, ev1);
+  }
 }
 
 template <class E, class KV>
 int launch_d(int head_dim, const DecodeArgs& da, const MergeArgs& ma, int grid,
-             hipStream_t stream, bool decode, bool nt, hipEvent_t ev0, hipEvent_t ev1) {
-  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode, nt, ev0, ev1);
-  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode, nt, ev0, ev1)
-                         : launch<64, E, KV>(da, ma, grid, stream, decode, nt, ev0, ev1);
+             hipStream_t stream, bool decode, int mode, hipEvent_t ev0, hipEvent_t ev1) {
+  if (head_dim == 256) return launch<256, E, KV>(da, ma, grid, stream, decode, mode, ev0, ev1);
+  return head_dim == 128 ? launch<128, E, KV>(da, ma, grid, stream, decode, mode, ev0, ev1)
+                         : launch<64, E, KV>(da, ma, grid, stream, decode, mode, ev0, ev1);
 }
 
 // The kernels of one head dimension and element-type pair (both checked by
 // the caller).
 int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& ma, int grid,
-               hipStream_t stream, bool decode, bool nt, hipEvent_t ev0 = nullptr,
+               hipStream_t stream, bool decode, int mode, hipEvent_t ev0 = nullptr,
                hipEvent_t ev1 = nullptr) {
   switch (dtype) {
     case PKV_DTYPE_BF16:
-      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
+      return launch_d<__bf16, __bf16>(head_dim, da, ma, grid, stream, decode, mode, ev0, ev1);
     case PKV_DTYPE_F16_KV_FP8:
-      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
+      return launch_d<_Float16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, mode, ev0, ev1);
     case PKV_DTYPE_BF16_KV_FP8:
-      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
+      return launch_d<__bf16, Fp8E4M3>(head_dim, da, ma, grid, stream, decode, mode, ev0, ev1);
     default:
-      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode, nt, ev0, ev1);
+      return launch_d<_Float16, _Float16>(head_dim, da, ma, grid, stream, decode, mode, ev0, ev1);
   }
 }
 
@@ -1659,12 +1676,12 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
     do_merge = false;
   }
   int grid = 1;
-  bool nt = false;
+  int load = 0;
   if (do_decode) {
     int cus = 0;
     st = pkv::num_cus_of_current_device(&cus);
     if (st != PKV_OK) return st;
-    nt = pkv::streaming_loads(head_dim, dtype, num_tasks, cus);
+    load = pkv::load_mode(head_dim, dtype, num_tasks, cus);
     // as many workgroups as fit at once (persistent: a workgroup that had to
     // wait for a slot would hold its static tasks until the others finish)
     int64_t g = static_cast<int64_t>(cus) * (head_dim == 256 ? 1 : 2);
@@ -1677,7 +1694,7 @@ int run(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool decode = da.num_tasks > 0;
   da.task_cap = da.num_tasks > 0 ? da.num_tasks : 1;
-  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode, nt,
+  return pkv::launch_any(head_dim, dtype, da, ma, grid, s, decode, load,
                          static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1));
 }
 
@@ -1884,7 +1901,7 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   const int grid = num_cus;
   if (max_splits <= pol.fuse_max_splits && pa.groups_fit) ma.B = 0;
   return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true,
-                         pkv::streaming_loads(head_dim, dtype, -1, num_cus));
+                         pkv::load_mode(head_dim, dtype, -1, num_cus));
 }
 
 int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,

@@ -53,14 +53,14 @@ int pkv_policy_defaults(pkv_policy_params* p) {
   p->fuse_max_splits = 16;
   // Fitted on the calibration seed (paged_gqa_decode_pkv_amd/calibration/
   // mi355x_fit.json, written by policy_fit.py from calibrate.py's runs).
-  p->t0_us = 0.2777;
-  p->t_round_us = 5.491;
-  p->alpha = 0.8341;
-  p->cu_gbps = 45.85;
-  p->hbm_gbps = 8292.0;
-  p->t_two_us = 6.975;
-  p->t_two_split_us = 0.0218;
-  p->t_fused_split_us = 0.2892;
+  p->t0_us = 0.0;
+  p->t_round_us = 5.775;
+  p->alpha = 1.121;
+  p->cu_gbps = 45.47;
+  p->hbm_gbps = 8928.0;
+  p->t_two_us = 6.86;
+  p->t_two_split_us = 0.02178;
+  p->t_fused_split_us = 0.285;
   return PKV_OK;
 }
 
