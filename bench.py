@@ -231,7 +231,7 @@ def main():
     # the page loads' cache policy the library picks for this plan (0: default,
     # 1: nt on V, 2: nt on K and V)
     fp8 = args.kv_dtype == "fp8"
-    if (cfg.D == 256 and not fp8) or 8 * T < 7 * num_cus:
+    if cfg.D == 256 and not fp8:
         load_mode = 0
     else:
         load_mode = 2 if (not fp8 and T > 2 * num_cus) else 1

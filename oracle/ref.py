@@ -251,9 +251,9 @@ def split_merge(q, k_pool, v_pool, block_table, seq_lens, scale, tasks, split_of
 # fitted on the calibration seed (the library's pkv_policy_defaults; a test
 # checks the two against the committed fit).
 POLICY_DEFAULTS = dict(split_max=256, chunk_min=4, chunk_max=256, fuse_max_splits=16,
-                       t0_us=0.0, t_round_us=5.775, alpha=1.121, cu_gbps=45.47,
-                       hbm_gbps=8928.0, t_two_us=6.86, t_two_split_us=0.02178,
-                       t_fused_split_us=0.285)
+                       t0_us=0.0, t_round_us=5.726, alpha=1.097, cu_gbps=46.64,
+                       hbm_gbps=8865.0, t_two_us=6.631, t_two_split_us=0.02415,
+                       t_fused_split_us=0.2848)
 
 
 def plan_shape(seq_lens, Hkv, page_size, mode, param):

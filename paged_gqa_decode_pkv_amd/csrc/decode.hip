@@ -258,21 +258,21 @@ constexpr int kRsrcDword3 = 0x00020000;
 // write back or invalidate a whole L2.
 constexpr int kCoherent = 17;   // sc0 | sc1
 
-// Cache policy of the page loads.  A step reads every K/V tile exactly once.
-// With the nt (non-temporal, streaming) bit, a grid that keeps every CU busy
-// streams the pools faster, but one workgroup alone on its CU streams slower
-// (about 28 instead of 34 GB/s).  Measured at the best plan of each workload,
-// the modes (kLoadMode) are:
-//   0  default policy for K and V: plans with fewer tasks than about 7/8 of
-//      the CUs, and 2-byte pools at d = 256 (one workgroup per CU, 8 KiB
-//      tiles: about 7% slower with the bit);
-//   1  nt on the V loads only: every other plan, except
-//   2  nt on K and V: 2-byte pools whose plan runs more than two tasks per
-//      CU (fp16 B32: 408 against 428 us with V alone).
-// With V alone, B8 bimodal at d = 128 takes 47.5 instead of 48.5 us (both)
-// and 51 us (neither), and B8 uniform 77 instead of 82 us (both).  The loads
-// must be wide: fp8 K rows read in 8-byte pieces streamed far slower with the
-// bit (B64: 833 -> 1066 us), hence the 16-byte K loads of load_page.
+// Cache policy of the page loads.  A step reads every K/V tile exactly once,
+// and the nt (non-temporal, streaming) bit makes the V loads faster on every
+// plan measured: with it, B8 bimodal at d = 128 takes 47.5 instead of 51 us,
+// B8 Zipf at c = 256 (208 tasks) 70 instead of 75 us.  On the K loads it
+// pays only where a 2-byte pool's plan runs more than two tasks per CU (fp16
+// B32: 408 against 428 us with V alone) and costs elsewhere (B8 uniform: 82
+// against 77 us).  2-byte pools at d = 256 (one workgroup per CU, 8 KiB
+// tiles) stream about 7% slower with the bit.  The modes (kLoadMode):
+//   0  default policy for K and V: 2-byte pools at d = 256;
+//   1  nt on the V loads: every other plan, except
+//   2  nt on K and V: 2-byte pools whose plan has more tasks than twice the
+//      CUs.
+// The loads must be wide: fp8 K rows read in 8-byte pieces streamed far
+// slower with the bit (B64: 833 -> 1066 us), hence the 16-byte K loads of
+// load_page.
 constexpr int kStream = 2;   // nt
 constexpr int kDefault = 0;
 
@@ -280,8 +280,6 @@ constexpr int kDefault = 0;
 inline int load_mode(int head_dim, int dtype, int64_t num_tasks, int num_cus) {
   const bool fp8 = dtype == PKV_DTYPE_F16_KV_FP8 || dtype == PKV_DTYPE_BF16_KV_FP8;
   if (head_dim == 256 && !fp8) return 0;
-  if (num_tasks < 0) return 1;
-  if (8 * num_tasks < 7 * static_cast<int64_t>(num_cus)) return 0;
   return (!fp8 && num_tasks > 2 * static_cast<int64_t>(num_cus)) ? 2 : 1;
 }
 
@@ -1506,15 +1504,15 @@ template <int D, class E, class KV>
 int launch(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream, bool decode,
            int mode, hipEvent_t ev0, hipEvent_t ev1) {
   // Only the modes load_mode can give this pool type and head dimension are
-  // compiled: mode 0 alone for 2-byte pools at d = 256, no mode 2 for fp8.
+  // compiled: 0 for 2-byte pools at d = 256, 1 for fp8 pools, 1 or 2 else.
   constexpr bool kFp8 = kv_bytes<KV>() == 1;
   if constexpr (D == 256 && !kFp8) {
     return launch_mode<D, E, KV, 0>(da, ma, grid, stream, decode, ev0, ev1);
+  } else if constexpr (kFp8) {
+    return launch_mode<D, E, KV, 1>(da, ma, grid, stream, decode, ev0, ev1);
   } else {
-    if (!kFp8 && mode == 2)
-      return launch_mode<D, E, KV, kFp8 ? 1 : 2>(da, ma, grid, stream, decode, ev0, ev1);
-    return mode >= 1 ? launch_mode<D, E, KV, 1>(da, ma, grid, stream, decode, ev0, ev1)
-                     : launch_mode<D, E, KV, 0>(da, ma, grid, stream, decode, ev0, ev1);
+    return mode == 2 ? launch_mode<D, E, KV, 2>(da, ma, grid, stream, decode, ev0, ev1)
+                     : launch_mode<D, E, KV, 1>(da, ma, grid, stream, decode, ev0, ev1);
   }
 }
 

@@ -54,13 +54,13 @@ int pkv_policy_defaults(pkv_policy_params* p) {
   // Fitted on the calibration seed (paged_gqa_decode_pkv_amd/calibration/
   // mi355x_fit.json, written by policy_fit.py from calibrate.py's runs).
   p->t0_us = 0.0;
-  p->t_round_us = 5.775;
-  p->alpha = 1.121;
-  p->cu_gbps = 45.47;
-  p->hbm_gbps = 8928.0;
-  p->t_two_us = 6.86;
-  p->t_two_split_us = 0.02178;
-  p->t_fused_split_us = 0.285;
+  p->t_round_us = 5.726;
+  p->alpha = 1.097;
+  p->cu_gbps = 46.64;
+  p->hbm_gbps = 8865.0;
+  p->t_two_us = 6.631;
+  p->t_two_split_us = 0.02415;
+  p->t_fused_split_us = 0.2848;
   return PKV_OK;
 }
 
