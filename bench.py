@@ -228,13 +228,11 @@ def main():
     dec_ms = np.array([e0.elapsed_time(e1) / win for e0, e1 in events])
     mode, param, T, nslots = dec.last[:4]
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
-    # the page loads' cache policy the library picks for this plan (0: default,
-    # 1: nt on V, 2: nt on K and V)
+    # the page loads' cache policy the library gives this plan (0: default,
+    # 1: non-temporal V loads, 2: non-temporal K and V loads)
     fp8 = args.kv_dtype == "fp8"
-    if cfg.D == 256 and not fp8:
-        load_mode = 0
-    else:
-        load_mode = 2 if (not fp8 and T > 2 * num_cus) else 1
+    load_mode = pkv.pkv_page_load_mode(cfg.D, pkv.PKV_DTYPE_F16_KV_FP8 if fp8 else pkv.PKV_DTYPE_F16,
+                                       T, num_cus)
     two_launch = bool(dec.last[5])
     avg_dec_s = float(dec_ms.mean()) * 1e-3
     achieved = kv_bytes / avg_dec_s / 1e9

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 /* Fixed-size head of every workspace: control words (task counter, exit
  * counter, error word) and the per-(row, KV head) arrival counters of the
@@ -124,6 +124,21 @@ typedef struct pkv_policy_params {
 
 /* ABI version (PKV_ABI_VERSION of the built library). */
 int pkv_abi_version(void);
+
+/*
+ * Cache policy the decode kernel gives its K/V page loads for a plan (a
+ * performance choice of the library; results do not depend on it):
+ *   0  default for K and V (2-byte pools at head_dim 256);
+ *   1  non-temporal (streaming) V loads: every other plan, except
+ *   2  non-temporal K and V loads: 2-byte pools whose plan has more than
+ *      2 * num_cus tasks.
+ * num_tasks < 0 asks for a self-planned step (pkv_decode_device_plan).
+ * Host only; no device is touched.  PKV_ERR_INVALID_ARG for a NULL `mode`,
+ * num_cus < 1 or an unknown dtype, PKV_ERR_UNSUPPORTED for a head_dim outside
+ * {64, 128, 256}.
+ */
+int pkv_page_load_mode(int32_t head_dim, int32_t dtype, int64_t num_tasks, int32_t num_cus,
+                       int32_t* mode);
 
 /* Static, human-readable text of a status code.  Never NULL. */
 const char* pkv_status_string(int status);
@@ -364,19 +379,20 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
  * step onto the GPU.)
  *
  * Source: gist.science explainer, "Row-Local Bounds", "Compact Workqueue" and
- * "2. Calibrated Adaptive Policy".  Three launches on `stream`:
- *   1. a one-workgroup planner kernel: with mode = -1 it picks (mode, param)
- *      exactly as pkv_policy would with `policy` limited to the capacity
- *      (split_max <= max_splits; workqueue chunks c with
- *      ceil(max_pages_per_row / c) <= max_splits); then it writes the same
- *      split_offsets and task records as pkv_plan, and a header;
- *   2. the persistent decode kernel, num_cus workgroups, reading the task
- *      count from the header;
- *   3. the merge kernel, which returns at once when the header says the
+ * "2. Calibrated Adaptive Policy".  The plan: with mode = -1, (mode, param)
+ * exactly as pkv_policy would pick them with `policy` limited to the capacity
+ * (split_max <= max_splits; workqueue chunks c with ceil(max_pages_per_row /
+ * c) <= max_splits); then the same split_offsets and task records as pkv_plan,
+ * and a header.  Launches on `stream`:
+ *   B <= 1024: the persistent decode kernel (num_cus workgroups), every
+ *      workgroup planning for itself from the lengths it stages (workgroup 0
+ *      writes the plan out for pkv_device_plan_read);
+ *   B > 1024: a one-workgroup planner kernel, then the decode kernel reading
+ *      the task count from the header;
+ *   then, unless max_splits <= fuse_max_splits (every plan is then fused),
+ *      the merge kernel, which returns at once when the header says the
  *      decode kernel merged (the fused form: no row deeper than
- *      policy->fuse_max_splits and B * Hkv <= PKV_MAX_FUSED_GROUPS).  It is
- *      not launched when max_splits <= fuse_max_splits (every plan is then
- *      fused): two launches per step.
+ *      policy->fuse_max_splits and B * Hkv <= PKV_MAX_FUSED_GROUPS).
  * Arguments as for pkv_decode, except:
  *   seq_lens     device int32 [B]; a row with N_b < 0 or needing more than
  *                max_pages_per_row pages is planned as empty (out = 0,

@@ -19,7 +19,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-PKV_ABI_VERSION = 4               # include/pkv.h; the argument lists below follow it
+PKV_ABI_VERSION = 5               # include/pkv.h; the argument lists below follow it
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = 1
 PKV_ERR_UNSUPPORTED = 2
@@ -44,7 +44,8 @@ WORKSPACE_HEADER_BYTES = 65536      # PKV_WORKSPACE_HEADER_BYTES
 
 # Every symbol include/pkv.h declares.
 ABI_SYMBOLS = (
-    "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_policy_defaults",
+    "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_page_load_mode",
+    "pkv_policy_defaults",
     "pkv_policy", "pkv_policy_predict", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
     "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_splits", "pkv_merge",
     "pkv_workspace_size_device_plan", "pkv_decode_device_plan", "pkv_device_plan_read",
@@ -112,6 +113,7 @@ def _load():
         "pkv_abi_version": ([], ctypes.c_int),
         "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "pkv_last_hip_error": ([], ctypes.c_int),
+        "pkv_page_load_mode": ([i32, i32, i64, i32, _i32p], ctypes.c_int),
         "pkv_policy_defaults": ([ctypes.POINTER(pkv_policy_params)], ctypes.c_int),
         "pkv_policy": ([_vp, i32, i32, i32, i32, i32, ctypes.POINTER(pkv_policy_params), _i32p,
                         _i32p],
@@ -184,6 +186,16 @@ def pkv_status_string(status: int) -> str:
 
 def pkv_last_hip_error() -> int:
     return _load().pkv_last_hip_error()
+
+
+def pkv_page_load_mode(head_dim: int, dtype: int, num_tasks: int, num_cus: int) -> int:
+    """Cache policy of the decode kernel's page loads for a plan: 0 default,
+    1 non-temporal V loads, 2 non-temporal K and V loads (num_tasks < 0: a
+    self-planned step); see pkv_page_load_mode in include/pkv.h."""
+    mode = ctypes.c_int32()
+    _check(_load().pkv_page_load_mode(head_dim, dtype, num_tasks, num_cus, ctypes.byref(mode)),
+           "pkv_page_load_mode")
+    return mode.value
 
 
 def pkv_policy_defaults() -> pkv_policy_params:

@@ -1545,6 +1545,15 @@ int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& m
 
 extern "C" {
 
+int pkv_page_load_mode(int32_t head_dim, int32_t dtype, int64_t num_tasks, int32_t num_cus,
+                       int32_t* mode) {
+  if (!mode || num_cus < 1 || dtype < PKV_DTYPE_F16 || dtype > PKV_DTYPE_BF16_KV_FP8)
+    return PKV_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKV_ERR_UNSUPPORTED;
+  *mode = pkv::load_mode(head_dim, dtype, num_tasks < 0 ? -1 : num_tasks, num_cus);
+  return PKV_OK;
+}
+
 int pkv_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || workspace_bytes < PKV_WORKSPACE_HEADER_BYTES) return PKV_ERR_INVALID_ARG;
   hipError_t e = hipMemsetAsync(workspace, 0, PKV_WORKSPACE_HEADER_BYTES,

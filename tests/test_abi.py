@@ -38,6 +38,30 @@ def test_version_and_status_strings():
     assert pkv.pkv_status_string(99) == "unknown status"
 
 
+def test_page_load_mode_rule():
+    """The cache policy of the page loads, a host-side choice per plan: the
+    default for 2-byte pools at d = 256, non-temporal K and V for 2-byte plans
+    of more than two tasks per CU, non-temporal V otherwise (also for a
+    self-planned step, num_tasks < 0)."""
+    F16, BF16, F8, BF8 = (pkv.PKV_DTYPE_F16, pkv.PKV_DTYPE_BF16, pkv.PKV_DTYPE_F16_KV_FP8,
+                          pkv.PKV_DTYPE_BF16_KV_FP8)
+    cases = [
+        ((128, F16, 1, 256), 1), ((128, F16, 256, 256), 1), ((128, F16, 512, 256), 1),
+        ((128, F16, 513, 256), 2), ((128, BF16, 4752, 256), 2), ((64, F16, 2472, 256), 2),
+        ((128, F8, 4752, 256), 1), ((64, BF8, 100000, 256), 1), ((256, F8, 4752, 256), 1),
+        ((256, F16, 4752, 256), 0), ((256, BF16, 10, 256), 0),
+        ((128, F16, -1, 256), 1), ((256, BF16, -1, 256), 0), ((128, F16, 513, 304), 1),
+    ]
+    for args, want in cases:
+        assert pkv.pkv_page_load_mode(*args) == want, args
+    for args, status in [((96, F16, 10, 256), pkv.PKV_ERR_UNSUPPORTED),
+                         ((128, 7, 10, 256), pkv.PKV_ERR_INVALID_ARG),
+                         ((128, F16, 10, 0), pkv.PKV_ERR_INVALID_ARG)]:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_page_load_mode(*args)
+        assert e.value.status == status
+
+
 def test_constants_agree_with_oracle():
     assert pkv.PKV_MODE_SPLIT == oracle.MODE_SPLIT
     assert pkv.PKV_MODE_WORKQUEUE == oracle.MODE_WORKQUEUE
