@@ -499,8 +499,9 @@ def pkv_runner_last_plan(runner):
 
 class PagedDecoder:
     """Decode steps through the native runner: one library call per step runs
-    policy -> host plan -> async plan upload -> decode kernel -> merge kernel on
-    the current stream.
+    policy -> host plan -> decode kernel (-> merge kernel in the two-launch
+    form) on the given stream; the kernels read a new plan from the runner's
+    pinned memory and a repeated one from its device copy.
 
     The decoder owns the workspace (a torch allocation, grown on demand) and a
     runner, whose pinned plan ring the kernels read in place.  The argument
