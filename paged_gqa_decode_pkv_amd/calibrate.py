@@ -40,14 +40,14 @@ SPLITS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 CHUNKS = (4, 8, 16, 32, 64, 128, 256)
 
 
-def measure_config(name: str, seed: int, steps: int, out_f):
+def measure_config(name: str, seed: int, steps: int, out_f, dtype: str = "f16"):
     import torch
 
     import paged_gqa_decode_pkv_amd as pkv
     from workloads import CONFIGS, make_workload
 
     cfg = CONFIGS[name]
-    wl = make_workload(cfg, seed, device="cuda", fill="zero")
+    wl = make_workload(cfg, seed, device="cuda", fill="zero", dtype=dtype)
     B = cfg.B
     L = max(1, min(16, -(-2 * 2 ** 30 // max(wl.kv_bytes, 1))))
     pools = [(wl.k_pool, wl.v_pool)] + [(wl.k_pool.clone(), wl.v_pool.clone())
@@ -100,6 +100,7 @@ def measure_config(name: str, seed: int, steps: int, out_f):
             "step_us_max": round(float(np.max(reps)), 3),
             "layers": L, "steps": n, "error_flags": errs,
             "kv_bytes": int(wl.kv_bytes),
+            "dtype": dtype,
         }
         out_f.write(json.dumps(rec) + "\n")
         out_f.flush()
@@ -116,12 +117,14 @@ def main(argv=None):
     ap.add_argument("--seeds", nargs="*", type=int,
                     default=[CALIBRATION_SEED] + list(HELD_OUT_SEEDS))
     ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--dtype", default="f16", choices=("f16", "bf16", "fp8", "bf16_fp8"),
+                    help="element types of q/out and the pools (workloads.make_workload)")
     args = ap.parse_args(argv)
     with open(args.out, "a") as f:
         for name in args.configs:
             for seed in args.seeds:
                 t0 = time.perf_counter()
-                measure_config(name, seed, args.steps, f)
+                measure_config(name, seed, args.steps, f, args.dtype)
                 print(f"[calibrate] {name} seed {seed}: {time.perf_counter() - t0:.1f} s",
                       flush=True)
 

@@ -113,8 +113,10 @@ def pick(x, lens, Hkv, cus, head_dim):
 
 def compact_runs(jsonl_path):
     runs = defaultdict(dict)
+    dtypes = set()
     for line in open(jsonl_path):
         r = json.loads(line)
+        dtypes.add(r.get("dtype", "f16"))
         key = r["config"]
         d = runs[key].setdefault(str(r["seed"]), {"lens": r["lens"], "runs": [], "rule": None})
         row = [r["mode"], r["param"], int(r["two_launch"]), r["num_tasks"], r["max_splits"],
@@ -123,7 +125,13 @@ def compact_runs(jsonl_path):
             d["rule"] = row
         else:
             d["runs"].append(row)
-    return {"device": "1x MI355X (gfx950), 256 CUs", "Hkv": 8, "head_dim": 128, "cus": 256,
+    assert len(dtypes) == 1, dtypes
+    dtype = dtypes.pop()
+    # fp8 pools: the model sees half the head dimension (the same bytes per
+    # tile), as the runner passes it
+    head_dim = 64 if dtype in ("fp8", "bf16_fp8") else 128
+    return {"device": "1x MI355X (gfx950), 256 CUs", "Hkv": 8, "head_dim": head_dim, "cus": 256,
+            "dtype": dtype,
             "columns": ["mode", "param", "two_launch", "num_tasks", "max_splits", "step_us"],
             "command": "python -m paged_gqa_decode_pkv_amd.calibrate --out RUNS.jsonl",
             "traces": runs}
@@ -227,9 +235,11 @@ def main(argv=None):
     ap.add_argument("--runs", help="compacted runs (calibration/mi355x_runs.json)")
     ap.add_argument("--revalidate", action="store_true",
                     help="judge the committed constants on the runs in JSONL (no new fit)")
+    ap.add_argument("--name", default="mi355x_revalidation.json",
+                    help="output file (in calibration/) of --revalidate")
     args = ap.parse_args(argv)
     if args.revalidate:
-        s = revalidate(args.jsonl)
+        s = revalidate(args.jsonl, args.name)
         print({k: v for k, v in s.items() if k not in ("rows", "runs")})
         return 0
     if args.jsonl:
