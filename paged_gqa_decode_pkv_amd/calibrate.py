@@ -22,7 +22,8 @@ plus the step the policy picks by itself.  The time kept per candidate is
            The median over 5 repetitions of the K steps is kept.
 
 Output: one JSON object per line.  ``python -m paged_gqa_decode_pkv_amd.calibrate
---out FILE`` (GPU required).  The fit of the policy's constants from these
+--out FILE [--dtype f16|bf16|fp8|bf16_fp8]`` (GPU required; the constants are
+fitted on fp16 runs, other element types serve to judge them).  The fit of the policy's constants from these
 measurements is done by ``policy_fit.py`` on the CPU.
 """
 from __future__ import annotations

@@ -14,8 +14,10 @@ thresholds fixed on a calibration seed and then evaluated on held-out seeds
            (picked / best); also the regret of the runner's own pick during the
            runs (the policy the library held when they were taken)
 
-``python -m paged_gqa_decode_pkv_amd.policy_fit --revalidate RUNS.jsonl`` judges the
-committed constants on fresh runs instead (``calibration/mi355x_revalidation.json``).
+``python -m paged_gqa_decode_pkv_amd.policy_fit --revalidate RUNS.jsonl [--name F]``
+judges the committed constants on fresh runs instead (``calibration/F``, by default
+``mi355x_revalidation.json``; fp8-pool runs are judged with the model fed half the
+head dimension, as the runner does).
 ``python -m paged_gqa_decode_pkv_amd.policy_fit RUNS.jsonl`` writes
 ``calibration/mi355x_runs.json`` (the runs, compacted) and
 ``calibration/mi355x_fit.json`` (constants + evaluation) and prints the table.
