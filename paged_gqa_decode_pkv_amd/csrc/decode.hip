@@ -1059,13 +1059,17 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     if (tid == 0) a.plan_tasks_out[t] = rec;
     return rec;
   };
-  // Staging loads first (vector), then the first task record (scalar), then
-  // the LDS stores: the two load latencies overlap instead of adding up.
+  // The first task record (scalar) is issued first, then the staging loads
+  // (vector), then the LDS stores: the two load latencies overlap instead of
+  // adding up.  The scheduling barrier keeps the compiler from sinking the
+  // record load below the stores, which wait for the staging loads.
   int4 rec0;
   if constexpr (kSelfPlan) {
     rec0 = self_record(blockIdx.x);
   } else if constexpr (kStaged) {
     constexpr int kPer = (kRowStage + kThreads) / kThreads;   // covers B+1 <= kRowStage+1
+    rec0 = load_record(a, tasks_in, blockIdx.x);
+    __builtin_amdgcn_sched_barrier(0);
     int lv[kPer], ov[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -1073,7 +1077,6 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       lv[k] = i < a.B ? seq_lens_in[i] : 0;
       ov[k] = i <= a.B ? offs_in[i] : 0;
     }
-    rec0 = load_record(a, tasks_in, blockIdx.x);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kThreads;
@@ -1142,14 +1145,17 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   PageRegs<D, E, KV> ring[kRing];
   bool valid[kRing];
   {
+    // q is loaded before the pages: vector loads complete in order, so its
+    // wait (and the barrier behind it) does not also wait for the first
+    // round of pages, and every wave starts consuming (and refilling) its
+    // ring as soon as its first page lands.
+    vecE<E, 8> qf[KK];
+    if (wave == 0) load_q(cur, qf);
+    __builtin_amdgcn_sched_barrier(0);
     const Round<kRing> r0 = load_round<kRing>(a, bt_in, cur, wave, 0);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
-    if (wave == 0) {
-      vecE<E, 8> qf[KK];
-      load_q(cur, qf);
-      store_q(cur, qf, s_q[0]);
-    }
+    if (wave == 0) store_q(cur, qf, s_q[0]);
   }
   __syncthreads();
 
@@ -1166,19 +1172,14 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       nxt = load_meta<kStaged, kRing>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off,
                                       num_tasks, t_nxt);
     const Round<kRing> nr0 = load_round<kRing>(a, bt_in, nxt, wave, 0);
-    // Wave 0: the index after next and the next task's q, both to LDS.
-    // Their loads queue behind this task's first round, which the wave has
-    // to wait for next anyway, so the wait costs nothing extra.
-    if (wave == 0) {
-      const bool fetch = t_nxt < num_tasks;
-      uint32_t raw_nn = 0;
-      if (fetch && lane == 0) raw_nn = atomicAdd(a.ctrl, 1u);
-      vecE<E, 8> qn[KK];
-      load_q(nxt, qn);
-      store_q(nxt, qn, s_q[par ^ 1]);
-      if (lane == 0)
-        s_next[par] = fetch ? static_cast<int>(2u * gridDim.x + raw_nn) : num_tasks;
-    }
+    // Wave 0: the index after next (counter atomic, issued now) and the next
+    // task's q (loaded at the start of this task's last round), both stored
+    // to LDS at the end of the last round.  Vector loads complete in order,
+    // so those waits cover only pages already consumed, never the refills
+    // in flight behind them.
+    const bool fetch = t_nxt < num_tasks;
+    uint32_t raw_nn = 0;
+    if (wave == 0 && fetch && lane == 0) raw_nn = atomicAdd(a.ctrl, 1u);
 
     WaveState<D> st;
     st.m = -INFINITY;
@@ -1188,6 +1189,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
 
     for (int j = 0; j < cur.rounds; ++j) {
       const bool last = (j + 1 == cur.rounds);
+      vecE<E, 8> qn[KK];
+      if (last && wave == 0) load_q(nxt, qn);
       const Round<kRing> fr = last ? nr0 : load_round<kRing>(a, bt_in, cur, wave, j + 1);
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
@@ -1201,6 +1204,11 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
           valid[r] = issue(nxt, r, fr.e[r], ring[r]);
         else
           valid[r] = issue(cur, kRing * (j + 1) + r, fr.e[r], ring[r]);
+      }
+      if (last && wave == 0) {
+        store_q(nxt, qn, s_q[par ^ 1]);
+        if (lane == 0)
+          s_next[par] = fetch ? static_cast<int>(2u * gridDim.x + raw_nn) : num_tasks;
       }
     }
 
