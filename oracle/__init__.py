@@ -15,40 +15,34 @@ What it computes is fixed by the PersistentKV pages (arXiv 2606.26666):
     online-softmax states, row-local bounds from the true lengths, and a
     compact list of non-empty (row, KV head, split) tasks (same section, items
     "Sequentie Splitting", "Row-Local Bounds", "Compact Workqueue").
-  * A host policy choosing split or workqueue scheduling from the batch size
-    and lengths, calibrated on one seed and judged on held-out seeds (same
-    page, "2. Calibrated Adaptive Policy" and "Resultaten"); the v2 abstract
-    calls it roofline-style.  Here: a roofline-style time model of each
-    candidate plan (``predict_us``), fastest candidate wins.
+  The schedule (split count, chunk) only decides how the same result is
+    computed, so it has no place here: the task list is computed for any
+    given mode and parameter, and every schedule must reach ``attend``'s
+    result.  (The library's scheduling policy is checked against the pages'
+    mode rule and against a second implementation of its documented model in
+    the tests, not against this package.)
 
 fp8 KV pools (beyond the pages, which use FP16): the values are the OCP E4M3
 codes of the pool times a per-tensor scale (``e4m3_decode``, ``kv_values``),
 decoded from the format's published definition.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   scale = 1/sqrt(d); query head h reads KV head floor(h/G); token t of a row
   lives in page block_table[b, t // 16] at slot t % 16; K and V pools are
   [num_pages, Hkv, 16, d]; a row with N_b = 0 yields out = 0, lse = -inf.
 
 Pins: every function here is checked against something other than itself in
 ``tests/test_oracle_pins.py`` (brute force, closed forms, a library special
-case, invariances) -- except the policy's constants, which are this
-project's own fit to MI355X measurements: parity unpinned for ``policy`` and
-``predict_us`` (``plan_shape`` is pinned against the task list, and the
-policy's structural properties are tested).
+case, invariances).
 """
 from .ref import (  # noqa: F401
     MODE_SPLIT,
     MODE_WORKQUEUE,
-    POLICY_DEFAULTS,
     attend,
     e4m3_decode,
     kv_values,
     merge_states,
     partial_state,
-    plan_shape,
     plan_tasks,
-    policy,
-    predict_us,
     split_merge,
 )

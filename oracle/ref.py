@@ -241,99 +241,3 @@ def split_merge(q, k_pool, v_pool, block_table, seq_lens, scale, tasks, split_of
                 oo = np.concatenate([oo, np.zeros((extra_neutral, D))])
             out[b, h], lse[b, h] = merge_states(mm, ll, oo)
     return out, lse
-
-
-# ---------------------------------------------------------------------------
-# policy
-# ---------------------------------------------------------------------------
-
-# Defaults of the policy: candidate sets and the cost model's constants as
-# fitted on the calibration seed (the library's pkv_policy_defaults; a test
-# checks the two against the committed fit).
-POLICY_DEFAULTS = dict(split_max=256, chunk_min=4, chunk_max=256, fuse_max_splits=16,
-                       t0_us=0.0, t_round_us=5.726, alpha=1.097, cu_gbps=46.64,
-                       hbm_gbps=8865.0, t_two_us=6.631, t_two_split_us=0.02415,
-                       t_fused_split_us=0.2848)
-
-
-def plan_shape(seq_lens, Hkv, page_size, mode, param):
-    """(T, P, pmax, maxS) of the plan plan_tasks would build: tasks, page
-    tiles in all, pages of the largest task, splits of the deepest row."""
-    T = P = pmax = maxS = 0
-    for N in seq_lens:
-        n = -(-int(N) // page_size)
-        if n == 0:
-            continue
-        c = -(-n // param) if mode == MODE_SPLIT else int(param)
-        S = -(-n // c)
-        T += Hkv * S
-        P += Hkv * n
-        pmax = max(pmax, min(c, n))
-        maxS = max(maxS, S)
-    return T, P, pmax, maxS
-
-
-def predict_us(shape, num_cus, head_dim, page_size, two, k):
-    """Roofline-style time of one step for a plan shape (microseconds).
-
-    v2 abstract (fugumt.com): the calibrated policy is "roofline-style".
-    Reading: the step streams every page tile once; it is bound by the
-    slowest CU, which holds its share of the tiles (or, with every task
-    placed statically, its tasks) and streams at the smaller of one CU's
-    rate and its share of the chip's rate; each round of tasks costs a fixed
-    time, and so do the launch and the merge of the deepest row.
-    W = min(T, 2 num_cus) workgroups, A = min(W, num_cus) CUs in use.
-    All in float64, operation by operation.
-    """
-    T, P, pmax, maxS = shape
-    if T == 0:
-        return k["t0_us"]
-    W = min(T, 2 * num_cus)
-    A = min(W, num_cus)
-    rho = min(k["cu_gbps"], k["hbm_gbps"] / A)
-    if T <= W:
-        load = float(-(-T // A) * pmax)
-    else:
-        load = P / A + k["alpha"] * pmax
-    tile = 2.0 * page_size * head_dim * 2.0       # K and V of one page, one KV head
-    t = k["t0_us"] + k["t_round_us"] * (-(-T // W)) + load * tile / (rho * 1e3)
-    if two:
-        t = t + k["t_two_us"] + k["t_two_split_us"] * maxS
-    else:
-        t = t + k["t_fused_split_us"] * maxS
-    return t
-
-
-def policy(seq_lens, Hkv, page_size, num_cus, head_dim=128, **overrides):
-    """Pick (mode, param) for one step.
-
-    "2. Calibrated Adaptive Policy": one long row uses sequence splitting, a
-    batch of 8 or more long rows the compact workqueue, with thresholds
-    calibrated on one seed and judged on held-out seeds ("Resultaten").  The
-    branches that route to another library are not part of this path.
-    Reading: the policy evaluates every candidate -- split mode with
-    S = 1, 2, 4, ... <= split_max, then workqueue mode with
-    c = chunk_min, 2 chunk_min, ... <= chunk_max -- by predict_us (the
-    two-launch term when the deepest row has more than fuse_max_splits
-    splits) and keeps the first fastest.  No active row gives (split, 1).
-    """
-    k = dict(POLICY_DEFAULTS)
-    k.update(overrides)
-    if not any(int(x) > 0 for x in seq_lens):
-        return MODE_SPLIT, 1
-    best = None
-    cands = []
-    S = 1
-    while S <= k["split_max"]:
-        cands.append((MODE_SPLIT, S))
-        S *= 2
-    c = k["chunk_min"]
-    while c <= k["chunk_max"]:
-        cands.append((MODE_WORKQUEUE, c))
-        c *= 2
-    for mode, param in cands:
-        shape = plan_shape(seq_lens, Hkv, page_size, mode, param)
-        t = predict_us(shape, num_cus, head_dim, page_size, shape[3] > k["fuse_max_splits"], k)
-        if best is None or t < best[0]:
-            best = (t, mode, param)
-    return best[1], best[2]

@@ -686,15 +686,27 @@ __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_
   int nchunk = 0;
   for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) ++nchunk;
   const int ncand = nsplit + nchunk;
+  // The mode follows the explainer's rule, as pkv_policy: one active row is
+  // split along the sequence (candidates [0, nsplit)), several rows go
+  // through the workqueue (candidates [nsplit, ncand)); if the capacity left
+  // no workqueue candidate, the split candidates serve.
+  int act = 0;
+  for (int b = tid; b < B; b += kThreads) act += row_n(b) > 0 ? 1 : 0;
+  const int thr_active = __syncthreads_count(act > 0);
+  const int thr_multi = __syncthreads_or(act > 1);
+  const bool one_row = thr_active <= 1 && !thr_multi;
+  const bool use_split = one_row || nchunk == 0;
+  const int c_lo = use_split ? 0 : nsplit;
+  const int c_hi = use_split ? nsplit : ncand;
   const int j = tid % kCandBatch;
   const int grp = tid / kCandBatch;
   double best_t = 0.0;
   int best_i = -1;
   int64_t total_pages = 0;
-  for (int cb = 0; cb < ncand; cb += kCandBatch) {
+  for (int cb = c_lo; cb < c_hi; cb += kCandBatch) {
     const int i = cb + j;
     PlanShape f;
-    if (i < ncand) {
+    if (i < c_hi) {
       const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
       const uint32_t v = i < nsplit ? (1u << i)
                                     : static_cast<uint32_t>(p.chunk_min) << (i - nsplit);
@@ -705,7 +717,7 @@ __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_
     L.pmax[grp][j] = f.pmax;
     L.maxS[grp][j] = f.maxS;
     __syncthreads();
-    if (tid < kCandBatch && i < ncand) {
+    if (tid < kCandBatch && i < c_hi) {
       PlanShape F;
       for (int r = 0; r < kCandGroups; ++r) {
         F.T += L.T[r][j];
@@ -719,7 +731,7 @@ __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_
     __syncthreads();
     if (tid == 0) {
       total_pages = L.pages;
-      for (int k = 0; k < kCandBatch && cb + k < ncand; ++k) {
+      for (int k = 0; k < kCandBatch && cb + k < c_hi; ++k) {
         if (best_i < 0 || L.t[k] < best_t) {
           best_t = L.t[k];
           best_i = cb + k;

@@ -152,8 +152,14 @@ int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim
       *param = static_cast<int32_t>(v);
     }
   };
-  for (int64_t S = 1; S <= p.split_max; S *= 2) consider(PKV_MODE_SPLIT, S);
-  for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) consider(PKV_MODE_WORKQUEUE, c);
+  // The mode follows the explainer's rule: a single long row is split along
+  // the sequence, a batch of rows goes through the compact workqueue.  The
+  // fitted model picks the split count or the chunk.
+  if (active == 1) {
+    for (int64_t S = 1; S <= p.split_max; S *= 2) consider(PKV_MODE_SPLIT, S);
+  } else {
+    for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) consider(PKV_MODE_WORKQUEUE, c);
+  }
   return PKV_OK;
 }
 

@@ -90,20 +90,24 @@ def predict(x, T, P, pmax, maxS, two, cus, head_dim):
     return t
 
 
-def candidates():
-    S = 1
-    while S <= SPLIT_MAX:
-        yield 0, S
-        S *= 2
-    c = CHUNK_MIN
-    while c <= CHUNK_MAX:
-        yield 1, c
-        c *= 2
+def candidates(lens):
+    """The candidates pkv_policy searches: split counts for a single active
+    row, workqueue chunks for a batch (the explainer's mode rule)."""
+    if sum(1 for n in lens if int(n) > 0) <= 1:
+        S = 1
+        while S <= SPLIT_MAX:
+            yield 0, S
+            S *= 2
+    else:
+        c = CHUNK_MIN
+        while c <= CHUNK_MAX:
+            yield 1, c
+            c *= 2
 
 
 def pick(x, lens, Hkv, cus, head_dim):
     best = None
-    for mode, param in candidates():
+    for mode, param in candidates(lens):
         T, P, pmax, maxS = plan_features(lens, Hkv, mode, param)
         t = predict(x, T, P, pmax, maxS, maxS > FUSE_MAX_SPLITS, cus, head_dim)
         if best is None or t < best[0]:

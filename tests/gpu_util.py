@@ -69,6 +69,23 @@ def run_hip(wl, mode=None, param=None, decoder=None, lse=True, repeats=1, two_la
     return out, lse_t, decoder
 
 
+def check_bf16_rows(wl, got, got_lse, ref, ref_lse, rows=None, k_scale=1.0, v_scale=1.0,
+                    where=""):
+    """bf16 outputs (bf16 q; 2-byte or fp8 pools) against the oracle's ref /
+    ref_lse on ``rows``: the rigorous elementwise and the statistical normwise
+    bounds of tests/rounding_bound.py, with the softmax weights of the
+    dequantised inputs.  Returns (max abs error, worst normwise ratio)."""
+    from tests import rounding_bound
+    if rows is None:
+        rows = range(len(wl.seq_lens_np))
+    q, k, v, bt, sl = compact_rows(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, rows)
+    stats = rounding_bound.softmax_stats(q, oracle.kv_values(k, k_scale), oracle.kv_values(v, v_scale),
+                                     bt, sl, wl.cfg.scale * 1.0, ref)
+    err, ratio = rounding_bound.check(got, got_lse, ref, ref_lse, stats, where)
+    log_case("bf16 max abs err", f"{err:.3e}", "normwise / bound", f"{ratio:.3f}")
+    return err, ratio
+
+
 def oracle_rows(wl, rows=None, k_scale=1.0, v_scale=1.0):
     """Float64 oracle on the given rows (all rows by default), pages copied
     from wherever the workload lives (fp8 pools as their E4M3 codes)."""

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import policy_model_check as pmc
 import paged_gqa_decode_pkv_amd as pkv
 from workloads import CONFIGS, CALIBRATION_SEED, HELD_OUT_SEEDS, make_lengths
 
@@ -162,19 +163,21 @@ def _policy_cases():
     return cases
 
 
-def test_policy_matches_oracle():
-    """The library's cost-model policy takes the oracle's decision, bit for bit,
-    over the workload configs, their seeds and random batches."""
+def test_policy_matches_second_implementation():
+    """The library's cost-model policy takes the decision of the independent
+    transcription in tests/policy_model_check.py (a cross-implementation
+    check, not the oracle), bit for bit, over the workload configs, their
+    seeds and random batches."""
     for lens in _policy_cases():
         for cus in (1, 80, 256, 304):
             for Hkv in (1, 8):
                 for D in (64, 128):
                     got = pkv.pkv_policy(lens, Hkv, cus, head_dim=D)
-                    want = oracle.policy(lens, Hkv, 16, cus, head_dim=D)
+                    want = pmc.policy(lens, Hkv, 16, cus, head_dim=D)
                     assert got == tuple(int(x) for x in want), (lens[:4], cus, Hkv, D)
 
 
-def test_policy_predict_matches_oracle_bit_for_bit():
+def test_policy_predict_matches_second_implementation_bit_for_bit():
     """The model times themselves agree exactly (same float64 operations, no
     contraction), for every candidate and both launch forms."""
     rng = np.random.default_rng(6)
@@ -184,25 +187,25 @@ def test_policy_predict_matches_oracle_bit_for_bit():
                                 (0, int(rng.integers(1, 500))), (1, int(rng.integers(1, 500)))]:
                 for two in (-1, 0, 1):
                     got = pkv.pkv_policy_predict(lens, 8, cus, mode, param, two)
-                    shape = oracle.plan_shape(lens, 8, 16, mode, param)
-                    t2 = shape[3] > oracle.POLICY_DEFAULTS["fuse_max_splits"] if two < 0 else bool(two)
-                    want = oracle.predict_us(shape, cus, 128, 16, t2, oracle.POLICY_DEFAULTS)
+                    shape = pmc.plan_shape(lens, 8, 16, mode, param)
+                    t2 = shape[3] > pmc.POLICY_DEFAULTS["fuse_max_splits"] if two < 0 else bool(two)
+                    want = pmc.predict_us(shape, cus, 128, 16, t2, pmc.POLICY_DEFAULTS)
                     assert got == want, (lens[:4], cus, mode, param, two, got, want)
 
 
 def test_policy_defaults_are_the_committed_fit():
-    """pkv_policy_defaults and the oracle's defaults hold the constants that
-    policy_fit.py fitted on the calibration seed."""
+    """pkv_policy_defaults and the second implementation's defaults hold the
+    constants that policy_fit.py fitted on the calibration seed."""
     import json
     fit = json.load(open(os.path.join(ROOT, "paged_gqa_decode_pkv_amd", "calibration",
                                       "mi355x_fit.json")))
     d = pkv.pkv_policy_defaults()
     for name, v in fit["params"].items():
         assert getattr(d, name) == v, name
-        assert oracle.POLICY_DEFAULTS[name] == v, name
+        assert pmc.POLICY_DEFAULTS[name] == v, name
     assert (d.split_max, d.chunk_min, d.chunk_max, d.fuse_max_splits) == (256, 4, 256, 16)
     for k in ("split_max", "chunk_min", "chunk_max", "fuse_max_splits"):
-        assert oracle.POLICY_DEFAULTS[k] == getattr(d, k)
+        assert pmc.POLICY_DEFAULTS[k] == getattr(d, k)
 
 
 def test_policy_params_and_errors():
@@ -214,11 +217,12 @@ def test_policy_params_and_errors():
     d = pkv.pkv_policy_defaults()
     d.chunk_min, d.chunk_max = 1024, 1024
     d.split_max = 8
-    # one long row: only S <= 8 or c = 1024 are candidates
+    # one long row: split, S <= 8; two rows: workqueue, c = 1024 only
     m, p = pkv.pkv_policy([32768], 8, 256, params=d)
-    assert (m, p) in [(pkv.PKV_MODE_SPLIT, 8), (pkv.PKV_MODE_WORKQUEUE, 1024)]
-    assert (m, p) == oracle.policy([32768], 8, 16, 256, split_max=8, chunk_min=1024,
-                                   chunk_max=1024)
+    assert m == pkv.PKV_MODE_SPLIT and p in (1, 2, 4, 8)
+    assert (m, p) == pmc.policy([32768], 8, 16, 256, split_max=8, chunk_min=1024,
+                                chunk_max=1024)
+    assert pkv.pkv_policy([32768, 5], 8, 256, params=d) == (pkv.PKV_MODE_WORKQUEUE, 1024)
     with pytest.raises(pkv.PkvError):
         pkv.pkv_policy([-5], 8, 256)
     with pytest.raises(pkv.PkvError):

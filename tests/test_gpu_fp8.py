@@ -5,15 +5,15 @@ The oracle decodes the pools' codes itself (``oracle.e4m3_decode``, from the
 format's definition) and applies the per-tensor scales in float64.  Every
 E4M3 value is exact in fp16 and in bf16, and the kernel converts the codes
 exactly before the same MFMA path as the 2-byte pools, so the tolerances are
-those of q's type: max abs 2e-3 and rel 1e-2 for fp16 q; for bf16 q the bound
-derived in test_gpu_bf16.py (2^-7 max|v| + 2^-9 max|ref|, lse 2^-8), with v
-the dequantised values.
+those of q's type: max abs 2e-3 and rel 1e-2 for fp16 q; for bf16 q the
+bounds of tests/rounding_bound.py, with the softmax weights and values of the
+dequantised pools.
 """
 import numpy as np
 import pytest
 
-from tests.gpu_util import check_close, check_lse, log_case, oracle_rows, run_hip
-from workloads import CALIBRATION_SEED, HELD_OUT_SEEDS, Config, compact_rows, make_workload
+from tests.gpu_util import check_bf16_rows, check_close, check_lse, log_case, oracle_rows, run_hip
+from workloads import CALIBRATION_SEED, HELD_OUT_SEEDS, Config, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -31,19 +31,8 @@ def _parity(wl, mode=None, param=None, two_launch=None, k_scale=1.0, v_scale=1.0
     got_lse = lse.cpu().numpy()[sel]
     import torch
     if wl.q.dtype == torch.bfloat16:
-        import oracle
-        q, k, v, bt, sl = compact_rows(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens,
-                                       range(len(wl.seq_lens_np)) if rows is None else rows)
-        vals = oracle.kv_values(v, v_scale)
-        vmax = float(np.nanmax(np.abs(vals))) if vals.size else 0.0
-        err = float(np.max(np.abs(got - ref))) if got.size else 0.0
-        bound = 2.0 ** -7 * vmax + 2.0 ** -9 * float(np.max(np.abs(ref)) if ref.size else 0.0)
-        log_case("bf16 q, fp8 pools: max abs err", f"{err:.3e}", "bound", f"{bound:.3e}")
-        assert np.all(np.isfinite(got)) and err <= bound
-        inf = np.isneginf(ref_lse)
-        assert np.array_equal(np.isneginf(got_lse), inf)
-        if (~inf).any():
-            assert float(np.max(np.abs(got_lse[~inf] - ref_lse[~inf]))) <= 2.0 ** -8
+        check_bf16_rows(wl, got, got_lse, ref, ref_lse, rows, k_scale, v_scale,
+                        where=f"bf16 q fp8 pools {wl.cfg.name}")
     else:
         check_close(got, ref, atol=2e-3 * max(1.0, v_scale))   # out scales with v_scale
         check_lse(got_lse, ref_lse)

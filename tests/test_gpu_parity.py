@@ -70,20 +70,36 @@ def test_b8_bimodal_held_out_seeds(seed):
 
 @pytest.fixture(scope="module")
 def b64():
+    """The full-size B=64 batch (34.4 GB pool) and the oracle on 16 of its
+    rows: the four longest (the deepest split groups), the two shortest and
+    ten spread over the batch."""
     import torch
     wl = make_workload("b64", SEED, device="cuda")
-    yield wl
+    n = wl.seq_lens_np
+    order = np.argsort(n)
+    rows = sorted(set(order[-4:].tolist()) | set(order[:2].tolist()) |
+                  set(range(0, 64, 7)) | {63})
+    assert len(rows) >= 16, rows
+    log_case("b64 oracle rows", rows, "lens", n[rows].tolist())
+    ref, ref_lse = oracle_rows(wl, rows)
+    yield wl, rows, ref, ref_lse
     del wl
     torch.cuda.empty_cache()
 
 
+@pytest.mark.slow
 @pytest.mark.parametrize("two_launch", TWO)
 @pytest.mark.parametrize("mode", [None, 0, 1])
 def test_b64_sampled_rows(b64, mode, two_launch):
-    """Full-size B=64 batch (34.4 GB pool), oracle on sampled rows."""
-    rows = [0, 17, 42, 63]
+    """Full-size B=64 batch in the launch configuration the bench times (and
+    the other schedules), oracle on 16 rows."""
+    wl, rows, ref, ref_lse = b64
     param = {None: None, 0: 16, 1: 64}[mode]
-    _parity(b64, mode, param, rows=rows, two_launch=two_launch)
+    log_case("b64", "mode", mode, "param", param, "two_launch", two_launch)
+    out, lse, dec = run_hip(wl, mode, param, two_launch=two_launch)
+    check_close(out.float().cpu().numpy()[rows], ref)
+    check_lse(lse.cpu().numpy()[rows], ref_lse)
+    assert dec.error_flags() == 0
 
 
 # --------------------------------------------------------------------------- edge cases
@@ -199,13 +215,32 @@ def test_plan_device_copy_reuse_and_switch():
 
 
 def test_split_counts_agree():
+    """Any split count computes the same attention.  lse (fp32) agrees within
+    1e-5 relative.  out cannot agree within 1e-5: the kernel rounds each
+    p = 2^(s - m) to fp16 (unit roundoff 2^-11), and every split keeps its own
+    reference maximum, so two split counts round different values; their
+    outputs differ by two independent rounding errors of the size derived in
+    tests/rounding_bound.py.  So each split count is checked against the
+    oracle with that statistical bound at u = 2^-11 (far tighter than the
+    2e-3 bar), and every pair against the first with the pairwise bound."""
+    from tests import rounding_bound
+    import oracle
+    from workloads import compact_rows
     wl = make_workload("b1", CALIBRATION_SEED, device="cuda")
-    lses = []
-    for S in (1, 2, 8, 64, 256):
-        _, lse, _ = run_hip(wl, 0, S)
-        lses.append(lse.cpu().numpy())
-    for x in lses[1:]:
-        assert np.max(np.abs(x - lses[0])) < 1e-4
+    q, k, v, bt, sl = compact_rows(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, [0])
+    ref, ref_lse = oracle.attend(q, k, v, bt, sl, wl.cfg.scale)
+    stats = rounding_bound.softmax_stats(q, k, v, bt, sl, wl.cfg.scale, ref)
+    outs, lses = [], []
+    for S in (1, 2, 8, 32, 64, 256):
+        o, lse, _ = run_hip(wl, 0, S)
+        outs.append(o.float().cpu().numpy().astype(np.float64))
+        lses.append(lse.cpu().numpy().astype(np.float64))
+        r = rounding_bound.check(outs[-1], None, ref, ref_lse, stats, f"S={S}",
+                                 u=rounding_bound.U_FP16)
+        log_case("S", S, "max abs err / normwise ratio vs oracle", r)
+    for S, o, lse in zip((2, 8, 32, 64, 256), outs[1:], lses[1:]):
+        assert np.max(np.abs(lse - lses[0]) / np.abs(lses[0])) <= 1e-5
+        rounding_bound.check_pair(o, outs[0], ref, stats, f"S={S} vs S=1")
 
 
 def test_task_list_readback_bit_exact():

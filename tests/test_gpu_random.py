@@ -5,15 +5,15 @@ Each case draws G, d, Hkv, B, the row lengths (including empty rows, single
 tokens, page-boundary lengths and rows at the table width), the pool type,
 the schedule (split S or workqueue c), the launch form and, for fp8 pools,
 the dequantisation scales.  The bar is that of the element type (see
-test_gpu_parity.py, test_gpu_bf16.py and test_gpu_fp8.py); with v_scale > 1
+test_gpu_parity.py and tests/rounding_bound.py); with v_scale > 1
 the absolute fp16 bound is 2e-3 * v_scale, since out and its rounding error
 both scale with v_scale.
 """
 import numpy as np
 import pytest
 
-from tests.gpu_util import check_close, check_lse, log_case, oracle_rows, run_hip
-from workloads import Config, compact_rows, make_workload
+from tests.gpu_util import check_bf16_rows, check_close, check_lse, log_case, oracle_rows, run_hip
+from workloads import Config, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,6 @@ def _case(seed):
 @pytest.mark.parametrize("seed", range(150))
 def test_random_case(seed):
     import torch
-    import oracle
     G, D, Hkv, B, maxp, lens, dtype, mode, param, two, fill, (ks, vs) = _case(seed)
     log_case("random", seed, "G", G, "D", D, "Hkv", Hkv, "lens", lens, "dtype", dtype, "mode", mode,
              "param", param, "two", two, "fill", fill, "scales", ks, vs)
@@ -54,17 +53,7 @@ def test_random_case(seed):
     got = out.float().cpu().numpy()
     got_lse = lse.cpu().numpy()
     if wl.q.dtype == torch.bfloat16:
-        q, k, v, bt, sl = compact_rows(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens,
-                                       range(B))
-        vals = oracle.kv_values(v, vs)
-        vmax = float(np.nanmax(np.abs(vals))) if vals.size else 0.0
-        err = float(np.max(np.abs(got - ref)))
-        bound = 2.0 ** -7 * vmax + 2.0 ** -9 * float(np.max(np.abs(ref)))
-        assert np.all(np.isfinite(got)) and err <= bound, (err, bound)
-        inf = np.isneginf(ref_lse)
-        assert np.array_equal(np.isneginf(got_lse), inf)
-        if (~inf).any():
-            assert float(np.max(np.abs(got_lse[~inf] - ref_lse[~inf]))) <= 2.0 ** -8
+        check_bf16_rows(wl, got, got_lse, ref, ref_lse, None, ks, vs, where=f"random {seed}")
     else:
         # out is linear in v_scale, and so is its rounding error: the absolute
         # bound scales with it (the relative one does not change)

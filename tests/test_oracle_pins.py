@@ -129,67 +129,6 @@ def test_task_list_errors():
         oracle.plan_tasks([16], 1, 16, oracle.MODE_SPLIT, 0)
 
 
-# --------------------------------------------------------------------------- policy
-
-@pytest.mark.parametrize("seed", range(6))
-def test_plan_shape_pinned_to_the_task_list(seed):
-    """plan_shape's closed form equals what the enumerated task list holds."""
-    rng = np.random.default_rng(400 + seed)
-    lens = rng.integers(0, 5000, size=int(rng.integers(1, 12)))
-    lens[rng.integers(0, len(lens))] = 0
-    for mode, params in ((oracle.MODE_SPLIT, (1, 2, 5, 64)), (oracle.MODE_WORKQUEUE, (1, 3, 16, 999))):
-        for p in params:
-            tasks, offs = oracle.plan_tasks(lens, 3, 16, mode, p)
-            walk = brute.tasks_by_walking(lens, 3, 16, (lambda b, n: -(-n // p)) if mode == 0
-                                          else (lambda b, n: p))
-            n = [-(-int(x) // 16) for x in lens]
-            pages = [min((s + 1) * c, n[b]) - s * c for b, g, s, c in walk]
-            T, P, pmax, maxS = oracle.plan_shape(lens, 3, 16, mode, p)
-            assert (T, P, pmax) == (len(walk), sum(pages), max(pages, default=0))
-            assert maxS == max((offs[i + 1] - offs[i] for i in range(len(lens))), default=0)
-
-
-def test_predict_us_closed_forms():
-    """Special cases of the time model that reduce to plain arithmetic."""
-    k = dict(oracle.POLICY_DEFAULTS)
-    # no task: the fixed time
-    assert oracle.predict_us((0, 0, 0, 0), 256, 128, 16, False, k) == k["t0_us"]
-    # one task of 10 pages on a 256-CU chip: one CU at the smaller rate
-    rho = min(k["cu_gbps"], k["hbm_gbps"] / 1)
-    t = oracle.predict_us((1, 10, 10, 1), 256, 128, 16, False, k)
-    want = k["t0_us"] + k["t_round_us"] + 10 * 8192 / (rho * 1e3) + k["t_fused_split_us"]
-    assert abs(t - want) < 1e-9
-    # a full chip of equal tasks streams at the chip rate
-    t = oracle.predict_us((512, 512 * 20, 20, 1), 256, 128, 16, False, k)
-    rho = min(k["cu_gbps"], k["hbm_gbps"] / 256)
-    want = k["t0_us"] + k["t_round_us"] + 40 * 8192 / (rho * 1e3) + k["t_fused_split_us"]
-    assert abs(t - want) < 1e-9
-    # head_dim 64 halves the streaming term
-    t128 = oracle.predict_us((64, 6400, 100, 8), 256, 128, 16, True, k)
-    t64 = oracle.predict_us((64, 6400, 100, 8), 256, 64, 16, True, k)
-    fixed = k["t0_us"] + k["t_round_us"] + k["t_two_us"] + k["t_two_split_us"] * 8
-    assert abs((t128 - fixed) - 2 * (t64 - fixed)) < 1e-9
-
-
-def test_policy_structure():
-    """The pages: one long row -> enough sequence splits to fill the chip;
-    8 long ragged rows -> the compact workqueue.  (The constants are this
-    project's fit: parity unpinned.)"""
-    from workloads import CONFIGS, make_lengths
-    m, p = oracle.policy([32768], 8, 16, 256)
-    T, _, _, _ = oracle.plan_shape([32768], 8, 16, m, p)
-    assert T >= 256 // 2
-    for seed in range(20260622, 20260628):
-        lens = make_lengths(CONFIGS["b8_bimodal"], seed)
-        m, p = oracle.policy(lens, 8, 16, 256)
-        assert m == oracle.MODE_WORKQUEUE and 4 <= p <= 256 and p & (p - 1) == 0
-    assert oracle.policy([0, 0], 8, 16, 256) == (oracle.MODE_SPLIT, 1)
-    # a short row: some split, never more tasks than (page, head) tiles
-    m, p = oracle.policy([100, 0], 8, 16, 256)
-    T, _, _, _ = oracle.plan_shape([100, 0], 8, 16, m, p)
-    assert 8 <= T <= 8 * 7
-
-
 # --------------------------------------------------------------------------- fp8 KV values
 
 def test_e4m3_decode_spec_values():
