@@ -166,9 +166,12 @@ int pkv_policy_defaults(pkv_policy_params* params);
  * policy "roofline-style".  The branches that hand work to another library
  * are outside this library.
  *
- * The policy predicts the time of every candidate plan with a roofline-style
- * model and returns the fastest.  Candidates, in this order (ties keep the
- * earlier one): SPLIT with S = 1, 2, 4, ... <= split_max, then WORKQUEUE with
+ * The mode follows the explainer's rule: a batch with one active row (N_b >
+ * 0) is split along the sequence, a batch with two or more active rows goes
+ * through the workqueue.  Within the mode, the policy predicts the time of
+ * every candidate plan with a roofline-style model and returns the fastest.
+ * Candidates, in this order (ties keep the earlier one): one active row,
+ * SPLIT with S = 1, 2, 4, ... <= split_max; otherwise WORKQUEUE with
  * c = chunk_min, 2 chunk_min, ... <= chunk_max.  For a candidate, with
  * n_b = ceil(N_b / page_size), c_b the chunk of row b (SPLIT: ceil(n_b/S);
  * WORKQUEUE: c) and S_b = ceil(n_b / c_b) over rows with n_b > 0:
@@ -382,8 +385,10 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
  * "2. Calibrated Adaptive Policy".  The plan: with mode = -1, (mode, param)
  * exactly as pkv_policy would pick them with `policy` limited to the capacity
  * (split_max <= max_splits; workqueue chunks c with ceil(max_pages_per_row /
- * c) <= max_splits); then the same split_offsets and task records as pkv_plan,
- * and a header.  Launches on `stream`:
+ * c) <= max_splits; a batch of several rows for which the capacity leaves no
+ * workqueue candidate takes the split candidates); then the same
+ * split_offsets and task records as pkv_plan, and a header.  Launches on
+ * `stream`:
  *   B <= 1024: the persistent decode kernel (num_cus workgroups), every
  *      workgroup planning for itself from the lengths it stages (workgroup 0
  *      writes the plan out for pkv_device_plan_read);
