@@ -20,8 +20,8 @@
 //   split offsets, task records), for the device-planned step.
 //
 // Kernel 2, pkv_merge_kernel: the exact log-sum-exp combination of a row's
-//   partial states in the two-launch form, one workgroup per (row, KV head)
-//   for the G heads of the group.
+//   partial states in the two-launch form, (G*D/4 R)/64 64-thread workgroups
+//   per (row, KV head), folding every column as the fused merge does.
 //
 // Kernel 3, pkv_plan_kernel: the device-planned step's plan for batches too
 //   large to stage in LDS (one workgroup).
@@ -1306,22 +1306,101 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   }
 }
 
-// Kernel 2 of the two-launch form: one workgroup per (row, KV head).
+// Kernel 2 of the two-launch form, 64-thread workgroups.  A group's C =
+// G*D/4 float4 columns are folded exactly as merge_group folds them inside
+// the decode kernel -- R = 256/C threads per column (1 for C > 256), each
+// over slots r, r+R, ..., the R states combined in LDS in the same order --
+// so the two launch forms give the same bits; but the columns are spread
+// over (C R) / 64 workgroups per group instead of one, so a deep group is
+// merged by many CUs at once.
+constexpr int kMergeKernelThreads = 64;
+
+template <int D>
+__device__ __forceinline__ int merge_threads_per_column(int G) {
+  const int cols = G * (D / 4);
+  return cols > kThreads ? 1 : kThreads / cols;
+}
+
+template <int D>
+inline int merge_kernel_blocks(int G) {
+  const int cols = G * (D / 4);
+  const int R = cols > kThreads ? 1 : kThreads / cols;
+  return cols * R / kMergeKernelThreads;
+}
+
 template <int D, class E>
-__global__ void __launch_bounds__(kThreads) pkv_merge_kernel(MergeArgs a) {
-  __shared__ __attribute__((aligned(16))) float lds[merge_lds_floats<D>()];
+__global__ void __launch_bounds__(kMergeKernelThreads) pkv_merge_kernel(MergeArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[kMergeKernelThreads * 6];
   if (a.plan_hdr && a.plan_hdr[1]) return;   // merged inside the decode kernel
-  const int b = blockIdx.x / a.Hkv;
-  const int g = blockIdx.x - b * a.Hkv;
+  const int G = a.G;
+  const int R = merge_threads_per_column<D>(G);
+  const int cpw = kMergeKernelThreads / R;         // columns per workgroup
+  const int nch = G * (D / 4) / cpw;
+  const int bg = blockIdx.x / nch;
+  const int chunk = blockIdx.x - bg * nch;
+  const int b = bg / a.Hkv;
+  const int g = bg - b * a.Hkv;
+  const int tid = threadIdx.x;
+  const int r = tid / cpw;
+  const int c = chunk * cpw + (tid - r * cpw);
+  const int h = (4 * c) / D;
+  const int64_t head0 = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(g) * G;
   const int o0 = __builtin_amdgcn_readfirstlane(a.split_offsets[b]);
   const int S = __builtin_amdgcn_readfirstlane(a.split_offsets[b + 1]) - o0;
   if (S == 1) return;   // written directly by the decode kernel
+  auto write = [&](float Mt, float Lt, floatx4 Ot) {
+    const float inv = 1.f / Lt;
+    E* dst = static_cast<E*>(a.out) + head0 * D + 4 * c;
+    dst[0] = static_cast<E>(Ot[0] * inv);
+    dst[1] = static_cast<E>(Ot[1] * inv);
+    dst[2] = static_cast<E>(Ot[2] * inv);
+    dst[3] = static_cast<E>(Ot[3] * inv);
+    if ((4 * c) % D == 0 && a.lse) a.lse[head0 + h] = (Mt + __log2f(Lt)) * kLn2;
+  };
   if (S <= 0 || o0 < 0 || static_cast<int64_t>(o0) + S > a.num_slots) {
-    if (S != 0 && threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_SLOT);
-    write_empty_group<D, E>(a, b, g);
+    // an empty row (out = 0, lse = -inf), or a bad offset (flagged)
+    if (S != 0 && chunk == 0 && tid == 0) flag_error(a.ctrl, PKV_DEVERR_SLOT);
+    if (r == 0) {
+      E* dst = static_cast<E*>(a.out) + head0 * D + 4 * c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = static_cast<E>(0.f);
+      if ((4 * c) % D == 0 && a.lse) a.lse[head0 + h] = -INFINITY;
+    }
     return;
   }
-  merge_group<D, kMergeBatch, E>(a, b, g, o0, S, lds);
+  // Coherent (L2-bypassing) loads: the states come from other XCDs.
+  const __amdgpu_buffer_rsrc_t ml_rsrc = make_rsrc(
+      a.part_ml + static_cast<int64_t>(o0) * a.Hq, static_cast<uint32_t>(S) * a.Hq * 8u);
+  const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+      a.part_o + static_cast<int64_t>(o0) * a.Hq * D, static_cast<uint32_t>(S) * a.Hq * D * 4u);
+  float M, L;
+  floatx4 O;
+  fold_column<D, kMergeBatch>(ml_rsrc, o_rsrc, a.Hq, 8 * (g * G + h), 4 * (g * G * D + 4 * c),
+                              r, R, S, M, L, O);
+  if (R == 1) {
+    write(M, L, O);
+    return;
+  }
+  float* s_M = lds;
+  float* s_L = lds + kMergeKernelThreads;
+  floatx4* s_O = reinterpret_cast<floatx4*>(lds + 2 * kMergeKernelThreads);
+  s_M[tid] = M;
+  s_L[tid] = L;
+  s_O[tid] = O;
+  __syncthreads();
+  if (tid < cpw) {
+    float Mt = -INFINITY;
+    for (int j = 0; j < R; ++j) Mt = fmaxf(Mt, s_M[tid + j * cpw]);
+    float Lt = 0.f;
+    floatx4 Ot = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < R; ++j) {
+      const float mj = s_M[tid + j * cpw];
+      const float w = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mt);
+      Lt += w * s_L[tid + j * cpw];
+      Ot += w * s_O[tid + j * cpw];
+    }
+    write(Mt, Lt, Ot);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1509,8 +1588,8 @@ int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t
     }
   }
   if (ma.B > 0) {
-    hipLaunchKernelGGL((pkv_merge_kernel<D, E>), dim3(ma.B * ma.Hkv), dim3(kThreads), 0, stream,
-                       ma);
+    hipLaunchKernelGGL((pkv_merge_kernel<D, E>), dim3(ma.B * ma.Hkv * merge_kernel_blocks<D>(ma.G)),
+                       dim3(kMergeKernelThreads), 0, stream, ma);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       set_hip_error(static_cast<int>(e));
