@@ -451,18 +451,24 @@ int pkv_device_plan_read(const void* workspace, size_t workspace_bytes, int32_t 
  * Methodologie ("Row-Local Bounds", "Compact Workqueue").  "Evaluatieprotocol"
  * counts host planning in the synchronized wall time of a step.
  *
- * A runner owns a ring of pinned plan buffers, each guarded by a HIP event
- * recorded after the merge kernel, so it never rewrites a plan that
- * enqueued kernels still read, plus one device buffer and a side stream
- * (default priority) for a device copy of the last distinct plan.  When a
- * step's plan differs from the previous distinct plan, its kernels read it
- * in place from pinned host memory (16 bytes per task) and the plan is
- * uploaded on the side stream; a later step with the same plan reads the
- * device copy (the caller's stream waits for the upload).  Other device
- * memory belongs to the caller.  One runner serves one thread at a time and
- * the device that was current when it was created (on another device it
- * always reads the pinned plan).  A stream passed to a step must stay valid
- * until pkv_runner_destroy returns.
+ * A runner owns a ring of pinned host plan buffers, each guarded by a HIP
+ * event recorded after the merge kernel, so it never rewrites a plan that
+ * enqueued kernels still read, and a side stream (default priority).  It
+ * allocates no device memory.  When a step's plan differs from the previous
+ * distinct plan, its kernels read it in place from pinned host memory (16
+ * bytes per task) and the plan is uploaded on the side stream into the tail
+ * of the caller's workspace; a later step with the same plan and the same
+ * workspace reads that device copy (the caller's stream waits for the
+ * upload).  The workspace of a step must therefore hold the partial states
+ * and the plan: workspace_bytes_needed = pkv_workspace_size(num_partial_slots,
+ * Hq, head_dim) + the plan's size (4 (pad4(B + 1) + 4 num_tasks) bytes)
+ * rounded up to 256; the copy sits in the last such bytes of the workspace.
+ * Steps may move between streams: a step that reads the device copy on a new
+ * stream first waits for the readers on the previous one, and an upload
+ * waits for the readers of the old copy.  One runner serves one thread at a
+ * time and the device that was current when it was created (on another
+ * device it always reads the pinned plan).  A stream passed to a step must
+ * stay valid until pkv_runner_destroy returns.
  */
 typedef struct pkv_runner pkv_runner;
 
@@ -520,7 +526,8 @@ int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t 
                       pkv_runner** runner);
 
 /* Enqueue one step.  Fills the output fields of *args.  If the workspace is
- * too small, nothing is enqueued, workspace_bytes_needed holds the size, and
+ * too small (partial states and the plan copy, see above), nothing is
+ * enqueued, workspace_bytes_needed holds the size, and
  * PKV_ERR_BUFFER_TOO_SMALL is returned.  The block table
  * is not checked here: pkv_plan with a host copy of it does that.  Other
  * errors are those of pkv_policy, pkv_plan and pkv_decode, or PKV_ERR_HIP. */

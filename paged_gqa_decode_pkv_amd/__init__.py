@@ -497,6 +497,79 @@ def pkv_runner_last_plan(runner):
     return t[:4 * T.value].reshape(T.value, 4).copy(), o
 
 
+# --------------------------------------------------------------------------- plan / decode
+
+class Plan:
+    """A step's schedule: (mode, param), the compact task list and split
+    offsets on the host (numpy) and on the device (int32 tensors), the number
+    of partial-state slots and the deepest row's split count."""
+
+    def __init__(self, mode, param, tasks, split_offsets, num_partial_slots, device):
+        import torch
+        self.mode, self.param = int(mode), int(param)
+        self.tasks_host, self.offsets_host = tasks, split_offsets
+        self.num_partial_slots = int(num_partial_slots)
+        self.max_splits = int(np.max(np.diff(split_offsets))) if len(split_offsets) > 1 else 0
+        self.tasks = torch.from_numpy(np.ascontiguousarray(tasks)).to(device)
+        self.split_offsets = torch.from_numpy(np.ascontiguousarray(split_offsets)).to(device)
+
+    @property
+    def num_tasks(self) -> int:
+        return len(self.tasks_host)
+
+
+def plan(seq_lens, Hkv: int, max_pages_per_row: int, mode: Optional[int] = None,
+         param: Optional[int] = None, num_cus: Optional[int] = None, head_dim: int = 128,
+         dtype: int = PKV_DTYPE_F16, block_table=None, num_pages: int = 0,
+         params: Optional[pkv_policy_params] = None, device="cuda") -> Plan:
+    """Policy (when mode is None) and task list for host lengths ``seq_lens``:
+    pkv_policy then pkv_plan (optionally checking a host block table), with
+    the plan copied to ``device``."""
+    import torch
+    if mode is None:
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+        fp8 = dtype in (PKV_DTYPE_F16_KV_FP8, PKV_DTYPE_BF16_KV_FP8)
+        mode, param = pkv_policy(seq_lens, Hkv, num_cus, params,
+                                 head_dim=head_dim // 2 if fp8 else head_dim)
+    tasks, offs, slots = pkv_plan(seq_lens, Hkv, max_pages_per_row, mode, param,
+                                  block_table=block_table, num_pages=num_pages)
+    return Plan(mode, param, tasks, offs, slots, device)
+
+
+def decode(q, k_pool, v_pool, block_table, seq_lens, plan: Plan, scale: Optional[float] = None,
+           out=None, lse=None, workspace=None, two_launch: Optional[bool] = None, stream=None,
+           k_scale: float = 1.0, v_scale: float = 1.0,
+           params: Optional[pkv_policy_params] = None):
+    """One decode step on a plan: pkv_decode (merge fused), or
+    pkv_decode_splits then pkv_merge when ``two_launch`` (None: the policy's
+    rule, more than fuse_max_splits splits in a row).  ``workspace`` (uint8,
+    >= pkv_workspace_size, zeroed once by pkv_workspace_init) is made here
+    when not given.  Returns (out, lse)."""
+    import torch
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.zeros(pkv_workspace_size(plan.num_partial_slots, Hq, D),
+                                dtype=torch.uint8, device=q.device)
+        pkv_workspace_init(workspace, stream)
+    if two_launch is None:
+        p = params if params is not None else pkv_policy_defaults()
+        two_launch = plan.max_splits > p.fuse_max_splits
+    args = (q, k_pool, v_pool, block_table, seq_lens, plan.tasks, plan.split_offsets,
+            plan.num_partial_slots, scale, out, workspace)
+    if two_launch:
+        pkv_decode_splits(*args, lse=lse, stream=stream, k_scale=k_scale, v_scale=v_scale)
+        pkv_merge(plan.split_offsets, plan.num_partial_slots, k_pool.shape[1], out, workspace,
+                  lse=lse, stream=stream)
+    else:
+        pkv_decode(*args, lse=lse, stream=stream, k_scale=k_scale, v_scale=v_scale)
+    return out, lse
+
+
 class PagedDecoder:
     """Decode steps through the native runner: one library call per step runs
     policy -> host plan -> decode kernel (-> merge kernel in the two-launch
@@ -593,12 +666,20 @@ class PagedDecoder:
         else:
             a.event_before_decode = None
             a.event_after_decode = None
+        step_stream = torch.cuda.current_stream() if stream is None else stream
         while pkv_runner_step(self.runner, a) == PKV_ERR_BUFFER_TOO_SMALL:
+            # Replace the workspace: every kernel that uses the old one is
+            # queued on a stream of earlier steps (this one or the current
+            # stream), so wait for both before torch may reuse it; the new
+            # one is zeroed and initialised on the current stream, and
+            # waited for, before any step on `step_stream` uses it.
+            step_stream.synchronize()
             torch.cuda.current_stream().synchronize()
             if a.workspace_bytes_needed > a.workspace_bytes:
                 self.workspace = torch.zeros(a.workspace_bytes_needed * 5 // 4 + 256,
                                              dtype=torch.uint8, device=self.device)
                 pkv_workspace_init(self.workspace)
+                torch.cuda.current_stream().synchronize()
             self._bind_buffers()
         self.last = (a.chosen_mode, a.chosen_param, a.num_tasks, a.num_partial_slots, a.B,
                      a.chosen_two_launch)

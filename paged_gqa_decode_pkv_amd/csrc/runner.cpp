@@ -11,12 +11,13 @@
 // The runner owns a ring of pinned plan buffers, each guarded by a HIP event,
 // so a slot is rewritten only after the kernels that read it have completed.
 // A step whose plan differs from the previous one is read by its kernels in
-// place from pinned host memory (16 bytes per task); the plan is also copied
-// to a runner-owned device buffer on a side stream.  Later steps with the
-// same plan (the steady state of decoding, where a row's task records only
-// change when it crosses a chunk boundary) read that device copy, which
-// removes a host-memory round trip from the start of every workgroup.  The
-// remaining device memory (workspace) belongs to the caller.
+// place from pinned host memory (16 bytes per task); the plan is also copied,
+// on a side stream, into the tail of the caller's workspace.  Later steps
+// with the same plan (the steady state of decoding, where a row's task
+// records only change when it crosses a chunk boundary) read that device
+// copy, which removes a host-memory round trip from the start of every
+// workgroup.  The runner allocates no device memory: every device buffer
+// (inputs, outputs, workspace with the plan copy) belongs to the caller.
 
 #include <hip/hip_runtime_api.h>
 
@@ -59,11 +60,13 @@ struct pkv_runner {
   std::vector<Slot> ring;
   size_t next = 0;
   Slot* last = nullptr;
-  // device copy of the last distinct plan
-  int device = -1;                 // device of `dplan`
+  // device copy of the last distinct plan, in the tail of the caller's
+  // workspace (dplan_ws, dplan_ws_bytes identify the workspace)
+  int device = -1;                 // device the runner was created on
   hipStream_t side = nullptr;      // stream of the uploads
   int32_t* dplan = nullptr;
-  size_t dplan_bytes = 0;          // capacity
+  const void* dplan_ws = nullptr;
+  size_t dplan_ws_bytes = 0;
   std::vector<int32_t> shadow;     // what dplan holds (or will hold)
   bool shadow_valid = false;
   Slot* upload_src = nullptr;      // slot the pending upload reads
@@ -83,10 +86,11 @@ int hip_fail(hipError_t e) {
   return PKV_ERR_HIP;
 }
 
-// Start copying the plan in `s` (words int32) to the device buffer on the
-// side stream, after every kernel enqueued so far on the stream that last
-// read the old copy.
-int upload_plan(pkv_runner* r, Slot& s, size_t words) {
+// Start copying the plan in `s` (words int32) to `dst` (in the caller's
+// workspace) on the side stream, after every kernel enqueued so far on the
+// stream that last read the old copy.
+int upload_plan(pkv_runner* r, Slot& s, size_t words, int32_t* dst, const void* ws,
+                size_t ws_bytes) {
   const size_t bytes = words * sizeof(int32_t);
   hipError_t e = hipSuccess;
   r->shadow_valid = false;
@@ -96,25 +100,12 @@ int upload_plan(pkv_runner* r, Slot& s, size_t words) {
     if (e != hipSuccess) return hip_fail(e);
     r->have_reader = false;
   }
-  if (r->dplan_bytes < bytes) {
-    if (r->dplan) {
-      e = hipStreamSynchronize(r->side);
-      if (e != hipSuccess) return hip_fail(e);
-      hipFree(r->dplan);
-      r->dplan = nullptr;
-      r->dplan_bytes = 0;
-    }
-    const size_t want = grown_size(bytes);
-    e = hipMalloc(reinterpret_cast<void**>(&r->dplan), want);
-    if (e != hipSuccess) {
-      r->dplan = nullptr;
-      return hip_fail(e);
-    }
-    r->dplan_bytes = want;
-  }
-  e = hipMemcpyAsync(r->dplan, s.host, bytes, hipMemcpyHostToDevice, r->side);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, r->side);
   if (e == hipSuccess) e = hipEventRecord(r->uploaded, r->side);
   if (e != hipSuccess) return hip_fail(e);
+  r->dplan = dst;
+  r->dplan_ws = ws;
+  r->dplan_ws_bytes = ws_bytes;
   r->shadow.assign(s.host, s.host + words);
   r->shadow_valid = true;
   r->upload_src = &s;
@@ -173,16 +164,6 @@ int pkv_runner_create(int32_t num_cus, const pkv_policy_params* params, int32_t 
     }
     s.bytes = grown_size(0);
   }
-  {
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&r->dplan), grown_size(0));
-    if (e != hipSuccess) {
-      r->dplan = nullptr;
-      pkv::set_hip_error(static_cast<int>(e));
-      pkv_runner_destroy(r);
-      return PKV_ERR_HIP;
-    }
-    r->dplan_bytes = grown_size(0);
-  }
   *runner = r;
   return PKV_OK;
 }
@@ -200,7 +181,6 @@ int pkv_runner_destroy(pkv_runner* r) {
     hipStreamDestroy(r->side);
   }
   if (r->uploaded) hipEventDestroy(r->uploaded);
-  if (r->dplan && hipFree(r->dplan) != hipSuccess) st = PKV_ERR_HIP;
   for (Slot& s : r->ring) {
     if (s.done) {
       if (s.armed) hipEventSynchronize(s.done);
@@ -237,9 +217,14 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   const size_t plan_bytes = (off_words + 4 * static_cast<size_t>(T)) * sizeof(int32_t);
   size_t ws_bytes = 0;
   pkv_workspace_size(slots, a->Hq, a->head_dim, &ws_bytes);
-  a->workspace_bytes_needed = ws_bytes;
+  // the device copy of the plan sits in the last plan_area bytes of the
+  // workspace, behind the partial states
+  const size_t plan_area = (plan_bytes + 255) & ~size_t(255);
+  a->workspace_bytes_needed = ws_bytes + plan_area;
   if (!a->workspace) return PKV_ERR_INVALID_ARG;
-  if (a->workspace_bytes < ws_bytes) return PKV_ERR_BUFFER_TOO_SMALL;
+  if (a->workspace_bytes < ws_bytes + plan_area) return PKV_ERR_BUFFER_TOO_SMALL;
+  int32_t* plan_dst = reinterpret_cast<int32_t*>(
+      static_cast<char*>(a->workspace) + ((a->workspace_bytes - plan_area) & ~size_t(255)));
 
   // a plan slot whose previous readers have finished
   Slot& s = r->ring[r->next];
@@ -301,7 +286,9 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   int dev = -1;
   bool use_dev = false;
   if (hipGetDevice(&dev) == hipSuccess && dev == r->device) {
-    if (r->shadow_valid && r->shadow.size() == words &&
+    if (r->shadow_valid && r->dplan_ws == a->workspace &&
+        r->dplan_ws_bytes == a->workspace_bytes && r->dplan == plan_dst &&
+        r->shadow.size() == words &&
         std::memcmp(r->shadow.data(), s.host, words * sizeof(int32_t)) == 0) {
       if (r->waited_seq != r->upload_seq || r->waited_stream != stream) {
         e = hipStreamWaitEvent(stream, r->uploaded, 0);
@@ -313,6 +300,14 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
       offs_d = r->dplan;
       tasks_d = r->dplan + off_words;
     }
+  }
+  // Readers of the device copy on another stream go first: the next upload
+  // is ordered only after the last reader stream, so a change of stream
+  // orders the new one behind the old one's readers.
+  if (use_dev && r->have_reader && r->reader_stream != stream) {
+    e = hipEventRecord(r->readers_done, r->reader_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, r->readers_done, 0);
+    if (e != hipSuccess) return hip_fail(e);
   }
 
   // the decode kernel (merge fused in), or decode then merge kernel; the
@@ -344,7 +339,7 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
     r->reader_stream = stream;
     r->have_reader = true;
   } else if (st == PKV_OK && dev == r->device) {
-    st = upload_plan(r, s, words);
+    st = upload_plan(r, s, words, plan_dst, a->workspace, a->workspace_bytes);
   }
   return st;
 }

@@ -348,3 +348,17 @@ def test_runner_rejects_bad_args_without_device():
     assert lib.pkv_runner_create(0, None, 0, ctypes.byref(h)) == pkv.PKV_ERR_INVALID_ARG
     assert lib.pkv_runner_step(None, None) == pkv.PKV_ERR_INVALID_ARG
     assert lib.pkv_runner_destroy(None) == pkv.PKV_OK
+
+
+def test_library_allocates_no_device_memory():
+    """The built library imports no device allocator: every device buffer
+    (the workspace and the runner's copy of the plan included) belongs to the
+    caller.  (Pinned host memory for the runner's plan ring is allowed.)"""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    for sym in ("hipMalloc", "hipMallocAsync", "hipMallocManaged", "hipExtMallocWithFlags",
+                "hipMallocPitch", "hipMalloc3D", "hipFree", "hipFreeAsync"):
+        assert sym not in imported, sym
+    assert "hipHostMalloc" in imported

@@ -1,0 +1,118 @@
+"""The one-shot entry points of the C ABI with caller-owned buffers, and the
+runner's workspace handling across streams.
+
+Every buffer here is a torch allocation made by the test (q, pools, table,
+lengths, plan, outputs, workspace); the library only launches kernels on
+them.  Results are compared with the float64 oracle (fp16 bar: max abs 2e-3,
+max abs / max |ref| 1e-2) and, between launch forms, bit for bit.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import check_close, check_lse, log_case, oracle_rows, run_hip
+from workloads import HELD_OUT_SEEDS, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SEED = HELD_OUT_SEEDS[0]
+
+
+def _caller_owned(wl, mode, param):
+    """Host plan -> device tensors, workspace sized by pkv_workspace_size."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    cfg = wl.cfg
+    tasks, offs, slots = pkv.pkv_plan(wl.seq_lens_np, cfg.Hkv, cfg.max_pages_per_row, mode, param,
+                                      block_table=wl.block_table_np,
+                                      num_pages=wl.k_pool.shape[0])
+    t_d = torch.from_numpy(tasks).cuda()
+    o_d = torch.from_numpy(offs).cuda()
+    ws = torch.zeros(pkv.pkv_workspace_size(slots, cfg.Hq, cfg.D), dtype=torch.uint8,
+                     device="cuda")
+    pkv.pkv_workspace_init(ws)
+    out = torch.full_like(wl.q, float("nan"))
+    lse = torch.full((wl.q.shape[0], cfg.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    return t_d, o_d, slots, ws, out, lse
+
+
+@pytest.mark.parametrize("name,mode,param", [("tiny", 0, 4), ("b1", 0, 32), ("b8_bimodal", 1, 128),
+                                             ("b8_bimodal", 1, 16)])
+def test_one_shot_entry_points(name, mode, param):
+    """pkv_decode (merge fused), and pkv_decode_splits then pkv_merge, on
+    caller-owned buffers: each matches the oracle, and the two give the same
+    bits."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    log_case("one-shot", name, "mode", mode, "param", param)
+    wl = make_workload(name, SEED, device="cuda")
+    cfg = wl.cfg
+    ref, ref_lse = oracle_rows(wl)
+    t_d, o_d, slots, ws, out, lse = _caller_owned(wl, mode, param)
+    pkv.pkv_decode(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, t_d, o_d, slots,
+                   cfg.scale, out, ws, lse=lse)
+    torch.cuda.synchronize()
+    a, la = out.cpu().numpy().copy(), lse.cpu().numpy().copy()
+    check_close(a.astype(np.float64), ref)
+    check_lse(la, ref_lse)
+    assert pkv.pkv_workspace_error_flags(ws) == 0
+    t_d, o_d, slots, ws2, out2, lse2 = _caller_owned(wl, mode, param)
+    pkv.pkv_decode_splits(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, t_d, o_d,
+                          slots, cfg.scale, out2, ws2, lse=lse2)
+    pkv.pkv_merge(o_d, slots, cfg.Hkv, out2, ws2, lse=lse2)
+    torch.cuda.synchronize()
+    assert np.array_equal(a, out2.cpu().numpy())
+    assert np.array_equal(la, lse2.cpu().numpy())
+    assert pkv.pkv_workspace_error_flags(ws2) == 0
+
+
+@pytest.mark.parametrize("name", ["b1", "b8_bimodal"])
+def test_plan_and_decode(name):
+    """The plan() / decode() names: policy, plan and one step, both launch forms."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    wl = make_workload(name, SEED, device="cuda")
+    cfg = wl.cfg
+    p = pkv.plan(wl.seq_lens_np, cfg.Hkv, cfg.max_pages_per_row, head_dim=cfg.D,
+                 block_table=wl.block_table_np, num_pages=wl.k_pool.shape[0])
+    assert p.mode == (pkv.PKV_MODE_SPLIT if name == "b1" else pkv.PKV_MODE_WORKQUEUE)
+    ref, ref_lse = oracle_rows(wl)
+    for two in (False, True):
+        lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
+        out, _ = pkv.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, p,
+                            cfg.scale, lse=lse, two_launch=two)
+        torch.cuda.synchronize()
+        check_close(out.float().cpu().numpy(), ref)
+        check_lse(lse.cpu().numpy(), ref_lse)
+
+
+def test_runner_regrows_workspace_on_a_side_stream():
+    """A step on a non-current stream whose plan needs a bigger workspace:
+    the decoder waits for that stream before replacing the workspace; then
+    steps alternate between streams (reading the runner's device copy of the
+    plan on both) and every result equals that of a fresh decoder."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    cfg = wl.cfg
+    fresh = {}
+    for mode, param in ((1, 128), (1, 8)):
+        o, l, _ = run_hip(wl, mode, param)
+        fresh[(mode, param)] = (o.cpu().numpy(), l.cpu().numpy())
+    dec = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=cfg.B,
+                           max_pages_per_row=cfg.max_pages_per_row)
+    small = dec.workspace.numel()
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
+    dec.set_inputs(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, wl.seq_lens_np,
+                   cfg.scale, out, lse)
+    side = torch.cuda.Stream()
+    steps = [(side, 1, 128), (side, 1, 128), (None, 1, 128), (side, 1, 8), (side, 1, 8),
+             (None, 1, 8), (side, 1, 8), (None, 1, 128), (side, 1, 128)]
+    for st, mode, param in steps:
+        log_case("runner stream step", "side" if st is not None else "current", mode, param)
+        dec.run(mode, param, stream=st)
+        (st or torch.cuda.current_stream()).synchronize()
+        assert np.array_equal(out.cpu().numpy(), fresh[(mode, param)][0])
+        assert np.array_equal(lse.cpu().numpy(), fresh[(mode, param)][1])
+    assert dec.workspace.numel() > small
+    assert dec.error_flags() == 0
