@@ -17,7 +17,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIB_PATH selects another build of the same library (the host-side
+# sanitizer build of paged_gqa_decode_pkv_amd/sanitize.py).
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(_HERE, "libpkv.so")
 
 PKV_ABI_VERSION = 5               # include/pkv.h; the argument lists below follow it
 PKV_OK = 0

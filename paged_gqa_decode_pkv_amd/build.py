@@ -49,24 +49,37 @@ def _run(cmd, verbose):
         sys.stderr.write(r.stderr)
 
 
-def build(verbose: bool = False, asm: bool = False) -> str:
+# Host-side sanitizers for the CPU checks of the planner, the policy, the
+# runner and the entry points' argument handling (sanitize=True).  Every
+# -fsanitize= goes to the host compilation only (-Xarch_host): the device code
+# of the kernels is built as usual.  The result is a separate library under
+# _build/sanitize/, loaded through PKV_LIB_PATH with the clang ASan runtime
+# preloaded (see paged_gqa_decode_pkv_amd/sanitize.py); it is never run on a GPU.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, asm: bool = False, sanitize: bool = False) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    common = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall"]
+    out_dir = os.path.join(BUILD_DIR, "sanitize") if sanitize else BUILD_DIR
+    os.makedirs(out_dir, exist_ok=True)
+    common = ["-O1" if sanitize else "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall"]
+    if sanitize:
+        common += SANITIZE_FLAGS
     objs = []
-    plan_o = os.path.join(BUILD_DIR, "plan.o")
+    plan_o = os.path.join(out_dir, "plan.o")
     # The policy's cost model must round every product and sum on its own
     # (its decisions are compared bit for bit with the reference): no FMA
     # contraction in the host planner.
     _run([hipcc, "-x", "c++", *common, "-ffp-contract=off", "-c",
           os.path.join(CSRC, "plan.cpp"), "-o", plan_o], verbose)
     objs.append(plan_o)
-    run_o = os.path.join(BUILD_DIR, "runner.o")
+    run_o = os.path.join(out_dir, "runner.o")
     rocm_inc = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc))), "include")
     _run([hipcc, "-x", "c++", *common, "-D__HIP_PLATFORM_AMD__", "-I", rocm_inc, "-c",
           os.path.join(CSRC, "runner.cpp"), "-o", run_o], verbose)
     objs.append(run_o)
-    dec_o = os.path.join(BUILD_DIR, "decode.o")
+    dec_o = os.path.join(out_dir, "decode.o")
     _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS, "-c",
           os.path.join(CSRC, "decode.hip"), "-o", dec_o], verbose)
     objs.append(dec_o)
@@ -74,15 +87,19 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS,
               "--cuda-device-only", "-S", os.path.join(CSRC, "decode.hip"),
               "-o", os.path.join(BUILD_DIR, "decode-gfx950.s")], verbose)
-    tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    lib = os.path.join(out_dir, "libpkv.so") if sanitize else LIB
+    tmp = lib + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *(SANITIZE_FLAGS if sanitize else []),
+          *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", action="store_true")
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="host-side ASan/UBSan build under _build/sanitize/ (CPU checks only)")
     args = ap.parse_args()
-    print(build(verbose=args.verbose, asm=args.asm))
+    print(build(verbose=args.verbose, asm=args.asm, sanitize=args.sanitize))
