@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 /* Fixed-size head of every workspace: control words (task counter, exit
  * counter, error word) and the per-(row, KV head) arrival counters of the
@@ -65,7 +65,9 @@ enum pkv_status {
   PKV_ERR_UNSUPPORTED = 2,      /* head_dim, page_size or G outside the supported set */
   PKV_ERR_BUFFER_TOO_SMALL = 3, /* caller buffer too small; size outputs hold the need */
   PKV_ERR_BAD_INDEX = 4,        /* block-table entry outside [0, num_pages) */
-  PKV_ERR_HIP = 5               /* a HIP runtime call failed; see pkv_last_hip_error */
+  PKV_ERR_HIP = 5,              /* a HIP runtime call failed; see pkv_last_hip_error */
+  PKV_ERR_SCRATCH_TOO_SMALL = 6 /* pkv_decode_static: the step needs more than its static
+                                   workspace (PKV_STATIC_SCRATCH_BYTES) */
 };
 
 /* Element types of q and out (E) and of the K and V pools.  Scores, softmax
@@ -337,6 +339,39 @@ int pkv_decode(const void* q, const void* k_pool, const void* v_pool, int64_t nu
                int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size, int32_t dtype,
                float scale, float k_scale, float v_scale, void* out, float* lse,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_decode_static -- pkv_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.
+ *
+ * The step's workspace is a static device array of PKV_STATIC_SCRATCH_BYTES
+ * (16 MiB) in the library, one per GPU, held from the library's first use
+ * on that GPU until the process ends; its address is looked up once per
+ * device (the first call on it, with that device current).  Nothing is
+ * allocated or freed, here or later.  Every call first zeroes the array's
+ * control block and this step's arrival counters with a small kernel on
+ * `stream` (no memset), then runs pkv_decode's kernels on it.  Every call on
+ * one GPU shares that GPU's array, and the array keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads)
+ * race, so they must be ordered.  The device error word of the array is
+ * cleared by each call and not reported; check the block table on the host
+ * (pkv_plan with block_table) beforehand.
+ * Arguments, layouts and results: those of pkv_decode without workspace and
+ * workspace_bytes; the results are bit for bit pkv_decode's.
+ * Errors: those of pkv_decode, and PKV_ERR_SCRATCH_TOO_SMALL when
+ * pkv_workspace_size(num_partial_slots, Hq, head_dim) exceeds
+ * PKV_STATIC_SCRATCH_BYTES (checked on the host before anything is
+ * launched).
+ */
+#define PKV_STATIC_SCRATCH_BYTES (16u << 20)
+int pkv_decode_static(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
+                      const int32_t* block_table, int32_t max_pages_per_row,
+                      const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
+                      const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
+                      int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                      int32_t dtype, float scale, float k_scale, float v_scale, void* out,
+                      float* lse, void* stream);
 
 /*
  * pkv_decode_splits -- the first of pkv_decode's two launches: the persistent

@@ -21,13 +21,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # sanitizer build of paged_gqa_decode_pkv_amd/sanitize.py).
 LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(_HERE, "libpkv.so")
 
-PKV_ABI_VERSION = 5               # include/pkv.h; the argument lists below follow it
+PKV_ABI_VERSION = 6               # include/pkv.h; the argument lists below follow it
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = 1
 PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_BUFFER_TOO_SMALL = 3
 PKV_ERR_BAD_INDEX = 4
 PKV_ERR_HIP = 5
+PKV_ERR_SCRATCH_TOO_SMALL = 6
+PKV_STATIC_SCRATCH_BYTES = 16 << 20   # PKV_STATIC_SCRATCH_BYTES
 
 PKV_DTYPE_F16 = 0
 PKV_DTYPE_BF16 = 1
@@ -49,7 +51,8 @@ ABI_SYMBOLS = (
     "pkv_abi_version", "pkv_status_string", "pkv_last_hip_error", "pkv_page_load_mode",
     "pkv_policy_defaults",
     "pkv_policy", "pkv_policy_predict", "pkv_plan", "pkv_workspace_size", "pkv_workspace_init",
-    "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_splits", "pkv_merge",
+    "pkv_workspace_error_flags", "pkv_decode", "pkv_decode_static", "pkv_decode_splits",
+    "pkv_merge",
     "pkv_workspace_size_device_plan", "pkv_decode_device_plan", "pkv_device_plan_read",
     "pkv_runner_create", "pkv_runner_step", "pkv_runner_destroy", "pkv_runner_last_plan",
 )
@@ -149,6 +152,7 @@ def _load():
                                  ctypes.c_int),
     }
     sig["pkv_decode_splits"] = sig["pkv_decode"]
+    sig["pkv_decode_static"] = (sig["pkv_decode"][0][:-3] + [_vp], ctypes.c_int)
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -369,8 +373,8 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
         _dev(split_offsets, i32, "split_offsets"), num_partial_slots, B, Hq, Hkv, D, P, code,
         float(scale), float(k_scale), float(v_scale), _dev(out, f16, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None,
-        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_ptr(stream),
-    )
+    ) + ((_dev(workspace, torch.uint8, "workspace"), workspace.numel())
+         if workspace is not None else ()) + (_stream_ptr(stream),)
     return args
 
 
@@ -381,6 +385,16 @@ def pkv_decode(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
     args = _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
                         num_partial_slots, scale, out, workspace, lse, stream, k_scale, v_scale)
     _check(_load().pkv_decode(*args), "pkv_decode")
+
+
+def pkv_decode_static(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+                      num_partial_slots: int, scale: float, out, lse=None, stream=None,
+                      k_scale: float = 1.0, v_scale: float = 1.0):
+    """pkv_decode on the library's static workspace (no workspace argument, no
+    allocation); see pkv_decode_static in include/pkv.h."""
+    args = _decode_args(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,
+                        num_partial_slots, scale, out, None, lse, stream, k_scale, v_scale)
+    _check(_load().pkv_decode_static(*args), "pkv_decode_static")
 
 
 def pkv_decode_splits(q, k_pool, v_pool, block_table, seq_lens, tasks, split_offsets,

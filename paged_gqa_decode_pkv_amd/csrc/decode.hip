@@ -55,6 +55,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "pkv.h"
@@ -1855,6 +1856,103 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
   return run(nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, 0, split_offsets,
              num_partial_slots, B, Hq, Hkv, head_dim, pkv::kPage, dtype, 1.0f, 1.0f, 1.0f, out,
              lse, workspace, workspace_bytes, stream, false, true, false);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// pkv_decode_static: pkv_decode with its workspace in a static device array,
+// for callers that cannot allocate (graph capture, serving loops, harnesses
+// that forbid it).
+
+namespace pkv {
+
+// The workspace of one step (control block, arrival counters, partial
+// states), one copy per GPU, held until the process ends.
+constexpr size_t kStaticScratchBytes = PKV_STATIC_SCRATCH_BYTES;
+static_assert(4 * (64 + PKV_MAX_FUSED_GROUPS) <= PKV_WORKSPACE_HEADER_BYTES,
+              "the zeroed control words lie in the header");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Zero n 32-bit words at p: the control block and the arrival counters of
+// the static workspace before each step (a kernel rather than a memset, so
+// that a captured graph replays it as an ordinary kernel node).
+__global__ void __launch_bounds__(256) pkv_zero_kernel(uint32_t* p, int n) {
+  for (int i = static_cast<int>(blockIdx.x * 256 + threadIdx.x); i < n;
+       i += static_cast<int>(gridDim.x * 256))
+    p[i] = 0u;
+}
+
+// Device address of `scratch` on the current device.  In host code the
+// array's name only stands for the symbol, so it is never passed to a
+// kernel: its address is looked up once per device, with that device
+// current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_hip_error(static_cast<int>(e));
+    return PKV_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_hip_error(static_cast<int>(e));
+      return PKV_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+int pkv_decode_static(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
+                      const int32_t* block_table, int32_t max_pages_per_row,
+                      const int32_t* seq_lens, const int32_t* tasks, int64_t num_tasks,
+                      const int32_t* split_offsets, int64_t num_partial_slots, int32_t B,
+                      int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t page_size,
+                      int32_t dtype, float scale, float k_scale, float v_scale, void* out,
+                      float* lse, void* stream) {
+  size_t need = 0;
+  if (pkv_workspace_size(num_partial_slots, Hq, head_dim, &need) != PKV_OK)
+    return PKV_ERR_INVALID_ARG;
+  if (need > pkv::kStaticScratchBytes) return PKV_ERR_SCRATCH_TOO_SMALL;
+  if (B <= 0 || Hkv < 1) {
+    // nothing to launch (B == 0), or invalid; the checks of run() decide
+    return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
+               num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size,
+               dtype, scale, k_scale, v_scale, out, lse, nullptr, 0, stream, true, true, true);
+  }
+  void* ws = nullptr;
+  int st = pkv::static_scratch(&ws);
+  if (st != PKV_OK) return st;
+  // the control block and this step's arrival counters start at zero
+  const int64_t groups = static_cast<int64_t>(B) * Hkv;
+  const int n = 64 + static_cast<int>(groups < PKV_MAX_FUSED_GROUPS ? groups
+                                                                     : PKV_MAX_FUSED_GROUPS);
+  const int blocks = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+  hipLaunchKernelGGL(pkv::pkv_zero_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint32_t*>(ws), n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    pkv::set_hip_error(static_cast<int>(e));
+    return PKV_ERR_HIP;
+  }
+  return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
+             num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
+             scale, k_scale, v_scale, out, lse, ws, pkv::kStaticScratchBytes, stream, true, true,
+             true);
 }
 
 }  // extern "C"

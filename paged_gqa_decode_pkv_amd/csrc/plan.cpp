@@ -41,6 +41,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_BUFFER_TOO_SMALL: return "buffer too small";
     case PKV_ERR_BAD_INDEX: return "block-table entry outside the page pool";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_SCRATCH_TOO_SMALL:
+      return "step larger than the static workspace of pkv_decode_static (16 MiB)";
     default: return "unknown status";
   }
 }
