@@ -108,11 +108,13 @@ typedef struct pkv_policy_params {
   int32_t split_max;        /* split candidates S = 1, 2, 4, ... <= split_max */
   int32_t chunk_min;        /* workqueue candidates c = chunk_min, 2 chunk_min, ... */
   int32_t chunk_max;        /*   ... <= chunk_max, in pages */
-  int32_t fuse_max_splits;  /* step runner: the fused single launch when no row
-                               has more splits than this, else the two-launch
-                               form (the fused merge runs at the tail of a
-                               split group, so long groups favour the separate
-                               merge kernel) */
+  int32_t fuse_max_splits;  /* the fused single launch when no row has more
+                               splits than this, ... */
+  int32_t fuse_max_group_splits; /* ... or when (row, KV head) groups x the deepest
+                               row's splits is at most this; else the two-launch
+                               form (the fused merge runs at the tail of a split
+                               group, one group per workgroup, so many long
+                               groups favour the separate merge kernel) */
   /* cost model of one step (microseconds, GB/s) */
   double t0_us;             /* fixed time of a step */
   double t_round_us;        /* per round of tasks, ceil(T / W) */
@@ -149,7 +151,7 @@ const char* pkv_status_string(int status);
 int pkv_last_hip_error(void);
 
 /* Fill *params with the default policy constants: split_max 256, chunks
- * 4..256, fuse_max_splits 16, and the cost model fitted on seed 20260622 of
+ * 4..256, fuse_max_splits 16, fuse_max_group_splits 256, and the cost model fitted on seed 20260622 of
  * the calibration traces on one MI355X (256 CUs): every candidate schedule of
  * eight trace families (B = 1 fixed and bucketed, 4, 8 bimodal / Zipf /
  * uniform, 32, 64) timed on the GPU, least squares on log time.  Returns
@@ -186,9 +188,10 @@ int pkv_policy_defaults(pkv_policy_params* params);
  *   tile = 2 * page_size * head_dim * 2 bytes (K and V of one page of one
  *          KV head, 2-byte elements; for fp8 pools the callers here pass
  *          head_dim / 2, the same bytes),
+ *   two = maxS > fuse_max_splits and Gr maxS > fuse_max_group_splits, with
+ *         Gr = Hkv x (rows with n_b > 0) the (row, KV head) groups,
  *   t = t0_us + t_round_us ceil(T / W) + load tile / (rho 1e3)
- *       + (maxS > fuse_max_splits ? t_two_us + t_two_split_us maxS
- *                                 : t_fused_split_us maxS).
+ *       + (two ? t_two_us + t_two_split_us maxS : t_fused_split_us maxS).
  * All in double precision, in this order of operations (pkv_policy_predict
  * returns t).  No active row gives (SPLIT, 1).
  *
@@ -197,15 +200,16 @@ int pkv_policy_defaults(pkv_policy_params* params);
  * Errors: PKV_ERR_INVALID_ARG for a NULL pointer, B < 0, Hkv < 1,
  * head_dim < 1, page_size < 1, num_cus < 1, a negative length or parameters
  * outside their domain (split_max < 1, chunk_min < 1, chunk_max < chunk_min,
- * fuse_max_splits < 0, a rate <= 0, a negative time or alpha).
+ * fuse_max_splits < 0, fuse_max_group_splits < 0, a rate <= 0, a negative
+ * time or alpha).
  */
 int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
                int32_t page_size, int32_t num_cus, const pkv_policy_params* params,
                int32_t* mode, int32_t* param);
 
 /* The model time t (microseconds) of one candidate (mode, param) of
- * pkv_policy, for tools and tests.  two_launch < 0 applies the
- * fuse_max_splits rule; 0 / 1 force the fused / two-launch term.  Same
+ * pkv_policy, for tools and tests.  two_launch < 0 applies the policy's
+ * launch-form rule (`two` above); 0 / 1 force the fused / two-launch term.  Same
  * arguments and errors as pkv_policy, plus PKV_ERR_INVALID_ARG for an unknown
  * mode or param < 1. */
 int pkv_policy_predict(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim,
@@ -429,10 +433,12 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
  *      writes the plan out for pkv_device_plan_read);
  *   B > 1024: a one-workgroup planner kernel, then the decode kernel reading
  *      the task count from the header;
- *   then, unless max_splits <= fuse_max_splits (every plan is then fused),
+ *   then, unless the launch-form rule (below pkv_policy_params) is fused
+ *      for maxS = max_splits and B * Hkv groups (every plan is then fused),
  *      the merge kernel, which returns at once when the header says the
- *      decode kernel merged (the fused form: no row deeper than
- *      policy->fuse_max_splits and B * Hkv <= PKV_MAX_FUSED_GROUPS).
+ *      decode kernel merged (the fused form: the rule fused on the plan's
+ *      own deepest row and active groups, and B * Hkv <=
+ *      PKV_MAX_FUSED_GROUPS).
  * Arguments as for pkv_decode, except:
  *   seq_lens     device int32 [B]; a row with N_b < 0 or needing more than
  *                max_pages_per_row pages is planned as empty (out = 0,
@@ -515,7 +521,8 @@ typedef struct pkv_step_args {
   int32_t param;                 /* S or c for an explicit mode */
   int32_t two_launch;            /* 0: pkv_decode (one launch, merge fused);
                                     1: pkv_decode_splits then pkv_merge;
-                                    -1: choose by the policy's fuse_max_splits */
+                                    -1: the policy's rule (fuse_max_splits,
+                                        fuse_max_group_splits) */
   /* device inputs, laid out as for pkv_decode */
   const void* q;
   const void* k_pool;
@@ -540,10 +547,12 @@ typedef struct pkv_step_args {
   void* stream;                  /* hipStream_t */
   void* event_before_decode;     /* optional hipEvent_t pair (created by the caller)
                                     that takes the decode kernel's own start ... */
-  void* event_after_decode;      /* ... and end timestamps (hipExtLaunchKernel); either
-                                    may be NULL.  In the two-launch form the merge
-                                    kernel comes after the end.  A step without tasks
-                                    records them where the kernel would have run. */
+  void* event_after_decode;      /* ... and the end timestamp of the step's last kernel
+                                    (hipExtLaunchKernel): the decode kernel, or the
+                                    merge kernel in the two-launch form, so the pair
+                                    spans the whole step on the GPU.  Either may be
+                                    NULL.  A step without tasks records them where
+                                    the decode kernel would have run. */
   /* outputs */
   int32_t chosen_mode;
   int32_t chosen_param;

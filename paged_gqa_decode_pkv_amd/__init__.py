@@ -71,6 +71,7 @@ class pkv_policy_params(ctypes.Structure):
     """Mirror of pkv_policy_params in include/pkv.h."""
     _fields_ = [("split_max", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
                 ("chunk_max", ctypes.c_int32), ("fuse_max_splits", ctypes.c_int32),
+                ("fuse_max_group_splits", ctypes.c_int32),
                 ("t0_us", ctypes.c_double), ("t_round_us", ctypes.c_double),
                 ("alpha", ctypes.c_double), ("cu_gbps", ctypes.c_double),
                 ("hbm_gbps", ctypes.c_double), ("t_two_us", ctypes.c_double),
@@ -559,7 +560,8 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, plan: Plan, scale: Optional
            params: Optional[pkv_policy_params] = None):
     """One decode step on a plan: pkv_decode (merge fused), or
     pkv_decode_splits then pkv_merge when ``two_launch`` (None: the policy's
-    rule, more than fuse_max_splits splits in a row).  ``workspace`` (uint8,
+    rule: the deepest row has more than fuse_max_splits splits and the (row,
+    KV head) groups times those splits exceed fuse_max_group_splits).  ``workspace`` (uint8,
     >= pkv_workspace_size, zeroed once by pkv_workspace_init) is made here
     when not given.  Returns (out, lse)."""
     import torch
@@ -574,7 +576,9 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, plan: Plan, scale: Optional
         pkv_workspace_init(workspace, stream)
     if two_launch is None:
         p = params if params is not None else pkv_policy_defaults()
-        two_launch = plan.max_splits > p.fuse_max_splits
+        groups = k_pool.shape[1] * int(np.count_nonzero(np.diff(plan.offsets_host)))
+        two_launch = (plan.max_splits > p.fuse_max_splits and
+                      groups * plan.max_splits > p.fuse_max_group_splits)
     args = (q, k_pool, v_pool, block_table, seq_lens, plan.tasks, plan.split_offsets,
             plan.num_partial_slots, scale, out, workspace)
     if two_launch:
@@ -669,7 +673,7 @@ class PagedDecoder:
         torch.cuda.Event pair that takes the decode kernel's start and end
         timestamps (either may be None), or None.  ``two_launch``: True =
         separate merge kernel, False = fused single launch, None = the
-        policy's choice (fuse_max_splits)."""
+        policy's rule (fuse_max_splits, fuse_max_group_splits)."""
         import torch
         a = self.args
         a.two_launch = -1 if two_launch is None else (1 if two_launch else 0)

@@ -646,6 +646,7 @@ __device__ __forceinline__ void plan_shape_add(PlanShape& f, int32_t n, int32_t 
   const uint32_t S = cdiv32(un, c);
   f.T += static_cast<int64_t>(Hkv) * S;
   f.P += static_cast<int64_t>(Hkv) * un;
+  f.groups += Hkv;
   const int64_t largest = c < un ? c : un;
   if (largest > f.pmax) f.pmax = largest;
   if (static_cast<int64_t>(S) > f.maxS) f.maxS = S;
@@ -665,6 +666,7 @@ struct CandLds {
   int64_t P[kCandGroups][kCandBatch];
   int64_t pmax[kCandGroups][kCandBatch];
   int64_t maxS[kCandGroups][kCandBatch];
+  int64_t groups[kCandGroups][kCandBatch];
   double t[kCandBatch];
   int64_t pages;
   int pick[2];
@@ -717,6 +719,7 @@ __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_
     L.P[grp][j] = f.P;
     L.pmax[grp][j] = f.pmax;
     L.maxS[grp][j] = f.maxS;
+    L.groups[grp][j] = f.groups;
     __syncthreads();
     if (tid < kCandBatch && i < c_hi) {
       PlanShape F;
@@ -725,8 +728,10 @@ __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_
         F.P += L.P[r][j];
         F.pmax = L.pmax[r][j] > F.pmax ? L.pmax[r][j] : F.pmax;
         F.maxS = L.maxS[r][j] > F.maxS ? L.maxS[r][j] : F.maxS;
+        F.groups += L.groups[r][j];
       }
-      L.t[j] = model_us(p, F, num_cus, head_dim, page_size, F.maxS > p.fuse_max_splits);
+      L.t[j] = model_us(p, F, num_cus, head_dim, page_size,
+                        two_launch_form(p, F.maxS, F.groups));
       if (j == 0) L.pages = F.P;
     }
     __syncthreads();
@@ -940,7 +945,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ int s_lastf[kMaxDone];
   // self-planned step only: the policy's candidate search and the row scan
   __shared__ typename std::conditional<kSelfPlan, CandLds, char>::type s_cand;
-  __shared__ int s_plan[kSelfPlan ? 2 * kWaves + 2 : 1];
+  __shared__ int s_plan[kSelfPlan ? 3 * kWaves + 2 : 1];
   static_assert(kWaves * kGroup * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
   static_assert(!kSelfPlan || kStaged, "a self-planned step stages its rows");
 
@@ -990,7 +995,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     // splits per row, then their exclusive prefix: thread t takes rows
     // kRows*t .. kRows*t + kRows-1
     int sv[kRows];
-    int sum = 0, mx = 0;
+    int sum = 0, mx = 0, act = 0;
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
       const int b = kRows * tid + k;
@@ -1006,7 +1011,11 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       sv[k] = S;
       sum += S;
       mx = S > mx ? S : mx;
+      act += S > 0 ? 1 : 0;
     }
+    int wact = act;   // rows with work, summed over the wave
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wact += __shfl_xor(wact, off);
     int incl = sum;   // inclusive scan over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1016,14 +1025,16 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const int wmax = static_cast<int>(wave_max64(mx));
     if (lane == 63) s_plan[wave] = incl;
     if (lane == 0) s_plan[kWaves + wave] = wmax;
+    if (lane == 0) s_plan[2 * kWaves + wave] = wact;
     __syncthreads();
     int base = incl - sum;
-    int total = 0, maxS = 0;
+    int total = 0, maxS = 0, active_rows = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       if (w < wave) base += s_plan[w];
       total += s_plan[w];
       maxS = s_plan[kWaves + w] > maxS ? s_plan[kWaves + w] : maxS;
+      active_rows += s_plan[2 * kWaves + w];
     }
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
@@ -1033,7 +1044,11 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     }
     if (tid == 0) s_off[a.B] = total;
     num_tasks = a.Hkv * total;
-    fuse = (num_tasks == 0 || (maxS <= a.plan_pol.fuse_max_splits && a.plan_groups_fit)) ? 1 : 0;
+    fuse = (num_tasks == 0 ||
+            (!two_launch_form(a.plan_pol, maxS, static_cast<int64_t>(a.Hkv) * active_rows) &&
+             a.plan_groups_fit))
+               ? 1
+               : 0;
     __syncthreads();
     if (blockIdx.x == 0) {
       for (int b = tid; b <= a.B; b += kThreads) a.plan_offs_out[b] = s_off[b];
@@ -1429,6 +1444,7 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   __shared__ int s_S[kThreads];
   __shared__ int s_c[kThreads];
   __shared__ int s_bad;
+  __shared__ int s_active;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -1442,7 +1458,10 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
     s_n[b] = n < 0 ? 0 : n;
   }
   for (int b = staged + tid; b < a.B; b += kThreads) bad |= plan_row_pages_global(a, b) < 0;
-  if (tid == 0) s_bad = 0;
+  if (tid == 0) {
+    s_bad = 0;
+    s_active = 0;
+  }
   __syncthreads();
   if (bad) s_bad = 1;
   auto row_n = [&](int b) -> int32_t {
@@ -1460,6 +1479,7 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   // ---- 2. split offsets and records, 256 rows at a time
   int carry = 0;
   int maxS = 0;
+  int act = 0;   // rows with work seen by this thread
   for (int base = 0; base < a.B; base += kThreads) {
     const int b = base + tid;
     int S = 0, c = 0;
@@ -1471,6 +1491,7 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
       }
     }
     maxS = S > maxS ? S : maxS;
+    act += S > 0 ? 1 : 0;
     s_S[tid] = S;
     s_c[tid] = c;
     s_scan[tid] = S;
@@ -1501,13 +1522,17 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   // ---- 3. header
   const int deep_w = static_cast<int>(wave_max64(maxS));
   if (lane == 0) s_best_i[wave] = deep_w;
+  if (act > 0) atomicAdd(&s_active, act);
   __syncthreads();
   if (tid == 0) {
     int deep = 0;
     for (int w = 0; w < kWaves; ++w) deep = s_best_i[w] > deep ? s_best_i[w] : deep;
     const int T = a.Hkv * carry;
     a.hdr[0] = T;
-    a.hdr[1] = (T == 0 || (deep <= a.pol.fuse_max_splits && a.groups_fit)) ? 1 : 0;
+    a.hdr[1] = (T == 0 || (!two_launch_form(a.pol, deep, static_cast<int64_t>(a.Hkv) * s_active) &&
+                           a.groups_fit))
+                   ? 1
+                   : 0;
     a.hdr[2] = mode;
     a.hdr[3] = param;
     a.hdr[4] = carry;
@@ -1550,6 +1575,9 @@ int num_cus_of_current_device(int* cus) {
 template <int D, class E, class KV, int kMode>
 int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t stream,
               bool decode, hipEvent_t ev0, hipEvent_t ev1) {
+  // With a merge kernel behind the decode kernel, the end event takes the
+  // merge kernel's end: the events then span the whole step.
+  const hipEvent_t ev_dec_end = ma.B > 0 ? nullptr : ev1;
   if (decode) {
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     const bool staged = da.B <= kRowStage;
@@ -1558,15 +1586,15 @@ int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t
       hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true, kMode == 2 ? 1 : kMode>),
                          dim3(grid), dim3(kThreads), 0, stream, da, tasks, da.block_table,
                          da.seq_lens, da.split_offsets);
-    } else if (ev0 || ev1) {
+    } else if (ev0 || ev_dec_end) {
       if (staged)
         hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
-                              dim3(kThreads), 0, stream, ev0, ev1, 0, da, tasks, da.block_table,
-                              da.seq_lens, da.split_offsets);
+                              dim3(kThreads), 0, stream, ev0, ev_dec_end, 0, da, tasks,
+                              da.block_table, da.seq_lens, da.split_offsets);
       else
         hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kMode>), dim3(grid),
-                              dim3(kThreads), 0, stream, ev0, ev1, 0, da, tasks, da.block_table,
-                              da.seq_lens, da.split_offsets);
+                              dim3(kThreads), 0, stream, ev0, ev_dec_end, 0, da, tasks,
+                              da.block_table, da.seq_lens, da.split_offsets);
     } else if (staged) {
       hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
                          dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
@@ -1579,7 +1607,7 @@ int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t
   } else {
     // no decode kernel (no tasks): the events still mark this point of the stream
     if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return PKV_ERR_HIP;
-    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return PKV_ERR_HIP;
+    if (ev_dec_end && hipEventRecord(ev_dec_end, stream) != hipSuccess) return PKV_ERR_HIP;
   }
   if (decode) {
     hipError_t e = hipGetLastError();
@@ -1589,8 +1617,13 @@ int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t
     }
   }
   if (ma.B > 0) {
-    hipLaunchKernelGGL((pkv_merge_kernel<D, E>), dim3(ma.B * ma.Hkv * merge_kernel_blocks<D>(ma.G)),
-                       dim3(kMergeKernelThreads), 0, stream, ma);
+    const dim3 mgrid(ma.B * ma.Hkv * merge_kernel_blocks<D>(ma.G));
+    if (ev1)
+      hipExtLaunchKernelGGL((pkv_merge_kernel<D, E>), mgrid, dim3(kMergeKernelThreads), 0,
+                            stream, nullptr, ev1, 0, ma);
+    else
+      hipLaunchKernelGGL((pkv_merge_kernel<D, E>), mgrid, dim3(kMergeKernelThreads), 0, stream,
+                         ma);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       set_hip_error(static_cast<int>(e));
@@ -1818,7 +1851,7 @@ int decode_timed(const void* q, const void* k_pool, const void* v_pool, int64_t 
                  bool fused, void* ev0, void* ev1) {
   return run(q, k_pool, v_pool, num_pages, block_table, max_pages_per_row, seq_lens, tasks,
              num_tasks, split_offsets, num_partial_slots, B, Hq, Hkv, head_dim, page_size, dtype,
-             scale, k_scale, v_scale, out, lse, workspace, workspace_bytes, stream, true, fused,
+             scale, k_scale, v_scale, out, lse, workspace, workspace_bytes, stream, true, true,
              fused, ev0, ev1);
 }
 }  // namespace pkv
@@ -2016,7 +2049,8 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   if (mode < -1 || mode > PKV_MODE_WORKQUEUE || max_splits < 1 || max_pages_per_row < 0)
     return PKV_ERR_INVALID_ARG;
   if (pol.split_max < 1 || pol.chunk_min < 1 || pol.chunk_max < pol.chunk_min ||
-      pol.fuse_max_splits < 0 || !(pol.cu_gbps > 0.0) || !(pol.hbm_gbps > 0.0))
+      pol.fuse_max_splits < 0 || pol.fuse_max_group_splits < 0 || !(pol.cu_gbps > 0.0) ||
+      !(pol.hbm_gbps > 0.0))
     return PKV_ERR_INVALID_ARG;
   // Capacity: no row may get more than max_splits splits.  Checked on the
   // host from max_pages_per_row alone, so the device never overruns.
@@ -2100,10 +2134,13 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   // The task count is known only on the device: one workgroup per CU (as
   // fast as two per CU on the measured workloads, and with no pair of
   // workgroups sharing a CU while others idle); workgroups past the count
-  // exit at once.  With a capacity of at most fuse_max_splits splits per row
-  // every plan is fused, and the merge kernel is not launched at all.
+  // exit at once.  When the launch-form rule is fused at the capacity's
+  // bounds (max_splits splits, B * Hkv groups) it is fused for every plan the
+  // capacity admits (the rule only grows with either), and the merge kernel
+  // is not launched at all.
   const int grid = num_cus;
-  if (max_splits <= pol.fuse_max_splits && pa.groups_fit) ma.B = 0;
+  if (!pkv::two_launch_form(pol, max_splits, static_cast<int64_t>(B) * Hkv) && pa.groups_fit)
+    ma.B = 0;
   return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true,
                          pkv::load_mode(head_dim, dtype, -1, num_cus));
 }

@@ -10,9 +10,10 @@ namespace pkv {
 // Record the hipError_t behind a PKV_ERR_HIP for pkv_last_hip_error (per thread).
 void set_hip_error(int e);
 
-// pkv_decode (fused) or pkv_decode_splits (not fused), with optional events
-// ev0 / ev1 (hipEvent_t) that take the decode kernel's own start and end
-// timestamps (hipExtLaunchKernel).  Used by the step runner.
+// pkv_decode (fused), or pkv_decode_splits then pkv_merge (not fused), with
+// optional events ev0 / ev1 (hipEvent_t) that take the decode kernel's own
+// start timestamp and the step's last kernel's own end timestamp
+// (hipExtLaunchKernel).  Used by the step runner.
 int decode_timed(const void* q, const void* k_pool, const void* v_pool, int64_t num_pages,
                  const int32_t* block_table, int32_t max_pages_per_row, const int32_t* seq_lens,
                  const int32_t* tasks, int64_t num_tasks, const int32_t* split_offsets,

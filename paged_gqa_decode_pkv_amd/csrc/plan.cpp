@@ -53,6 +53,7 @@ int pkv_policy_defaults(pkv_policy_params* p) {
   p->chunk_min = 4;
   p->chunk_max = 256;
   p->fuse_max_splits = 16;
+  p->fuse_max_group_splits = 256;
   // Fitted on the calibration seed (paged_gqa_decode_pkv_amd/calibration/
   // mi355x_fit.json, written by policy_fit.py from calibrate.py's runs).
   p->t0_us = 0.0;
@@ -86,7 +87,8 @@ int check_policy_args(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t h
                       int32_t page_size, int32_t num_cus, const pkv_policy_params& p) {
   if (B < 0 || (B > 0 && !seq_lens) || Hkv < 1 || head_dim < 1 || page_size < 1 || num_cus < 1)
     return PKV_ERR_INVALID_ARG;
-  if (p.split_max < 1 || p.chunk_min < 1 || p.chunk_max < p.chunk_min || p.fuse_max_splits < 0)
+  if (p.split_max < 1 || p.chunk_min < 1 || p.chunk_max < p.chunk_min || p.fuse_max_splits < 0 ||
+      p.fuse_max_group_splits < 0)
     return PKV_ERR_INVALID_ARG;
   if (!(p.cu_gbps > 0.0) || !(p.hbm_gbps > 0.0) || !(p.t0_us >= 0.0) ||
       !(p.t_round_us >= 0.0) || !(p.alpha >= 0.0) || !(p.t_two_us >= 0.0) ||
@@ -115,7 +117,7 @@ int pkv_policy_predict(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t 
   const int st = check_policy_args(seq_lens, B, Hkv, head_dim, page_size, num_cus, p);
   if (st != PKV_OK) return st;
   const PlanShape f = plan_shape(seq_lens, B, Hkv, page_size, mode, param);
-  const bool two = two_launch < 0 ? f.maxS > p.fuse_max_splits : two_launch != 0;
+  const bool two = two_launch < 0 ? pkv::two_launch_form(p, f.maxS, f.groups) : two_launch != 0;
   *us = model_us(p, f, num_cus, head_dim, page_size, two);
   return PKV_OK;
 }
@@ -146,7 +148,8 @@ int pkv_policy(const int32_t* seq_lens, int32_t B, int32_t Hkv, int32_t head_dim
   double best = 0.0;
   auto consider = [&](int32_t m, int64_t v) {
     const PlanShape f = plan_shape(seq_lens, B, Hkv, page_size, m, v);
-    const double t = model_us(p, f, num_cus, head_dim, page_size, f.maxS > p.fuse_max_splits);
+    const double t =
+        model_us(p, f, num_cus, head_dim, page_size, pkv::two_launch_form(p, f.maxS, f.groups));
     if (!have || t < best) {
       have = true;
       best = t;

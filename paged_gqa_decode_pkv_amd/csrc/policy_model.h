@@ -22,10 +22,11 @@ namespace pkv {
 
 // What the model needs to know about a plan.
 struct PlanShape {
-  int64_t T = 0;      // tasks
-  int64_t P = 0;      // page tiles (page x KV head) in all
-  int64_t pmax = 0;   // pages of the largest task
-  int64_t maxS = 0;   // splits of the deepest row
+  int64_t T = 0;       // tasks
+  int64_t P = 0;       // page tiles (page x KV head) in all
+  int64_t pmax = 0;    // pages of the largest task
+  int64_t maxS = 0;    // splits of the deepest row
+  int64_t groups = 0;  // (row, KV head) groups with work
 };
 
 PKV_HOST_DEVICE inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -38,9 +39,18 @@ PKV_HOST_DEVICE inline void shape_add_row(PlanShape& f, int64_t n, int32_t Hkv, 
   const int64_t S = cdiv(n, c);
   f.T += Hkv * S;
   f.P += Hkv * n;
+  f.groups += Hkv;
   const int64_t largest = c < n ? c : n;
   if (largest > f.pmax) f.pmax = largest;
   if (S > f.maxS) f.maxS = S;
+}
+
+// The launch form of a plan of shape f: two launches (decode kernel, then
+// merge kernel) when its deepest row has more than fuse_max_splits splits
+// and its groups times those splits exceed fuse_max_group_splits.
+PKV_HOST_DEVICE inline bool two_launch_form(const pkv_policy_params& p, int64_t maxS,
+                                            int64_t groups) {
+  return maxS > p.fuse_max_splits && groups * maxS > p.fuse_max_group_splits;
 }
 
 // Model time (microseconds) of one step of a plan of shape f.  `two`: the

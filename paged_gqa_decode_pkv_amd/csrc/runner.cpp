@@ -28,6 +28,7 @@
 
 #include "pkv.h"
 #include "internal.h"
+#include "policy_model.h"
 
 namespace {
 
@@ -267,10 +268,14 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   if (st != PKV_OK) return st;
   for (size_t i = static_cast<size_t>(a->B) + 1; i < off_words; ++i) offs_h[i] = 0;
   int32_t max_splits = 0;
-  for (int32_t b = 0; b < a->B; ++b)
-    if (offs_h[b + 1] - offs_h[b] > max_splits) max_splits = offs_h[b + 1] - offs_h[b];
+  int64_t active_groups = 0;
+  for (int32_t b = 0; b < a->B; ++b) {
+    const int32_t sb = offs_h[b + 1] - offs_h[b];
+    if (sb > max_splits) max_splits = sb;
+    if (sb > 0) active_groups += a->Hkv;
+  }
   a->max_splits = max_splits;
-  const bool two = a->two_launch < 0 ? (max_splits > r->params.fuse_max_splits)
+  const bool two = a->two_launch < 0 ? pkv::two_launch_form(r->params, max_splits, active_groups)
                                      : (a->two_launch != 0);
   a->chosen_two_launch = two ? 1 : 0;
   s.B = a->B;
@@ -311,7 +316,8 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
   }
 
   // the decode kernel (merge fused in), or decode then merge kernel; the
-  // events, if any, take the decode kernel's own start and end timestamps
+  // events, if any, take the decode kernel's own start and the last
+  // kernel's own end timestamps
   st = pkv::decode_timed(a->q, a->k_pool, a->v_pool, a->num_pages, a->block_table,
                          a->max_pages_per_row, a->seq_lens, tasks_d, T, offs_d, slots, a->B,
                          a->Hq, a->Hkv, a->head_dim, a->page_size, a->dtype, a->scale,
@@ -319,9 +325,6 @@ int pkv_runner_step(pkv_runner* r, pkv_step_args* a) {
                          a->workspace_bytes, a->stream, !two, a->event_before_decode,
                          a->event_after_decode);
   if (st != PKV_OK) return st;
-  if (two)
-    st = pkv_merge(offs_d, slots, a->B, a->Hq, a->Hkv, a->head_dim, a->dtype, a->out, a->lse,
-                   a->workspace, a->workspace_bytes, a->stream);
   // A slot the kernels read is free once everything enqueued so far has run.
   // A step served by the device copy leaves its slot unread, and records
   // nothing: an event between two steps costs the stream several

@@ -45,10 +45,18 @@ SPLIT_MAX = 256
 CHUNK_MIN = 4
 CHUNK_MAX = 256
 FUSE_MAX_SPLITS = 16
+FUSE_MAX_GROUP_SPLITS = 256
 WG_PER_CU = 2          # the decode kernel's grid: min(T, 2 * CUs)
 
 PARAM_NAMES = ("t0_us", "t_round_us", "alpha", "cu_gbps", "hbm_gbps", "t_two_us",
                "t_two_split_us", "t_fused_split_us")
+
+
+def two_launch_rule(maxS, groups):
+    """The launch form the policy takes: two launches when the deepest row
+    has more than FUSE_MAX_SPLITS splits and groups x those splits exceed
+    FUSE_MAX_GROUP_SPLITS."""
+    return maxS > FUSE_MAX_SPLITS and groups * maxS > FUSE_MAX_GROUP_SPLITS
 
 
 def plan_features(lens, Hkv, mode, param):
@@ -109,9 +117,11 @@ def pick(x, lens, Hkv, cus, head_dim):
     best = None
     for mode, param in candidates(lens):
         T, P, pmax, maxS = plan_features(lens, Hkv, mode, param)
-        t = predict(x, T, P, pmax, maxS, maxS > FUSE_MAX_SPLITS, cus, head_dim)
+        groups = Hkv * sum(1 for n in lens if int(n) > 0)
+        two = two_launch_rule(maxS, groups)
+        t = predict(x, T, P, pmax, maxS, two, cus, head_dim)
         if best is None or t < best[0]:
-            best = (t, mode, param, maxS > FUSE_MAX_SPLITS)
+            best = (t, mode, param, two)
     return best[1:]
 
 

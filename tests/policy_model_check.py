@@ -26,15 +26,17 @@ MODE_WORKQUEUE = 1
 # The library's pkv_policy_defaults (a test keeps the three copies equal:
 # this one, the C++ defaults and the committed fit).
 POLICY_DEFAULTS = dict(split_max=256, chunk_min=4, chunk_max=256, fuse_max_splits=16,
+                       fuse_max_group_splits=256,
                        t0_us=0.0, t_round_us=5.726, alpha=1.097, cu_gbps=46.64,
                        hbm_gbps=8865.0, t_two_us=6.631, t_two_split_us=0.02415,
                        t_fused_split_us=0.2848)
 
 
 def plan_shape(seq_lens, Hkv, page_size, mode, param):
-    """(T, P, pmax, maxS) of the plan: tasks, page tiles in all, pages of the
-    largest task, splits of the deepest row (closed form of the task list)."""
-    T = P = pmax = maxS = 0
+    """(T, P, pmax, maxS, groups) of the plan: tasks, page tiles in all,
+    pages of the largest task, splits of the deepest row, (row, KV head)
+    groups with work (closed form of the task list)."""
+    T = P = pmax = maxS = groups = 0
     for N in seq_lens:
         n = -(-int(N) // page_size)
         if n == 0:
@@ -43,9 +45,18 @@ def plan_shape(seq_lens, Hkv, page_size, mode, param):
         S = -(-n // c)
         T += Hkv * S
         P += Hkv * n
+        groups += Hkv
         pmax = max(pmax, min(c, n))
         maxS = max(maxS, S)
-    return T, P, pmax, maxS
+    return T, P, pmax, maxS, groups
+
+
+def two_launch(shape, k):
+    """The launch form rule: two launches when the deepest row has more than
+    fuse_max_splits splits and groups x those splits exceed
+    fuse_max_group_splits."""
+    maxS, groups = shape[3], shape[4]
+    return maxS > k["fuse_max_splits"] and groups * maxS > k["fuse_max_group_splits"]
 
 
 def predict_us(shape, num_cus, head_dim, page_size, two, k):
@@ -54,7 +65,7 @@ def predict_us(shape, num_cus, head_dim, page_size, two, k):
     num_cus) CUs, per-CU rate min(cu_gbps, hbm_gbps / A), the critical CU's
     load, a fixed time per round of tasks, and the merge term of the launch
     form."""
-    T, P, pmax, maxS = shape
+    T, P, pmax, maxS = shape[:4]
     if T == 0:
         return k["t0_us"]
     W = min(T, 2 * num_cus)
@@ -97,7 +108,7 @@ def policy(seq_lens, Hkv, page_size, num_cus, head_dim=128, **overrides):
     best = None
     for mode, param in cands:
         shape = plan_shape(seq_lens, Hkv, page_size, mode, param)
-        t = predict_us(shape, num_cus, head_dim, page_size, shape[3] > k["fuse_max_splits"], k)
+        t = predict_us(shape, num_cus, head_dim, page_size, two_launch(shape, k), k)
         if best is None or t < best[0]:
             best = (t, mode, param)
     return best[1], best[2]

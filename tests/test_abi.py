@@ -188,7 +188,7 @@ def test_policy_predict_matches_second_implementation_bit_for_bit():
                 for two in (-1, 0, 1):
                     got = pkv.pkv_policy_predict(lens, 8, cus, mode, param, two)
                     shape = pmc.plan_shape(lens, 8, 16, mode, param)
-                    t2 = shape[3] > pmc.POLICY_DEFAULTS["fuse_max_splits"] if two < 0 else bool(two)
+                    t2 = pmc.two_launch(shape, pmc.POLICY_DEFAULTS) if two < 0 else bool(two)
                     want = pmc.predict_us(shape, cus, 128, 16, t2, pmc.POLICY_DEFAULTS)
                     assert got == want, (lens[:4], cus, mode, param, two, got, want)
 
@@ -203,8 +203,9 @@ def test_policy_defaults_are_the_committed_fit():
     for name, v in fit["params"].items():
         assert getattr(d, name) == v, name
         assert pmc.POLICY_DEFAULTS[name] == v, name
-    assert (d.split_max, d.chunk_min, d.chunk_max, d.fuse_max_splits) == (256, 4, 256, 16)
-    for k in ("split_max", "chunk_min", "chunk_max", "fuse_max_splits"):
+    assert (d.split_max, d.chunk_min, d.chunk_max, d.fuse_max_splits,
+            d.fuse_max_group_splits) == (256, 4, 256, 16, 256)
+    for k in ("split_max", "chunk_min", "chunk_max", "fuse_max_splits", "fuse_max_group_splits"):
         assert pmc.POLICY_DEFAULTS[k] == getattr(d, k)
 
 
@@ -230,7 +231,8 @@ def test_policy_params_and_errors():
     with pytest.raises(pkv.PkvError):
         pkv.pkv_policy([5], 8, 256, head_dim=0)
     for field, bad in (("cu_gbps", 0.0), ("hbm_gbps", -1.0), ("alpha", -0.5), ("t0_us", -1.0),
-                       ("split_max", 0), ("fuse_max_splits", -1)):
+                       ("split_max", 0), ("fuse_max_splits", -1),
+                       ("fuse_max_group_splits", -1)):
         d = pkv.pkv_policy_defaults()
         setattr(d, field, bad)
         with pytest.raises(pkv.PkvError):

@@ -82,8 +82,9 @@ def test_plan_shape_pinned_to_the_task_list(seed):
             assert [tuple(t) for t in tasks] == [tuple(t) for t in walk]
             n = [-(-int(x) // 16) for x in lens]
             pages = [min((s + 1) * c, n[b]) - s * c for b, g, s, c in walk]
-            T, P, pmax, maxS = pmc.plan_shape(lens, 3, 16, mode, p)
+            T, P, pmax, maxS, groups = pmc.plan_shape(lens, 3, 16, mode, p)
             assert (T, P, pmax) == (len(walk), sum(pages), max(pages, default=0))
+            assert groups == len({(b, g) for b, g, s, c in walk})
             assert maxS == max((offs[i + 1] - offs[i] for i in range(len(lens))), default=0)
 
 
