@@ -433,12 +433,13 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
  *      writes the plan out for pkv_device_plan_read);
  *   B > 1024: a one-workgroup planner kernel, then the decode kernel reading
  *      the task count from the header;
- *   then, unless the launch-form rule (below pkv_policy_params) is fused
- *      for maxS = max_splits and B * Hkv groups (every plan is then fused),
- *      the merge kernel, which returns at once when the header says the
- *      decode kernel merged (the fused form: the rule fused on the plan's
- *      own deepest row and active groups, and B * Hkv <=
- *      PKV_MAX_FUSED_GROUPS).
+ *   nothing else when B * Hkv <= PKV_MAX_FUSED_GROUPS: the step is always
+ *      the fused single launch, and the policy times every candidate in
+ *      that form (its launch-form rule is not applied: a second launch in a
+ *      captured step costs more than the separate merge saves);
+ *   with more groups, the merge kernel (the two-launch form).
+ * The plan therefore equals pkv_policy's with fuse_max_splits raised to
+ * INT32_MAX when B * Hkv <= PKV_MAX_FUSED_GROUPS.
  * Arguments as for pkv_decode, except:
  *   seq_lens     device int32 [B]; a row with N_b < 0 or needing more than
  *                max_pages_per_row pages is planned as empty (out = 0,

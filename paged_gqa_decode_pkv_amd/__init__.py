@@ -45,6 +45,7 @@ PKV_DEVERR_SLOT = 8
 
 PAGE_SIZE = 16
 WORKSPACE_HEADER_BYTES = 65536      # PKV_WORKSPACE_HEADER_BYTES
+PKV_MAX_FUSED_GROUPS = (WORKSPACE_HEADER_BYTES - 256) // 4   # PKV_MAX_FUSED_GROUPS
 
 # Every symbol include/pkv.h declares.
 ABI_SYMBOLS = (

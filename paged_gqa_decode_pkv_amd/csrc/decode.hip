@@ -2069,6 +2069,10 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
       pol.chunk_min = static_cast<int32_t>(c);
     }
   }
+  // Groups within the fused merge's arrival counters: the step is always the
+  // fused single launch, so the policy times every candidate in that form.
+  const int32_t groups_fit = static_cast<int64_t>(B) * Hkv <= PKV_MAX_FUSED_GROUPS ? 1 : 0;
+  if (groups_fit) pol.fuse_max_splits = INT32_MAX;
   DevicePlanLayout L;
   int st = device_plan_layout(B, Hq, Hkv, head_dim, max_splits, &L);
   if (st != PKV_OK || B == 0) return st;
@@ -2100,7 +2104,7 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   pa.max_pages = max_pages_per_row;
   pa.mode = mode;
   pa.param = param;
-  pa.groups_fit = static_cast<int64_t>(B) * Hkv <= PKV_MAX_FUSED_GROUPS ? 1 : 0;
+  pa.groups_fit = groups_fit;
   pa.pol = pol;
   pa.hdr = hdr;
   pa.offs = offs;
@@ -2134,13 +2138,9 @@ int pkv_decode_device_plan(const void* q, const void* k_pool, const void* v_pool
   // The task count is known only on the device: one workgroup per CU (as
   // fast as two per CU on the measured workloads, and with no pair of
   // workgroups sharing a CU while others idle); workgroups past the count
-  // exit at once.  When the launch-form rule is fused at the capacity's
-  // bounds (max_splits splits, B * Hkv groups) it is fused for every plan the
-  // capacity admits (the rule only grows with either), and the merge kernel
-  // is not launched at all.
+  // exit at once.  A fused step launches no merge kernel.
   const int grid = num_cus;
-  if (!pkv::two_launch_form(pol, max_splits, static_cast<int64_t>(B) * Hkv) && pa.groups_fit)
-    ma.B = 0;
+  if (groups_fit) ma.B = 0;
   return pkv::launch_any(head_dim, dtype, da, ma, grid, s, true,
                          pkv::load_mode(head_dim, dtype, -1, num_cus));
 }

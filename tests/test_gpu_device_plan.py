@@ -17,9 +17,13 @@ pytestmark = pytest.mark.gpu
 SEED = HELD_OUT_SEEDS[0]
 
 
-def _capped_params(pkv, max_pages, cap):
-    """The host policy's candidate sets limited the way the device path limits them."""
+def _capped_params(pkv, max_pages, cap, groups):
+    """The host policy's candidate sets limited the way the device path limits
+    them; with the groups within the fused merge's counters, the launch-form
+    rule off (the device-planned step is always fused)."""
     p = pkv.pkv_policy_defaults()
+    if groups <= pkv.PKV_MAX_FUSED_GROUPS:
+        p.fuse_max_splits = 2 ** 31 - 1
     p.split_max = min(p.split_max, cap)
     c = p.chunk_min
     while c <= p.chunk_max and -(-max_pages // c) > cap:
@@ -51,16 +55,18 @@ def _check_plan(wl, cap, hdr, tasks, offs, mode, param):
     cfg = wl.cfg
     maxp = wl.block_table_np.shape[1]
     if mode < 0:
-        p = _capped_params(pkv, maxp, cap)
+        p = _capped_params(pkv, maxp, cap, len(wl.seq_lens_np) * cfg.Hkv)
         if p.chunk_min <= p.chunk_max:
             want = pkv.pkv_policy(wl.seq_lens_np, cfg.Hkv, _num_cus(), params=p, head_dim=cfg.D)
         else:
             # no workqueue schedule fits: the first fastest split candidate
+            # (timed with valid chunk bounds; the model does not read them)
+            p.chunk_min = p.chunk_max
             best = None
             S = 1
             while S <= p.split_max:
                 t = pkv.pkv_policy_predict(wl.seq_lens_np, cfg.Hkv, _num_cus(), 0, S,
-                                           head_dim=cfg.D)
+                                           params=p, head_dim=cfg.D)
                 if best is None or t < best[0]:
                     best = (t, (0, S))
                 S *= 2
@@ -74,7 +80,8 @@ def _check_plan(wl, cap, hdr, tasks, offs, mode, param):
     assert hdr["num_tasks"] == len(rt) and hdr["num_partial_slots"] == slots
     deepest = int(np.max(np.diff(ro))) if len(ro) > 1 else 0
     assert hdr["max_splits"] == deepest
-    assert hdr["fused"] == int(len(rt) == 0 or deepest <= 16)
+    groups = cfg.Hkv * len(wl.seq_lens_np)
+    assert hdr["fused"] == int(len(rt) == 0 or groups <= pkv.PKV_MAX_FUSED_GROUPS)
     assert hdr["row_flagged"] == 0
 
 
