@@ -622,8 +622,7 @@ struct PlanArgs {
 
 constexpr int kPlanHdrInts = 16;
 constexpr int kPlanStage = 4096;   // rows whose page counts the planner keeps in LDS
-constexpr int kCandBatch = 16;     // policy candidates evaluated together
-constexpr int kCandGroups = kThreads / kCandBatch;
+constexpr int kCandBatch = kThreads / 16;   // policy candidates evaluated together
 
 __device__ __forceinline__ uint32_t cdiv32(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
@@ -636,22 +635,6 @@ __device__ __forceinline__ int32_t plan_row_pages_global(const PlanArgs& a, int 
   return n > a.max_pages ? -1 : static_cast<int32_t>(n);
 }
 
-// Add one row of n pages to the plan shape (mode, param): the arithmetic of
-// shape_add_row in 32 bits (n, c, S fit) with 64-bit sums.
-__device__ __forceinline__ void plan_shape_add(PlanShape& f, int32_t n, int32_t Hkv, int m,
-                                               uint32_t v) {
-  if (n <= 0) return;
-  const uint32_t un = static_cast<uint32_t>(n);
-  const uint32_t c = m == PKV_MODE_SPLIT ? cdiv32(un, v) : v;
-  const uint32_t S = cdiv32(un, c);
-  f.T += static_cast<int64_t>(Hkv) * S;
-  f.P += static_cast<int64_t>(Hkv) * un;
-  f.groups += Hkv;
-  const int64_t largest = c < un ? c : un;
-  if (largest > f.pmax) f.pmax = largest;
-  if (static_cast<int64_t>(S) > f.maxS) f.maxS = S;
-}
-
 __device__ __forceinline__ int64_t wave_max64(int64_t v) {
   for (int off = 32; off >= 1; off >>= 1) {
     const int64_t o = __shfl_xor(v, off);
@@ -660,30 +643,78 @@ __device__ __forceinline__ int64_t wave_max64(int64_t v) {
   return v;
 }
 
-// LDS of the policy's candidate search.
-struct CandLds {
-  int64_t T[kCandGroups][kCandBatch];
-  int64_t P[kCandGroups][kCandBatch];
-  int64_t pmax[kCandGroups][kCandBatch];
-  int64_t maxS[kCandGroups][kCandBatch];
-  int64_t groups[kCandGroups][kCandBatch];
-  double t[kCandBatch];
-  int64_t pages;
-  int pick[2];
+// Exchanges inside 16-lane rows (DPP): lanes i and i^1, i and i^2, then
+// lanes i and 7-i of each 8, then i and 15-i of the row.  Applied in that
+// order with a commutative operation, every lane ends with the reduction of
+// its row (pairs, quads, 8-lane halves, the row).
+constexpr int kDppSwap1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+
+template <int kCtrl>
+__device__ __forceinline__ int64_t dpp_xchg64(int64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false);
+  const int hi =
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v >> 32), kCtrl, 0xF, 0xF, false);
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                              static_cast<uint32_t>(lo));
+}
+
+__device__ __forceinline__ int64_t row16_sum(int64_t v) {
+  v += dpp_xchg64<kDppSwap1>(v);
+  v += dpp_xchg64<kDppSwap2>(v);
+  v += dpp_xchg64<kDppHalfMirror>(v);
+  v += dpp_xchg64<kDppMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ int row16_max32(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppSwap1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppSwap2, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false));
+  return max(v, __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false));
+}
+
+// Maximum over the wave (every lane active): the rows' maxima, then the
+// four rows' through scalar reads.
+__device__ __forceinline__ int wave_max32(int v) {
+  v = row16_max32(v);
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// LDS of the policy's candidate search: each wave's first fastest candidate
+// of a batch, double-buffered over batches.
+struct PickLds {
+  double t[2][kWaves];
+  int i[2][kWaves];
 };
 
 // "2. Calibrated Adaptive Policy" on the device: the candidates of pkv_policy
 // in its order, each timed by the same model (policy_model.h), the earliest
-// fastest kept.  Candidates go 16 at a time: thread (candidate j, group r)
-// folds rows r, r+16, ... into a plan shape; 16 threads sum the groups and
-// evaluate the model; thread 0 keeps the first fastest.  row_n(b): pages of
-// row b (0 for an empty or flagged row).  All threads call it and all get
-// the choice.
+// fastest kept.  Candidates go 16 at a time, one per 16-lane row: lane r of
+// candidate j's row folds rows r, r+16, ... into a plan shape, the row sums
+// them with DPP exchanges and every lane of it evaluates the model; each
+// wave keeps the first fastest of its four candidates, and after one barrier
+// every thread takes the first fastest of the four waves'.  active_rows:
+// rows with at least one page; row_n(b): pages of row b (0 for an empty or
+// flagged row).  All threads call it and all get the choice.
 template <class RowN>
 __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_cus,
-                            int head_dim, int page_size, RowN row_n, CandLds& L, int& mode,
-                            int& param) {
+                            int head_dim, int page_size, RowN row_n, int64_t active_rows,
+                            PickLds& L, int& mode, int& param) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int nsplit = 0;
   for (int64_t S = 1; S <= p.split_max; S *= 2) ++nsplit;
   int nchunk = 0;
@@ -693,74 +724,81 @@ __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_
   // split along the sequence (candidates [0, nsplit)), several rows go
   // through the workqueue (candidates [nsplit, ncand)); if the capacity left
   // no workqueue candidate, the split candidates serve.
-  int act = 0;
-  for (int b = tid; b < B; b += kThreads) act += row_n(b) > 0 ? 1 : 0;
-  const int thr_active = __syncthreads_count(act > 0);
-  const int thr_multi = __syncthreads_or(act > 1);
-  const bool one_row = thr_active <= 1 && !thr_multi;
-  const bool use_split = one_row || nchunk == 0;
+  const bool use_split = active_rows <= 1 || nchunk == 0;
   const int c_lo = use_split ? 0 : nsplit;
   const int c_hi = use_split ? nsplit : ncand;
-  const int j = tid % kCandBatch;
-  const int grp = tid / kCandBatch;
+  const int j = tid >> 4;    // candidate of this thread's row within the batch
+  const int r = tid & 15;    // rows r, r + 16, ...
+  // page tiles and groups do not depend on the candidate
+  int64_t pages = 0;
+  for (int b = r; b < B; b += 16) pages += row_n(b);
+  const int64_t P = static_cast<int64_t>(Hkv) * row16_sum(pages);
+  const int64_t groups = static_cast<int64_t>(Hkv) * active_rows;
   double best_t = 0.0;
   int best_i = -1;
-  int64_t total_pages = 0;
-  for (int cb = c_lo; cb < c_hi; cb += kCandBatch) {
+  for (int cb = c_lo, par = 0; cb < c_hi; cb += kCandBatch, par ^= 1) {
     const int i = cb + j;
-    PlanShape f;
+    int64_t splits = 0;   // sum of the rows' splits
+    int pmax = 0, maxS = 0;
     if (i < c_hi) {
-      const int m = i < nsplit ? PKV_MODE_SPLIT : PKV_MODE_WORKQUEUE;
-      const uint32_t v = i < nsplit ? (1u << i)
-                                    : static_cast<uint32_t>(p.chunk_min) << (i - nsplit);
-      for (int b = grp; b < B; b += kCandGroups) plan_shape_add(f, row_n(b), Hkv, m, v);
-    }
-    L.T[grp][j] = f.T;
-    L.P[grp][j] = f.P;
-    L.pmax[grp][j] = f.pmax;
-    L.maxS[grp][j] = f.maxS;
-    L.groups[grp][j] = f.groups;
-    __syncthreads();
-    if (tid < kCandBatch && i < c_hi) {
-      PlanShape F;
-      for (int r = 0; r < kCandGroups; ++r) {
-        F.T += L.T[r][j];
-        F.P += L.P[r][j];
-        F.pmax = L.pmax[r][j] > F.pmax ? L.pmax[r][j] : F.pmax;
-        F.maxS = L.maxS[r][j] > F.maxS ? L.maxS[r][j] : F.maxS;
-        F.groups += L.groups[r][j];
-      }
-      L.t[j] = model_us(p, F, num_cus, head_dim, page_size,
-                        two_launch_form(p, F.maxS, F.groups));
-      if (j == 0) L.pages = F.P;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      total_pages = L.pages;
-      for (int k = 0; k < kCandBatch && cb + k < c_hi; ++k) {
-        if (best_i < 0 || L.t[k] < best_t) {
-          best_t = L.t[k];
-          best_i = cb + k;
-        }
+      const bool split = i < nsplit;
+      const uint32_t v = split ? (1u << i) : static_cast<uint32_t>(p.chunk_min) << (i - nsplit);
+      for (int b = r; b < B; b += 16) {
+        const uint32_t n = static_cast<uint32_t>(row_n(b));
+        if (n == 0) continue;
+        const uint32_t c = split ? cdiv32(n, v) : v;
+        const uint32_t S = cdiv32(n, c);
+        splits += S;
+        pmax = max(pmax, static_cast<int>(c < n ? c : n));
+        maxS = max(maxS, static_cast<int>(S));
       }
     }
-    __syncthreads();   // the shapes are rewritten by the next batch
-  }
-  if (tid == 0) {
-    if (total_pages == 0 || best_i < 0) {
-      L.pick[0] = PKV_MODE_SPLIT;
-      L.pick[1] = 1;
-    } else if (best_i < nsplit) {
-      L.pick[0] = PKV_MODE_SPLIT;
-      L.pick[1] = 1 << best_i;
-    } else {
-      L.pick[0] = PKV_MODE_WORKQUEUE;
-      L.pick[1] = p.chunk_min << (best_i - nsplit);
+    PlanShape F;
+    F.T = static_cast<int64_t>(Hkv) * row16_sum(splits);
+    F.P = P;
+    F.groups = groups;
+    F.pmax = row16_max32(pmax);
+    F.maxS = row16_max32(maxS);
+    const double t = i < c_hi ? model_us(p, F, num_cus, head_dim, page_size,
+                                         two_launch_form(p, F.maxS, F.groups))
+                              : 0.0;
+    // this wave's candidates cb + 4 wave + k sit in lanes 16 k
+    double wt = 0.0;
+    int wi = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ik = cb + 4 * wave + k;
+      const double tk = readlane_f64(t, 16 * k);
+      if (ik < c_hi && (wi < 0 || tk < wt)) {
+        wt = tk;
+        wi = ik;
+      }
+    }
+    if (lane == 0) {
+      L.t[par][wave] = wt;
+      L.i[par][wave] = wi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int iw = L.i[par][w];
+      const double tw = L.t[par][w];
+      if (iw >= 0 && (best_i < 0 || tw < best_t)) {
+        best_t = tw;
+        best_i = iw;
+      }
     }
   }
-  __syncthreads();
-  mode = L.pick[0];
-  param = L.pick[1];
+  if (active_rows == 0 || best_i < 0) {
+    mode = PKV_MODE_SPLIT;
+    param = 1;
+  } else if (best_i < nsplit) {
+    mode = PKV_MODE_SPLIT;
+    param = 1 << best_i;
+  } else {
+    mode = PKV_MODE_WORKQUEUE;
+    param = p.chunk_min << (best_i - nsplit);
+  }
 }
 
 // Everything the workgroup needs to know about one task.  All fields are
@@ -890,8 +928,10 @@ __device__ __forceinline__ void flush_done(const DecodeArgs& a, const MergeArgs&
 
 // Block-table entries of round j of task m for this wave: position 4j+r is
 // page p0 + wave + 16j + 4r.  Positions past the range read a clamped,
-// in-row entry that issue() never uses (it re-checks page < p1).  No select
-// on the loaded values, so the four scalar loads issue back to back.
+// in-row entry that issue() never uses (it re-checks page < p1); an invalid
+// task reads its row's first entry, and a table without columns is not read.
+// No select on the loaded values, so the four scalar loads issue back to
+// back.
 template <int R>
 struct Round {
   int e[R];
@@ -901,12 +941,57 @@ template <int R>
 __device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_t* __restrict__ bt,
                                                const Meta& m, int wave, int j) {
   Round<R> r;
+  if (a.max_pages <= 0) {   // a table without columns: no row has a page
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.e[i] = 0;
+    return r;
+  }
   const int32_t* row = bt + static_cast<int64_t>(m.b) * a.max_pages;
   const int last = m.ok ? m.p1 - 1 : 0;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int page = m.p0 + wave + kWaves * (R * j + i);
     r.e[i] = row[page < last ? page : last];
+  }
+  return r;
+}
+
+// v clamped into [0, n) (n >= 1), wave-uniform.
+__device__ __forceinline__ int clamp_index(int v, int n) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  return v < 0 ? 0 : (v >= n ? n - 1 : v);
+}
+
+// The first round's block-table entries of the task in record `rec`, for
+// this wave, from the record alone (the row's length is not yet known):
+// positions p0 + wave + 4i of the chunk [p0, p0 + c), p0 = split * c,
+// clamped to the chunk's last position and to the row's last table entry,
+// with the row clamped into [0, B).  Every page that issue() loads lies
+// below p1 = min(p0 + c, n_b) with n_b <= max_pages, where the clamps change
+// nothing: the entries it uses are those of load_round.  A table without
+// columns (max_pages = 0: no row has a page) is not read.
+template <int R>
+__device__ __forceinline__ Round<R> first_round(const DecodeArgs& a,
+                                                const int32_t* __restrict__ bt, int4 rec,
+                                                int wave) {
+  Round<R> r;
+  const int b = clamp_index(rec.x, a.B);
+  const int s = __builtin_amdgcn_readfirstlane(rec.z);
+  const int c = __builtin_amdgcn_readfirstlane(rec.w);
+  const int64_t cc = c < 1 ? 1 : c;
+  const int64_t p0 = static_cast<int64_t>(s < 0 ? 0 : s) * cc;
+  const int64_t end = p0 + cc < a.max_pages ? p0 + cc : a.max_pages;
+  const int64_t last = end - 1 > 0 ? end - 1 : 0;
+  if (a.max_pages > 0) {
+    const int32_t* row = bt + static_cast<int64_t>(b) * a.max_pages;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t pos = p0 + wave + kWaves * i;
+      r.e[i] = row[pos < last ? pos : last];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.e[i] = 0;
   }
   return r;
 }
@@ -944,8 +1029,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   __shared__ int4 s_done[kMaxDone];   // (row, KV head, first slot, splits)
   __shared__ int s_lastf[kMaxDone];
   // self-planned step only: the policy's candidate search and the row scan
-  __shared__ typename std::conditional<kSelfPlan, CandLds, char>::type s_cand;
-  __shared__ int s_plan[kSelfPlan ? 3 * kWaves + 2 : 1];
+  __shared__ typename std::conditional<kSelfPlan, PickLds, char>::type s_pick;
+  __shared__ int s_plan[kSelfPlan ? 4 * kWaves : 1];
   static_assert(kWaves * kGroup * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
   static_assert(!kSelfPlan || kStaged, "a self-planned step stages its rows");
 
@@ -973,29 +1058,40 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       lv[k] = i < a.B ? seq_lens_in[i] : 0;
     }
     // A row with N < 0 or more than max_pages pages is flagged and planned
-    // empty (its length staged as 0).
-    int bad = 0;
+    // empty (its length staged as 0).  Rows with pages and flagged rows are
+    // counted per wave (ballots) into LDS slots of their own: nothing to
+    // clear, one barrier.
+    int wact = 0, wbad = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kThreads;
-      if (i < a.B) {
-        const int N = lv[k];
-        const bool ok = N >= 0 && (static_cast<int64_t>(N) + kPage - 1) / kPage <= a.max_pages;
-        bad |= ok ? 0 : 1;
-        s_len[i] = ok ? N : 0;
-      }
+      const int N = lv[k];
+      const bool ok = N >= 0 && (static_cast<int64_t>(N) + kPage - 1) / kPage <= a.max_pages;
+      if (i < a.B) s_len[i] = ok ? N : 0;
+      wact += __builtin_popcountll(__ballot(i < a.B && ok && N > 0));
+      wbad |= __ballot(i < a.B && !ok) != 0 ? 1 : 0;
     }
-    const int any_bad = __syncthreads_or(bad);
+    if (lane == 0) {
+      s_plan[wave] = wact;
+      s_plan[kWaves + wave] = wbad;
+    }
+    __syncthreads();
+    int active_rows = 0, any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      active_rows += s_plan[w];
+      any_bad |= s_plan[kWaves + w];
+    }
     auto row_n = [&](int b) -> int32_t { return (s_len[b] + kPage - 1) / kPage; };
     plan_mode = a.plan_mode;
     plan_param = a.plan_param;
     if (plan_mode < 0)
-      choose_plan(a.plan_pol, a.B, a.Hkv, a.plan_num_cus, a.plan_head_dim, kPage, row_n, s_cand,
-                  plan_mode, plan_param);
+      choose_plan(a.plan_pol, a.B, a.Hkv, a.plan_num_cus, a.plan_head_dim, kPage, row_n,
+                  active_rows, s_pick, plan_mode, plan_param);
     // splits per row, then their exclusive prefix: thread t takes rows
     // kRows*t .. kRows*t + kRows-1
     int sv[kRows];
-    int sum = 0, mx = 0, act = 0;
+    int sum = 0, mx = 0;
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
       const int b = kRows * tid + k;
@@ -1011,30 +1107,24 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       sv[k] = S;
       sum += S;
       mx = S > mx ? S : mx;
-      act += S > 0 ? 1 : 0;
     }
-    int wact = act;   // rows with work, summed over the wave
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) wact += __shfl_xor(wact, off);
     int incl = sum;   // inclusive scan over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int v = __shfl_up(incl, off);
       if (lane >= off) incl += v;
     }
-    const int wmax = static_cast<int>(wave_max64(mx));
-    if (lane == 63) s_plan[wave] = incl;
-    if (lane == 0) s_plan[kWaves + wave] = wmax;
-    if (lane == 0) s_plan[2 * kWaves + wave] = wact;
+    const int wmax = wave_max32(mx);
+    if (lane == 63) s_plan[2 * kWaves + wave] = incl;
+    if (lane == 0) s_plan[3 * kWaves + wave] = wmax;
     __syncthreads();
     int base = incl - sum;
-    int total = 0, maxS = 0, active_rows = 0;
+    int total = 0, maxS = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (w < wave) base += s_plan[w];
-      total += s_plan[w];
-      maxS = s_plan[kWaves + w] > maxS ? s_plan[kWaves + w] : maxS;
-      active_rows += s_plan[2 * kWaves + w];
+      if (w < wave) base += s_plan[2 * kWaves + w];
+      total += s_plan[2 * kWaves + w];
+      maxS = s_plan[3 * kWaves + w] > maxS ? s_plan[3 * kWaves + w] : maxS;
     }
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
@@ -1066,9 +1156,9 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   }
   // Record of task t of a self-planned step, from the offsets in LDS: the
   // row is the last one whose first task is <= t (rows without tasks share
-  // the next row's offset and come before it).  Written out for read-back
-  // by the workgroup that takes the task.
-  auto self_record = [&](int t) -> int4 {
+  // the next row's offset and come before it).  With `publish`, thread 0
+  // writes it out for read-back (the workgroup that takes the task does).
+  auto self_record = [&](int t, bool publish) -> int4 {
     if (t >= num_tasks) return int4{0, 0, 0, 1};
     int lo = 0, hi = a.B;
     while (hi - lo > 1) {
@@ -1084,46 +1174,9 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const int c = plan_mode == PKV_MODE_SPLIT ? static_cast<int>(cdiv32(n, plan_param))
                                               : plan_param;
     const int4 rec = int4{b, g, r - g * S, c};
-    if (tid == 0) a.plan_tasks_out[t] = rec;
+    if (publish && tid == 0) a.plan_tasks_out[t] = rec;
     return rec;
   };
-  // The first task record (scalar) is issued first, then the staging loads
-  // (vector), then the LDS stores: the two load latencies overlap instead of
-  // adding up.  The scheduling barrier keeps the compiler from sinking the
-  // record load below the stores, which wait for the staging loads.
-  int4 rec0;
-  if constexpr (kSelfPlan) {
-    rec0 = self_record(blockIdx.x);
-  } else if constexpr (kStaged) {
-    constexpr int kPer = (kRowStage + kThreads) / kThreads;   // covers B+1 <= kRowStage+1
-    rec0 = load_record(a, tasks_in, blockIdx.x);
-    __builtin_amdgcn_sched_barrier(0);
-    int lv[kPer], ov[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kThreads;
-      lv[k] = i < a.B ? seq_lens_in[i] : 0;
-      ov[k] = i <= a.B ? offs_in[i] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < a.B) s_len[i] = lv[k];
-      if (i <= a.B) s_off[i] = ov[k];
-    }
-  } else {
-    rec0 = load_record(a, tasks_in, blockIdx.x);
-  }
-  __syncthreads();
-  if (fuse) {
-    // rows without tasks (N_b = 0): out = 0, lse = -inf
-    for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
-      const int sb = kStaged ? s_off[b + 1] - s_off[b] : offs_in[b + 1] - offs_in[b];
-      if (sb == 0)
-        for (int g = 0; g < a.Hkv; ++g) write_empty_group<D, E>(ma, b, g);
-    }
-  }
-
   const int G = a.G;
   const int64_t tile_elems = static_cast<int64_t>(kPage) * D;
   const int64_t stride_bytes = static_cast<int64_t>(a.Hkv) * tile_elems * kKvb;
@@ -1148,13 +1201,14 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
         r, make_rsrc(kpool + off, bytes), make_rsrc(vpool + off, bytes), koff, voff);
     return live;
   };
-  // q of task m (B operand of the score MFMA, column = head within the
-  // group).  Raw loads; columns >= G are zeroed when stored to LDS, so the
-  // loads can stay in flight until then.
-  auto load_q = [&](const Meta& m, vecE<E, 8> (&qf)[KK]) {
-    const bool live = m.ok && col < G;
-    const E* qp = static_cast<const E*>(a.q) + (static_cast<int64_t>(m.b) * a.Hq +
-                                static_cast<int64_t>(m.g) * G + (live ? col : 0)) * D;
+  // q of row b, KV head g (B operand of the score MFMA, column = head
+  // within the group); ok = false loads column 0 only.  Raw loads; columns
+  // >= G, and every column of a task that turns out invalid, are zeroed
+  // when stored to LDS, so the loads can stay in flight until then.
+  auto load_q = [&](int b, int g, bool ok, vecE<E, 8> (&qf)[KK]) {
+    const bool live = ok && col < G;
+    const E* qp = static_cast<const E*>(a.q) + (static_cast<int64_t>(b) * a.Hq +
+                                static_cast<int64_t>(g) * G + (live ? col : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = *reinterpret_cast<const vecE<E, 8>*>(qp + 8 * k_chunk<KV>(kk, grp));
@@ -1166,26 +1220,80 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   };
 
   // ---- prologue: task 0 = blockIdx.x, task 1 = blockIdx.x + gridDim.x
-  Meta cur = decode_meta<kStaged, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks,
-                                         blockIdx.x,
-                                  rec0);
-  int t_nxt = blockIdx.x + gridDim.x;
+  Meta cur;
   PageRegs<D, E, KV> ring[kRing];
   bool valid[kRing];
-  {
+  vecE<E, 8> qf[KK];   // wave 0: q of the first task
+  if constexpr (kSelfPlan) {
+    // the record and the row bounds come from the plan in LDS
+    cur = decode_meta<kStaged, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks,
+                                      blockIdx.x, self_record(blockIdx.x, false));
     // q is loaded before the pages: vector loads complete in order, so its
     // wait (and the barrier behind it) does not also wait for the first
     // round of pages, and every wave starts consuming (and refilling) its
     // ring as soon as its first page lands.
-    vecE<E, 8> qf[KK];
-    if (wave == 0) load_q(cur, qf);
+    if (wave == 0) load_q(cur.b, cur.g, cur.ok, qf);
     __builtin_amdgcn_sched_barrier(0);
     const Round<kRing> r0 = load_round<kRing>(a, bt_in, cur, wave, 0);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
-    if (wave == 0) store_q(cur, qf, s_q[0]);
+    // written out for read-back behind the page loads (recomputed, so that
+    // nothing is held across them)
+    self_record(blockIdx.x, true);
+  } else {
+    // Host plan.  The first task does not wait for the staging: its record
+    // (scalar) goes out first, then the staging loads (vector); from the
+    // record alone the first round's table entries (scalar) and q (vector,
+    // behind the staging loads, so their wait does not cover it); its row
+    // bounds are read from global memory (scalar), not from the staged
+    // copy.  Three scalar round trips lie before the first page load; the
+    // staging completes in their shadow and is stored to LDS for the later
+    // tasks.  The scheduling barriers keep that order.
+    const int4 rec0 = load_record(a, tasks_in, blockIdx.x);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kPer = kStaged ? (kRowStage + kThreads) / kThreads : 1;   // B+1 <= kRowStage+1
+    int lv[kPer], ov[kPer];
+    if constexpr (kStaged) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kThreads;
+        lv[k] = i < a.B ? seq_lens_in[i] : 0;
+        ov[k] = i <= a.B ? offs_in[i] : 0;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const Round<kRing> r0 = first_round<kRing>(a, bt_in, rec0, wave);
+    if (wave == 0) {
+      const int qb = clamp_index(rec0.x, a.B);
+      const int qg = clamp_index(rec0.y, a.Hkv);
+      load_q(qb, qg, true, qf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    cur = decode_meta<false, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, blockIdx.x,
+                                    rec0);
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
+    if constexpr (kStaged) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < a.B) s_len[i] = lv[k];
+        if (i <= a.B) s_off[i] = ov[k];
+      }
+    }
   }
+  // store_q zeroes the columns of an invalid first task
+  if (wave == 0) store_q(cur, qf, s_q[0]);
+  int t_nxt = blockIdx.x + gridDim.x;
   __syncthreads();
+  if (fuse) {
+    // rows without tasks (N_b = 0): out = 0, lse = -inf
+    for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+      const int sb = kStaged ? s_off[b + 1] - s_off[b] : offs_in[b + 1] - offs_in[b];
+      if (sb == 0)
+        for (int g = 0; g < a.Hkv; ++g) write_empty_group<D, E>(ma, b, g);
+    }
+  }
 
   int n_done = 0;   // entries of s_done (workgroup-uniform)
   for (int it = 0; cur.t < num_tasks; ++it) {
@@ -1195,7 +1303,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     Meta nxt;
     if constexpr (kSelfPlan)
       nxt = decode_meta<kStaged, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, t_nxt,
-                                        self_record(t_nxt));
+                                        self_record(t_nxt, true));
     else
       nxt = load_meta<kStaged, kRing>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off,
                                       num_tasks, t_nxt);
@@ -1218,7 +1326,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     for (int j = 0; j < cur.rounds; ++j) {
       const bool last = (j + 1 == cur.rounds);
       vecE<E, 8> qn[KK];
-      if (last && wave == 0) load_q(nxt, qn);
+      if (last && wave == 0) load_q(nxt.b, nxt.g, nxt.ok, qn);
       const Round<kRing> fr = last ? nr0 : load_round<kRing>(a, bt_in, cur, wave, j + 1);
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
@@ -1438,7 +1546,7 @@ __global__ void __launch_bounds__(kMergeKernelThreads) pkv_merge_kernel(MergeArg
 
 __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   __shared__ int32_t s_n[kPlanStage];
-  __shared__ CandLds s_cand;
+  __shared__ PickLds s_pick;
   __shared__ int s_best_i[kWaves];
   __shared__ int s_scan[kThreads];
   __shared__ int s_S[kThreads];
@@ -1450,20 +1558,28 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   const int wave = tid >> 6;
   const int staged = a.B < kPlanStage ? a.B : kPlanStage;
 
-  // ---- 0. page counts of the rows, once
-  int bad = 0;
-  for (int b = tid; b < staged; b += kThreads) {
-    const int32_t n = plan_row_pages_global(a, b);
-    bad |= n < 0;
-    s_n[b] = n < 0 ? 0 : n;
-  }
-  for (int b = staged + tid; b < a.B; b += kThreads) bad |= plan_row_pages_global(a, b) < 0;
+  // ---- 0. page counts of the rows, once; flagged rows and rows with pages
+  int bad = 0, act = 0;
   if (tid == 0) {
     s_bad = 0;
     s_active = 0;
   }
+  for (int b = tid; b < staged; b += kThreads) {
+    const int32_t n = plan_row_pages_global(a, b);
+    bad |= n < 0;
+    act += n > 0 ? 1 : 0;
+    s_n[b] = n < 0 ? 0 : n;
+  }
+  for (int b = staged + tid; b < a.B; b += kThreads) {
+    const int32_t n = plan_row_pages_global(a, b);
+    bad |= n < 0;
+    act += n > 0 ? 1 : 0;
+  }
   __syncthreads();
   if (bad) s_bad = 1;
+  if (act > 0) atomicAdd(&s_active, act);
+  __syncthreads();
+  const int active_rows = s_active;
   auto row_n = [&](int b) -> int32_t {
     if (b < kPlanStage) return s_n[b];
     const int32_t n = plan_row_pages_global(a, b);
@@ -1473,13 +1589,12 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   // ---- 1. policy
   int mode = a.mode, param = a.param;
   if (mode < 0)
-    choose_plan(a.pol, a.B, a.Hkv, a.num_cus, a.head_dim, a.page_size, row_n, s_cand, mode,
-                param);
+    choose_plan(a.pol, a.B, a.Hkv, a.num_cus, a.head_dim, a.page_size, row_n, active_rows,
+                s_pick, mode, param);
 
   // ---- 2. split offsets and records, 256 rows at a time
   int carry = 0;
   int maxS = 0;
-  int act = 0;   // rows with work seen by this thread
   for (int base = 0; base < a.B; base += kThreads) {
     const int b = base + tid;
     int S = 0, c = 0;
@@ -1491,7 +1606,6 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
       }
     }
     maxS = S > maxS ? S : maxS;
-    act += S > 0 ? 1 : 0;
     s_S[tid] = S;
     s_c[tid] = c;
     s_scan[tid] = S;
@@ -1522,17 +1636,14 @@ __global__ void __launch_bounds__(kThreads) pkv_plan_kernel(PlanArgs a) {
   // ---- 3. header
   const int deep_w = static_cast<int>(wave_max64(maxS));
   if (lane == 0) s_best_i[wave] = deep_w;
-  if (act > 0) atomicAdd(&s_active, act);
   __syncthreads();
   if (tid == 0) {
     int deep = 0;
     for (int w = 0; w < kWaves; ++w) deep = s_best_i[w] > deep ? s_best_i[w] : deep;
     const int T = a.Hkv * carry;
     a.hdr[0] = T;
-    a.hdr[1] = (T == 0 || (!two_launch_form(a.pol, deep, static_cast<int64_t>(a.Hkv) * s_active) &&
-                           a.groups_fit))
-                   ? 1
-                   : 0;
+    const int64_t groups = static_cast<int64_t>(a.Hkv) * active_rows;
+    a.hdr[1] = (T == 0 || (!two_launch_form(a.pol, deep, groups) && a.groups_fit)) ? 1 : 0;
     a.hdr[2] = mode;
     a.hdr[3] = param;
     a.hdr[4] = carry;

@@ -8,6 +8,7 @@
 // floating-point contraction off, so host and device take the same decision.
 #pragma once
 
+#include <climits>
 #include <cstdint>
 
 #include "pkv.h"
@@ -30,6 +31,16 @@ struct PlanShape {
 };
 
 PKV_HOST_DEVICE inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// cdiv for 0 <= a and 1 <= b; operands below 2^31 take a 32-bit division
+// (the same quotient; a 64-bit division is a long instruction sequence on
+// the GPU).
+PKV_HOST_DEVICE inline int64_t cdiv_nonneg(int64_t a, int64_t b) {
+  if (a <= INT32_MAX && b <= INT32_MAX)
+    return static_cast<int64_t>((static_cast<uint32_t>(a) + static_cast<uint32_t>(b) - 1u) /
+                                static_cast<uint32_t>(b));
+  return cdiv(a, b);
+}
 
 // Add row b (n pages) to the shape of the plan (mode, param).
 PKV_HOST_DEVICE inline void shape_add_row(PlanShape& f, int64_t n, int32_t Hkv, int32_t mode,
@@ -67,13 +78,13 @@ PKV_HOST_DEVICE inline double model_us(const pkv_policy_params& p, const PlanSha
   const double rho = share < p.cu_gbps ? share : p.cu_gbps;
   double load;
   if (f.T <= W) {
-    load = static_cast<double>(cdiv(f.T, A) * f.pmax);
+    load = static_cast<double>(cdiv_nonneg(f.T, A) * f.pmax);
   } else {
     load = static_cast<double>(f.P) / static_cast<double>(A) +
            p.alpha * static_cast<double>(f.pmax);
   }
   const double tile = 2.0 * page_size * head_dim * 2.0;
-  double t = p.t0_us + p.t_round_us * static_cast<double>(cdiv(f.T, W)) +
+  double t = p.t0_us + p.t_round_us * static_cast<double>(cdiv_nonneg(f.T, W)) +
              load * tile / (rho * 1e3);
   if (two) {
     t = t + p.t_two_us + p.t_two_split_us * static_cast<double>(f.maxS);
