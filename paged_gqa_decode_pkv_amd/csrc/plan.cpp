@@ -56,14 +56,14 @@ int pkv_policy_defaults(pkv_policy_params* p) {
   p->fuse_max_group_splits = 256;
   // Fitted on the calibration seed (paged_gqa_decode_pkv_amd/calibration/
   // mi355x_fit.json, written by policy_fit.py from calibrate.py's runs).
-  p->t0_us = 0.0;
-  p->t_round_us = 5.726;
-  p->alpha = 1.097;
-  p->cu_gbps = 46.64;
-  p->hbm_gbps = 8865.0;
-  p->t_two_us = 6.631;
-  p->t_two_split_us = 0.02415;
-  p->t_fused_split_us = 0.2848;
+  p->t0_us = 2.309;
+  p->t_round_us = 4.153;
+  p->alpha = 1.145;
+  p->cu_gbps = 46.34;
+  p->hbm_gbps = 8667.0;
+  p->t_two_us = 6.018;
+  p->t_two_split_us = 0.0436;
+  p->t_fused_split_us = 0.2422;
   return PKV_OK;
 }
 

@@ -167,14 +167,18 @@ def records(data):
                 step = row[ti]
                 Tf, P, pmax, mS = plan_features(d["lens"], data["Hkv"], mode, param)
                 assert (Tf, mS) == (T, maxS), (cfg, seed, mode, param)
+                groups = data["Hkv"] * sum(1 for n in d["lens"] if int(n) > 0)
                 out.append(dict(cfg=cfg, seed=int(seed), mode=mode, param=param, two=bool(two),
-                                T=T, P=P, pmax=pmax, maxS=maxS, step=step))
+                                T=T, P=P, pmax=pmax, maxS=maxS, groups=groups, step=step))
     return out
 
 
 def fit(recs, cus, head_dim):
     from scipy.optimize import least_squares
-    cal = [r for r in recs if r["seed"] == CALIBRATION_SEED]
+    # The launch form of a candidate is fixed by the rule, so the model is
+    # fitted on the runs in that form: the only ones the policy can pick.
+    cal = [r for r in recs if r["seed"] == CALIBRATION_SEED and
+           r["two"] == two_launch_rule(r["maxS"], r["groups"])]
 
     def resid(x):
         return np.array([math.log(predict(x, r["T"], r["P"], r["pmax"], r["maxS"], r["two"],

@@ -27,9 +27,9 @@ MODE_WORKQUEUE = 1
 # this one, the C++ defaults and the committed fit).
 POLICY_DEFAULTS = dict(split_max=256, chunk_min=4, chunk_max=256, fuse_max_splits=16,
                        fuse_max_group_splits=256,
-                       t0_us=0.0, t_round_us=5.726, alpha=1.097, cu_gbps=46.64,
-                       hbm_gbps=8865.0, t_two_us=6.631, t_two_split_us=0.02415,
-                       t_fused_split_us=0.2848)
+                       t0_us=2.309, t_round_us=4.153, alpha=1.145, cu_gbps=46.34,
+                       hbm_gbps=8667.0, t_two_us=6.018, t_two_split_us=0.0436,
+                       t_fused_split_us=0.2422)
 
 
 def plan_shape(seq_lens, Hkv, page_size, mode, param):
