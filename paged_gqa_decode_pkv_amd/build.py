@@ -59,9 +59,26 @@ SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitiz
                   "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 
-def build(verbose: bool = False, asm: bool = False, sanitize: bool = False) -> str:
+# The per-workgroup timeline (-DPKV_TIMELINE): the same kernels with
+# realtime-counter marks kept in registers and stored once per workgroup at
+# its exit, and pkv_timeline_read to fetch them.  A separate library beside
+# the product one (libpkv_timeline.so; objects under _build/timeline/),
+# loaded through PKV_LIB_PATH by timeline.py; the product library never
+# contains the marks.
+TIMELINE_FLAGS = ["-DPKV_TIMELINE"]
+TIMELINE_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv_timeline.so")
+
+
+def build(verbose: bool = False, asm: bool = False, sanitize: bool = False,
+          timeline: bool = False) -> str:
+    if sanitize and timeline:
+        raise ValueError("the sanitizer and timeline builds are separate libraries")
     hipcc = _hipcc()
-    out_dir = os.path.join(BUILD_DIR, "sanitize") if sanitize else BUILD_DIR
+    out_dir = BUILD_DIR
+    if sanitize:
+        out_dir = os.path.join(BUILD_DIR, "sanitize")
+    elif timeline:
+        out_dir = os.path.join(BUILD_DIR, "timeline")
     os.makedirs(out_dir, exist_ok=True)
     common = ["-O1" if sanitize else "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall"]
     if sanitize:
@@ -80,14 +97,20 @@ def build(verbose: bool = False, asm: bool = False, sanitize: bool = False) -> s
           os.path.join(CSRC, "runner.cpp"), "-o", run_o], verbose)
     objs.append(run_o)
     dec_o = os.path.join(out_dir, "decode.o")
-    _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS, "-c",
+    _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS,
+          *(TIMELINE_FLAGS if timeline else []), "-c",
           os.path.join(CSRC, "decode.hip"), "-o", dec_o], verbose)
     objs.append(dec_o)
-    if asm:
+    if asm and not (sanitize or timeline):
         _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *common, *DEVICE_FLAGS,
               "--cuda-device-only", "-S", os.path.join(CSRC, "decode.hip"),
               "-o", os.path.join(BUILD_DIR, "decode-gfx950.s")], verbose)
-    lib = os.path.join(out_dir, "libpkv.so") if sanitize else LIB
+    if sanitize:
+        lib = os.path.join(out_dir, "libpkv.so")
+    elif timeline:
+        lib = TIMELINE_LIB
+    else:
+        lib = LIB
     tmp = lib + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", *(SANITIZE_FLAGS if sanitize else []),
           *objs, "-o", tmp], verbose)
@@ -101,5 +124,8 @@ if __name__ == "__main__":
     ap.add_argument("-v", "--verbose", action="store_true")
     ap.add_argument("--sanitize", action="store_true",
                     help="host-side ASan/UBSan build under _build/sanitize/ (CPU checks only)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup timeline build, libpkv_timeline.so (timeline.py)")
     args = ap.parse_args()
-    print(build(verbose=args.verbose, asm=args.asm, sanitize=args.sanitize))
+    print(build(verbose=args.verbose, asm=args.asm, sanitize=args.sanitize,
+                timeline=args.timeline))

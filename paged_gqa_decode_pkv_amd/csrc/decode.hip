@@ -607,6 +607,41 @@ constexpr int ring_depth() {
 // together when the workgroup runs out of tasks or holds kMaxDone of them.
 constexpr int kMaxDone = 64;
 
+// Per-workgroup timeline, in a profiling build only (compiled with
+// -DPKV_TIMELINE: build.py --timeline, read back by timeline.py).  Each
+// workgroup keeps the realtime counter (100 MHz) at fixed points of its run
+// in registers and stores them once, at its exit, into a device array; the
+// product build compiles every mark away.  Marks: 0 entry, 1 device plan
+// done (self-planned step), 2 first page loads issued, 3 prologue barrier
+// passed, 4 first round of the first task consumed, 5 last round of the
+// latest task consumed, 6 task loop left, 7 final arrivals and merges done,
+// 8 exit; slot 9 holds the XCD, slot 10 the tasks run.
+#ifdef PKV_TIMELINE
+constexpr int kTimelineSlots = 16;
+constexpr int kTimelineWorkgroups = 4096;
+__device__ unsigned long long timeline[kTimelineWorkgroups * kTimelineSlots];
+#define PKV_TL_DECL unsigned long long tl_[9] = {}; unsigned tl_tasks_ = 0
+#define PKV_TL_MARK(i) (tl_[i] = __builtin_amdgcn_s_memrealtime())
+#define PKV_TL_TASK() (++tl_tasks_)
+#define PKV_TL_STORE()                                                                     \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kTimelineWorkgroups) {                           \
+      unsigned xcc;                                                                       \
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));                  \
+      unsigned long long* o = timeline + static_cast<size_t>(blockIdx.x) * kTimelineSlots; \
+      for (int k_ = 0; k_ < 8; ++k_) o[k_] = tl_[k_];                                     \
+      o[8] = __builtin_amdgcn_s_memrealtime();                                            \
+      o[9] = xcc;                                                                         \
+      o[10] = tl_tasks_;                                                                  \
+    }                                                                                     \
+  } while (0)
+#else
+#define PKV_TL_DECL
+#define PKV_TL_MARK(i) ((void)0)
+#define PKV_TL_TASK() ((void)0)
+#define PKV_TL_STORE() ((void)0)
+#endif
+
 struct PlanArgs {
   const int32_t* seq_lens;
   int32_t B, Hkv, head_dim, page_size, num_cus;
@@ -1016,6 +1051,8 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int col = lane & 15;
   const int grp = lane >> 4;
+  PKV_TL_DECL;
+  PKV_TL_MARK(0);
 
   __shared__ int s_len[kStaged ? kRowStage : 1];
   __shared__ int s_off[kStaged ? kRowStage + 1 : 1];
@@ -1154,6 +1191,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       }
     }
   }
+  if constexpr (kSelfPlan) PKV_TL_MARK(1);
   // Record of task t of a self-planned step, from the offsets in LDS: the
   // row is the last one whose first task is <= t (rows without tasks share
   // the next row's offset and come before it).  With `publish`, thread 0
@@ -1237,6 +1275,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     const Round<kRing> r0 = load_round<kRing>(a, bt_in, cur, wave, 0);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
+    PKV_TL_MARK(2);
     // written out for read-back behind the page loads (recomputed, so that
     // nothing is held across them)
     self_record(blockIdx.x, true);
@@ -1273,6 +1312,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
                                     rec0);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
+    PKV_TL_MARK(2);
     if constexpr (kStaged) {
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
@@ -1295,6 +1335,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     }
   }
 
+  PKV_TL_MARK(3);
   int n_done = 0;   // entries of s_done (workgroup-uniform)
   for (int it = 0; cur.t < num_tasks; ++it) {
     const int par = it & 1;
@@ -1341,6 +1382,13 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
         else
           valid[r] = issue(cur, kRing * (j + 1) + r, fr.e[r], ring[r]);
       }
+#ifdef PKV_TIMELINE
+      if (it == 0 && j == 0) PKV_TL_MARK(4);
+      if (last) {
+        PKV_TL_MARK(5);
+        PKV_TL_TASK();
+      }
+#endif
       if (last && wave == 0) {
         store_q(nxt, qn, s_q[par ^ 1]);
         if (lane == 0)
@@ -1418,7 +1466,10 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     cur = nxt;
   }
 
+  PKV_TL_MARK(6);
   if (n_done > 0) flush_done<D, kMergeBatch, E>(a, ma, n_done, s_done, s_lastf, &s_o[0][0][0]);
+  PKV_TL_MARK(7);
+  PKV_TL_STORE();
 
   // Last workgroup out resets the counters for the next launch.
   if (tid == 0) {
@@ -1788,6 +1839,20 @@ int launch_any(int head_dim, int dtype, const DecodeArgs& da, const MergeArgs& m
 }  // namespace pkv
 
 extern "C" {
+
+#ifdef PKV_TIMELINE
+// Profiling build only: copy the per-workgroup timeline of the last launch
+// (kTimelineWorkgroups x kTimelineSlots uint64, row w for workgroup w) to
+// host memory.  Returns PKV_OK or PKV_ERR_HIP.
+int pkv_timeline_read(void* host, size_t bytes) {
+  const size_t all = sizeof(pkv::timeline);
+  if (!host) return PKV_ERR_INVALID_ARG;
+  const hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(pkv::timeline),
+                                           bytes < all ? bytes : all, 0,
+                                           hipMemcpyDeviceToHost);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+#endif
 
 int pkv_page_load_mode(int32_t head_dim, int32_t dtype, int64_t num_tasks, int32_t num_cus,
                        int32_t* mode) {
