@@ -37,6 +37,7 @@ sys.path.insert(0, HERE)
 METRIC = "decode tokens/s + achieved KV HBM GB/s (% peak), B8 bimodal Hq32/Hkv8/d128"
 HBM_PEAK_GBPS = 8000.0
 DEVICE_PLAN_MAX_SPLITS = 64
+SPLIT_SWEEP = (8, 16, 32, 64)   # explicit split counts timed on a single-row batch
 
 
 def _kernel_source_hash() -> str:
@@ -270,7 +271,9 @@ def measure(name, args, seed, kv_dtype, steps, warmup):
         dp = {
             "synced_step_us": {"median": round(float(np.median(d_synced)), 2),
                                "p10": round(float(np.percentile(d_synced, 10)), 2),
-                               "p90": round(float(np.percentile(d_synced, 90)), 2)},
+                               "p90": round(float(np.percentile(d_synced, 90)), 2),
+                               "tokens_per_s": round(B / (float(np.median(d_synced)) * 1e-6),
+                                                     2)},
             "back_to_back_us_per_step": round(d_wall / K * 1e6, 2),
             "tokens_per_s": round(B * K / d_wall, 2),
             "plan": {"mode": ["split", "workqueue"][hdr["mode"]], "param": hdr["param"],
@@ -280,6 +283,37 @@ def measure(name, args, seed, kv_dtype, steps, warmup):
                     "step per graph, replayed alone and waited for; back to back: the "
                     f"{L} layer copies' steps in one graph, replayed {max(1, K // L)} times",
         }
+
+    # Explicit split counts of a single-row batch (the pages' sequence
+    # splitting at S = 8..64), each in the launch form the rule gives it:
+    # HIP-event time per step over three windows of 8 back-to-back steps.
+    sweep = None
+    if B == 1 and args.mode is None:
+        sweep = {}
+        for S in SPLIT_SWEEP:
+            for i in range(2 * L):
+                decs[i % L].run(pkv.PKV_MODE_SPLIT, S, stream=stream)
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()        # creates the underlying HIP events
+                e1.record()
+                torch.cuda.synchronize()
+                for i in range(8):
+                    ev = (e0 if i == 0 else None, e1 if i == 7 else None)
+                    decs[i % L].run(pkv.PKV_MODE_SPLIT, S, stream=stream, events=ev)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3 / 8)
+            two_s = bool(decs[0].last[5])
+            us = float(np.median(per))
+            sweep[f"S={S}"] = {"step_us": round(us, 2),
+                               "kv_gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+                               "merge": "two-launch" if two_s else "fused"}
+        for i in range(2 * L):     # back to the policy's plan
+            step(i)
+        torch.cuda.synchronize()
 
     wall = t1 - t0
     win_ms = np.array([e0.elapsed_time(e1) / win for e0, e1 in events])
@@ -349,7 +383,32 @@ def measure(name, args, seed, kv_dtype, steps, warmup):
             },
         },
         "device_planned": dp,
+        "split_sweep": sweep,
+        "merge_state_bytes": merge_state_bytes(cfg, sl_h, num_cus),
     }
+
+
+def merge_state_bytes(cfg, lens, num_cus):
+    """Merge-state traffic of the policy's best split-mode and best workqueue
+    plan for this batch (each by the policy's model, whatever the mode rule
+    picks): partial states written by the split tasks of rows with more than
+    one split and read back by the merge, Hq x (d + 2) fp32 per slot each
+    way."""
+    import paged_gqa_decode_pkv_amd as pkv
+    out = {}
+    for mode, name, cands in ((pkv.PKV_MODE_SPLIT, "split", [2 ** k for k in range(9)]),
+                              (pkv.PKV_MODE_WORKQUEUE, "workqueue",
+                               [4 * 2 ** k for k in range(7)])):
+        best = min(cands, key=lambda v: pkv.pkv_policy_predict(lens, cfg.Hkv, num_cus, mode, v,
+                                                               head_dim=cfg.D))
+        _, offs, _ = pkv.pkv_plan(lens, cfg.Hkv, cfg.max_pages_per_row, mode, best)
+        sp = np.diff(offs)
+        slots = int(sp[sp > 1].sum())
+        out[name] = {"param": best, "partial_slots": slots,
+                     "bytes": 2 * slots * cfg.Hq * (cfg.D + 2) * 4}
+    sb, wb = out["split"]["bytes"], out["workqueue"]["bytes"]
+    out["workqueue_vs_split"] = round(wb / sb, 4) if sb else None
+    return out
 
 
 def main():
@@ -426,6 +485,8 @@ def main():
         "gpu_us": m["gpu_us"],
         "roofline": m["roofline"],
         "device_planned": m["device_planned"],
+        "split_sweep": m["split_sweep"],
+        "merge_state_bytes": m["merge_state_bytes"],
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
@@ -448,6 +509,8 @@ def main():
             "gpu_us": x["gpu_us"],
             "roofline": x["roofline"],
             "device_planned": x["device_planned"],
+            "split_sweep": x["split_sweep"],
+            "merge_state_bytes": x["merge_state_bytes"],
         }
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
