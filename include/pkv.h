@@ -186,8 +186,9 @@ int pkv_policy_defaults(pkv_policy_params* params);
  *   load = ceil(T / A) pmax              if T <= W   (every task static)
  *        = P / A + alpha pmax            otherwise   (dynamic queue),
  *   tile = 2 * page_size * head_dim * 2 bytes (K and V of one page of one
- *          KV head, 2-byte elements; for fp8 pools the callers here pass
- *          head_dim / 2, the same bytes),
+ *          KV head at 2-byte elements; fp8 pools are priced the same, since
+ *          the kernel streams their pages at about the same pages per
+ *          second),
  *   two = maxS > fuse_max_splits and Gr maxS > fuse_max_group_splits, with
  *         Gr = Hkv x (rows with n_b > 0) the (row, KV head) groups,
  *   t = t0_us + t_round_us ceil(T / W) + load tile / (rho 1e3)

@@ -16,8 +16,8 @@ thresholds fixed on a calibration seed and then evaluated on held-out seeds
 
 ``python -m paged_gqa_decode_pkv_amd.policy_fit --revalidate RUNS.jsonl [--name F]``
 judges the committed constants on fresh runs instead (``calibration/F``, by default
-``mi355x_revalidation.json``; fp8-pool runs are judged with the model fed half the
-head dimension, as the runner does).
+``mi355x_revalidation.json``; fp8-pool runs are judged with the model pricing a page as
+a 2-byte page, as the runner does).
 ``python -m paged_gqa_decode_pkv_amd.policy_fit RUNS.jsonl`` writes
 ``calibration/mi355x_runs.json`` (the runs, compacted) and
 ``calibration/mi355x_fit.json`` (constants + evaluation) and prints the table.
@@ -143,9 +143,9 @@ def compact_runs(jsonl_path):
             d["runs"].append(row)
     assert len(dtypes) == 1, dtypes
     dtype = dtypes.pop()
-    # fp8 pools: the model sees half the head dimension (the same bytes per
-    # tile), as the runner passes it
-    head_dim = 64 if dtype in ("fp8", "bf16_fp8") else 128
+    # fp8 pools are priced as 2-byte pools of the same head dimension, as the
+    # runner and the device planner pass it
+    head_dim = 128
     return {"device": "1x MI355X (gfx950), 256 CUs", "Hkv": 8, "head_dim": head_dim, "cus": 256,
             "dtype": dtype,
             "columns": ["mode", "param", "two_launch", "num_tasks", "max_splits", "step_us"],
