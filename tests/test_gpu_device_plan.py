@@ -32,7 +32,7 @@ def _capped_params(pkv, max_pages, cap, groups):
     return p
 
 
-def _run(wl, cap, mode=-1, param=0, workspace=None):
+def _run(wl, cap, mode=-1, param=0, workspace=None, params=None):
     import torch
     import paged_gqa_decode_pkv_amd as pkv
     cfg = wl.cfg
@@ -44,7 +44,8 @@ def _run(wl, cap, mode=-1, param=0, workspace=None):
     out = torch.full_like(wl.q, float("nan"))
     lse = torch.full((B, cfg.Hq), float("nan"), dtype=torch.float32, device="cuda")
     pkv.pkv_decode_device_plan(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, cfg.scale,
-                               out, workspace, cap, lse=lse, mode=mode, param=param)
+                               out, workspace, cap, lse=lse, mode=mode, param=param,
+                               params=params)
     torch.cuda.synchronize()
     hdr, tasks, offs = pkv.pkv_device_plan_read(workspace, B, cfg.Hq, cfg.Hkv, cfg.D, cap)
     return out, lse, hdr, tasks, offs, workspace
@@ -126,6 +127,48 @@ def test_device_policy_under_a_small_capacity():
     out, lse, hdr, tasks, offs, _ = _run(wl, cap=4)
     _check_plan(wl, 4, hdr, tasks, offs, -1, 0)
     assert hdr["max_splits"] <= 4
+    _parity(wl, out, lse)
+
+
+@pytest.mark.parametrize("kind", ["workqueue", "split"])
+def test_device_policy_over_several_candidate_batches(kind):
+    """More than 16 candidates (the device search takes 16 per barrier): 21
+    chunk sizes c = 1 .. 2^20 for a batch, or 18 split counts S = 1 .. 2^17
+    for one row.  The device picks what the host policy picks under the same
+    constants, limits and launch form, and the step matches the oracle."""
+    import paged_gqa_decode_pkv_amd as pkv
+    rng = np.random.default_rng(41 if kind == "workqueue" else 42)
+    if kind == "workqueue":
+        lens = rng.integers(1, 64 * 16 + 1, size=6).tolist()
+        cap = 64
+    else:
+        lens = [int(rng.integers(200, 64 * 16 + 1))]
+        cap = 1 << 17
+    cfg = Config(f"multibatch_{kind}", B=len(lens), Hq=8, Hkv=2, D=64, max_pages_per_row=64,
+                 pool_pages=len(lens) * 64 + 8, lengths=None)
+    wl = make_workload(cfg, 43, device="cuda", seq_lens=lens)
+    log_case("device policy, several candidate batches", kind, lens)
+    p = pkv.pkv_policy_defaults()
+    p.split_max = 1 << 20
+    p.chunk_min = 1
+    p.chunk_max = 1 << 20
+    out, lse, hdr, tasks, offs, _ = _run(wl, cap, params=p)
+    # the host policy under the device path's limits and launch form
+    q = pkv.pkv_policy_defaults()
+    q.split_max = min(p.split_max, cap)
+    c = p.chunk_min
+    while c <= p.chunk_max and -(-64 // c) > cap:
+        c *= 2
+    q.chunk_min, q.chunk_max = c, p.chunk_max
+    q.fuse_max_splits = 2 ** 31 - 1
+    ncand = (q.split_max.bit_length() if kind == "split"
+             else (q.chunk_max // q.chunk_min).bit_length())
+    assert ncand > 16
+    want = pkv.pkv_policy(wl.seq_lens_np, cfg.Hkv, _num_cus(), params=q, head_dim=cfg.D)
+    assert (hdr["mode"], hdr["param"]) == want
+    assert hdr["mode"] == (0 if kind == "split" else 1)
+    rt, ro, slots = pkv.pkv_plan(wl.seq_lens_np, cfg.Hkv, 64, *want)
+    assert np.array_equal(tasks, rt) and np.array_equal(offs, ro)
     _parity(wl, out, lse)
 
 
