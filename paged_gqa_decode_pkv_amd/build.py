@@ -63,7 +63,7 @@ SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitiz
 # realtime-counter marks kept in registers and stored once per workgroup at
 # its exit, and pkv_timeline_read to fetch them.  A separate library beside
 # the product one (libpkv_timeline.so; objects under _build/timeline/),
-# loaded through PKV_LIB_PATH by timeline.py; the product library never
+# loaded by timeline.py in place of the product library, which never
 # contains the marks.
 TIMELINE_FLAGS = ["-DPKV_TIMELINE"]
 TIMELINE_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv_timeline.so")
