@@ -26,9 +26,12 @@ ARCH = "gfx950"
 # atomic optimizer is off too: the decode kernel issues one counter atomic
 # per task from one lane and consumes it a whole task later, and the
 # optimizer's broadcast of the result would force an immediate wait on every
-# load in flight.
+# load in flight.  The first two kernel arguments are preloaded into SGPRs
+# (the decode kernel's task list and its capacity), so the first record load
+# leaves at entry without a round trip to the argument segment.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+                "-mllvm", "-amdgpu-kernarg-preload-count=2"]
 
 
 def _hipcc() -> str:

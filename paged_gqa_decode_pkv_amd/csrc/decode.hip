@@ -857,9 +857,8 @@ struct Meta {
 // The record of task t (a scalar load).  The index is clamped to the
 // readable records, so the load does not wait for the task count; records
 // past the count are never used.
-__device__ __forceinline__ int4 load_record(const DecodeArgs& a, const int4* __restrict__ tasks,
-                                            int t) {
-  return tasks[t < a.task_cap ? t : a.task_cap - 1];
+__device__ __forceinline__ int4 load_record(const int4* __restrict__ tasks, int task_cap, int t) {
+  return tasks[t < task_cap ? t : task_cap - 1];
 }
 
 template <bool kStaged, int R>
@@ -928,11 +927,11 @@ __device__ __forceinline__ Meta decode_meta(const DecodeArgs& a,
 
 template <bool kStaged, int R>
 __device__ __forceinline__ Meta load_meta(const DecodeArgs& a, const int4* __restrict__ tasks,
-                                          const int32_t* __restrict__ seq_lens,
+                                          int task_cap, const int32_t* __restrict__ seq_lens,
                                           const int32_t* __restrict__ offs, const int* s_len,
                                           const int* s_off, int num_tasks, int t) {
   return decode_meta<kStaged, R>(a, seq_lens, offs, s_len, s_off, num_tasks, t,
-                              load_record(a, tasks, t));
+                              load_record(tasks, task_cap, t));
 }
 
 // Count in n deferred split tasks (row, KV head, first slot, splits) of this
@@ -1035,7 +1034,7 @@ __device__ __forceinline__ Round<R> first_round(const DecodeArgs& a,
 // larger tiles and accumulators need the AGPR half of the register file.
 template <int D, bool kStaged, class E, class KV, bool kSelfPlan, int kLoadMode>
 __global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
-pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
+pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArgs a,
                   const int32_t* __restrict__ bt_in, const int32_t* __restrict__ seq_lens_in,
                   const int32_t* __restrict__ offs_in) {
   constexpr int KK = D / 32;
@@ -1053,6 +1052,21 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
   const int grp = lane >> 4;
   PKV_TL_DECL;
   PKV_TL_MARK(0);
+  // Host plan: the first task's record is the kernel's first load.  Its
+  // address needs only the first two kernel arguments, which the kernel
+  // finds in SGPRs at entry (kernarg preload): no round trip to the
+  // argument segment lies before it.
+  uint4x rec0v{};
+  if constexpr (!kSelfPlan) {
+    const int t0 = static_cast<int>(blockIdx.x) < task_cap ? static_cast<int>(blockIdx.x)
+                                                           : task_cap - 1;
+    // a vector load marked volatile (aux bit 31): the compiler keeps it here
+    // instead of sinking it behind the argument loads to its first use
+    const uint32_t recs = static_cast<uint32_t>(t0) + 1u;   // records t0 may lie in
+    rec0v = __builtin_bit_cast(uint4x, __builtin_amdgcn_raw_buffer_load_b128(
+        make_rsrc(tasks_in, recs * 16u), 16 * t0, 0, static_cast<int>(1u << 31)));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   __shared__ int s_len[kStaged ? kRowStage : 1];
   __shared__ int s_off[kStaged ? kRowStage + 1 : 1];
@@ -1281,26 +1295,36 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
     self_record(blockIdx.x, true);
   } else {
     // Host plan.  The first task does not wait for the staging: its record
-    // (scalar) goes out first, then the staging loads (vector); from the
-    // record alone the first round's table entries (scalar) and q (vector,
-    // behind the staging loads, so their wait does not cover it); its row
-    // bounds are read from global memory (scalar), not from the staged
-    // copy.  Three scalar round trips lie before the first page load; the
-    // staging completes in their shadow and is stored to LDS for the later
-    // tasks.  The scheduling barriers keep that order.
-    const int4 rec0 = load_record(a, tasks_in, blockIdx.x);
-    __builtin_amdgcn_sched_barrier(0);
+    // went out at entry, the staging loads go out behind it (vector loads
+    // complete in order, so the record's wait does not cover them); from the
+    // record alone come the first round's table entries (scalar) and q
+    // (vector); its row bounds are read from global memory (scalar), not from
+    // the staged copy.  Two round trips lie before the first page load, the
+    // record's and the table's; the argument loads and the staging complete
+    // in their shadow, and the staging is stored to LDS for the later tasks.
+    // The scheduling barriers keep that order.
     constexpr int kPer = kStaged ? (kRowStage + kThreads) / kThreads : 1;   // B+1 <= kRowStage+1
     int lv[kPer], ov[kPer];
     if constexpr (kStaged) {
+      // Buffer loads bounded by the arrays' sizes (entries past them read
+      // 0): no branch around them, so the wait for the record below counts
+      // exactly the loads issued before it and none of these.
+      const __amdgpu_buffer_rsrc_t len_rsrc =
+          make_rsrc(seq_lens_in, static_cast<uint32_t>(a.B) * 4u);
+      const __amdgpu_buffer_rsrc_t off_rsrc =
+          make_rsrc(offs_in, static_cast<uint32_t>(a.B + 1) * 4u);
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const int i = tid + k * kThreads;
-        lv[k] = i < a.B ? seq_lens_in[i] : 0;
-        ov[k] = i <= a.B ? offs_in[i] : 0;
+        lv[k] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(len_rsrc, 4 * i, 0, 0));
+        ov[k] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(off_rsrc, 4 * i, 0, 0));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    const int4 rec0{static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[0])),
+                    static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[1])),
+                    static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[2])),
+                    static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[3]))};
     const Round<kRing> r0 = first_round<kRing>(a, bt_in, rec0, wave);
     if (wave == 0) {
       const int qb = clamp_index(rec0.x, a.B);
@@ -1346,7 +1370,7 @@ pkv_decode_kernel(DecodeArgs a, const int4* __restrict__ tasks_in,
       nxt = decode_meta<kStaged, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, t_nxt,
                                         self_record(t_nxt, true));
     else
-      nxt = load_meta<kStaged, kRing>(a, tasks_in, seq_lens_in, offs_in, s_len, s_off,
+      nxt = load_meta<kStaged, kRing>(a, tasks_in, task_cap, seq_lens_in, offs_in, s_len, s_off,
                                       num_tasks, t_nxt);
     const Round<kRing> nr0 = load_round<kRing>(a, bt_in, nxt, wave, 0);
     // Wave 0: the index after next (counter atomic, issued now) and the next
@@ -1746,25 +1770,25 @@ int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t
     if (da.plan_out) {   // self-planned step (staged rows only; checked by the caller)
       // (load_mode never gives mode 2 to a self-planned step)
       hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true, kMode == 2 ? 1 : kMode>),
-                         dim3(grid), dim3(kThreads), 0, stream, da, tasks, da.block_table,
-                         da.seq_lens, da.split_offsets);
+                         dim3(grid), dim3(kThreads), 0, stream, tasks, da.task_cap, da,
+                         da.block_table, da.seq_lens, da.split_offsets);
     } else if (ev0 || ev_dec_end) {
       if (staged)
         hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
-                              dim3(kThreads), 0, stream, ev0, ev_dec_end, 0, da, tasks,
-                              da.block_table, da.seq_lens, da.split_offsets);
+                              dim3(kThreads), 0, stream, ev0, ev_dec_end, 0, tasks, da.task_cap,
+                              da, da.block_table, da.seq_lens, da.split_offsets);
       else
         hipExtLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kMode>), dim3(grid),
-                              dim3(kThreads), 0, stream, ev0, ev_dec_end, 0, da, tasks,
-                              da.block_table, da.seq_lens, da.split_offsets);
+                              dim3(kThreads), 0, stream, ev0, ev_dec_end, 0, tasks, da.task_cap,
+                              da, da.block_table, da.seq_lens, da.split_offsets);
     } else if (staged) {
       hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
-                         dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
-                         da.split_offsets);
+                         dim3(kThreads), 0, stream, tasks, da.task_cap, da, da.block_table,
+                         da.seq_lens, da.split_offsets);
     } else {
       hipLaunchKernelGGL((pkv_decode_kernel<D, false, E, KV, false, kMode>), dim3(grid),
-                         dim3(kThreads), 0, stream, da, tasks, da.block_table, da.seq_lens,
-                         da.split_offsets);
+                         dim3(kThreads), 0, stream, tasks, da.task_cap, da, da.block_table,
+                         da.seq_lens, da.split_offsets);
     }
   } else {
     // no decode kernel (no tasks): the events still mark this point of the stream
