@@ -288,6 +288,23 @@ def test_gqa_16_long_bimodal(D, Hkv):
 
 # --------------------------------------------------------------------------- large batches
 
+@pytest.mark.parametrize("B", [1023, 1024])
+def test_batch_at_the_lds_staging_limit(B):
+    """B = 1023 and 1024 rows, the largest batches staged in LDS: the
+    staging reads lengths [0, B) and offsets [0, B] in five bounded loads per
+    thread, the last one reaching offsets[B]."""
+    rng = np.random.default_rng(37 + B)
+    lens = rng.integers(0, 200, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    lens[-1] = 177   # the last row has work
+    cfg = Config(f"b{B}", B=0, Hq=8, Hkv=2, D=64, max_pages_per_row=13, pool_pages=B * 13 + 64,
+                 lengths=lambda r: np.zeros(0))
+    wl = make_workload(cfg, 37, device="cuda", seq_lens=lens.tolist())
+    rows = sorted(set(rng.choice(B, size=48, replace=False).tolist()) | {0, B - 2, B - 1})
+    for mode, param, two in [(None, None, None), (1, 4, True), (0, 2, False)]:
+        _parity(wl, mode, param, rows=rows, two_launch=two)
+
+
 @pytest.mark.parametrize("two_launch", TWO)
 def test_batch_beyond_lds_staging(two_launch):
     """B > 1024 rows: the kernel variant that reads row lengths and split
