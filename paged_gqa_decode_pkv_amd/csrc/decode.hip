@@ -593,14 +593,22 @@ __device__ __forceinline__ void write_empty_group(const MergeArgs& a, int b, int
 // Batches up to kRowStage rows get their lengths and split offsets staged in
 // LDS once per workgroup.  Larger batches read them with scalar loads.
 constexpr int kRowStage = 1024;
-// Page tiles in flight per wave (one "round"): 4 at d <= 128; at d = 256 a
-// tile holds twice the bytes and registers, so 2 keep the same 32 KiB in
-// flight per wave within the register budget.  fp8 pools keep the same
-// depth (half the bytes in flight): twice the depth measured 3 us slower on
-// the short B1 / B4 / B8 steps and within 3% on the long ones.
-template <int D>
+// Page tiles in flight per wave (one "round").  Plans of at most two tasks
+// per CU (load modes 0 and 1): about 16 KiB of K and V per wave.  A 2-byte
+// page at d = 128 holds 8 KiB, so 2; at d = 64 and for fp8 pools at d = 128
+// a page holds 4 KiB, so 4 (the most the task rounds use).  At d = 256 a
+// 2-byte page holds 16 KiB and a wave keeps 2, so that it still has a page in
+// flight while it consumes one.  Plans of more tasks (load mode 2, two
+// workgroups per CU that stream for hundreds of microseconds) keep 4 at
+// d = 128.  Measured with 2-byte pools at d = 128: 16 KiB per wave instead of
+// 32 made the short steps 0.3-0.9 us faster (B1, B1 bucketed, B4 and B8;
+// the extra bytes in flight only lengthen every load's wait in the memory
+// queues) and the long ones 0.7-2.2% slower (B64, B32); for fp8 pools twice
+// the depth was 3 us slower on the short steps.
+template <int D, class KV, int kLoadMode>
 constexpr int ring_depth() {
-  return D == 256 ? 2 : 4;
+  if constexpr (D == 256) return 2;
+  return (D == 128 && kv_bytes<KV>() == 2 && kLoadMode != 2) ? 2 : 4;
 }
 
 // Split tasks of a workgroup whose arrival is deferred: they are counted in
@@ -1042,7 +1050,7 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
   constexpr int LDS_STRIDE = D + 4;
   constexpr int kKvb = kv_bytes<KV>();
   constexpr uint32_t kTileBytes = static_cast<uint32_t>(kPage * D * kKvb);
-  constexpr int kRing = ring_depth<D>();
+  constexpr int kRing = ring_depth<D, KV, kLoadMode>();
   constexpr int kGroup = kMaxG;
 
   const int tid = threadIdx.x;
@@ -1495,8 +1503,12 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
   PKV_TL_MARK(7);
   PKV_TL_STORE();
 
-  // Last workgroup out resets the counters for the next launch.
-  if (tid == 0) {
+  // Last workgroup out resets the counters for the next launch.  With no
+  // more tasks than workgroups every task is static: no workgroup touched
+  // the task counter (its next index, blockIdx.x + gridDim.x, is past the
+  // list), so there is nothing to reset and no workgroup waits for the exit
+  // count (a round trip at the end of the launch, about 0.5 us at B8).
+  if (tid == 0 && num_tasks > static_cast<int>(gridDim.x)) {
     const uint32_t prev = atomicAdd(a.ctrl + 1, 1u);
     if (prev == gridDim.x - 1) {
       atomicExch(a.ctrl, 0u);

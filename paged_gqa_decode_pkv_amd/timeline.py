@@ -215,6 +215,7 @@ def main(argv=None):
             print(f"  {kind}: " + "; ".join(f"{k} {v:.2f}" for k, v in split.items()),
                   flush=True)
         if args.out_dir:
+            os.makedirs(args.out_dir, exist_ok=True)
             write_markdown(os.path.join(args.out_dir, f"decode_{name}_timeline.md"), name,
                            args.seed, wl.kv_bytes, results, command)
     return 0
