@@ -869,11 +869,19 @@ __device__ __forceinline__ int4 load_record(const int4* __restrict__ tasks, int 
   return tasks[t < task_cap ? t : task_cap - 1];
 }
 
-template <bool kStaged, int R>
-__device__ __forceinline__ Meta decode_meta(const DecodeArgs& a,
-                                            const int32_t* __restrict__ seq_lens,
-                                            const int32_t* __restrict__ offs, const int* s_len,
-                                            const int* s_off, int num_tasks, int t, int4 rec) {
+// v clamped into [0, n) (n >= 1), wave-uniform.
+__device__ __forceinline__ int clamp_index(int v, int n) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  return v < 0 ? 0 : (v >= n ? n - 1 : v);
+}
+
+// Task metadata from its record and its row's length and split offsets
+// (N = seq_lens[b], o0 = offs[b], o1 = offs[b + 1], read by the caller for
+// the record's row clamped into range, so that the reads may leave before
+// the record is checked).
+template <int R>
+__device__ __forceinline__ Meta meta_from_row(const DecodeArgs& a, int num_tasks, int t, int4 rec,
+                                              int N, int o0, int o1) {
   Meta m;
   m.t = t;
   m.b = m.g = m.N = m.p0 = m.p1 = m.Sb = m.o0 = 0;
@@ -888,19 +896,6 @@ __device__ __forceinline__ Meta decode_meta(const DecodeArgs& a,
   if (!(b >= 0 && b < a.B && g >= 0 && g < a.Hkv && s >= 0 && c >= 1)) {
     if (threadIdx.x == 0) flag_error(a.ctrl, PKV_DEVERR_TASK);
     return m;
-  }
-  // Staging is a compile-time choice.  A runtime select between an LDS and
-  // a global pointer would become a flat load, whose wait also drains every
-  // page load in flight.
-  int N, o0, o1;
-  if constexpr (kStaged) {
-    N = s_len[b];
-    o0 = s_off[b];
-    o1 = s_off[b + 1];
-  } else {
-    N = seq_lens[b];
-    o0 = offs[b];
-    o1 = offs[b + 1];
   }
   N = __builtin_amdgcn_readfirstlane(N);
   o0 = __builtin_amdgcn_readfirstlane(o0);
@@ -931,6 +926,28 @@ __device__ __forceinline__ Meta decode_meta(const DecodeArgs& a,
   m.rounds = (per_wave + R - 1) / R;
   m.ok = true;
   return m;
+}
+
+template <bool kStaged, int R>
+__device__ __forceinline__ Meta decode_meta(const DecodeArgs& a,
+                                            const int32_t* __restrict__ seq_lens,
+                                            const int32_t* __restrict__ offs, const int* s_len,
+                                            const int* s_off, int num_tasks, int t, int4 rec) {
+  // Staging is a compile-time choice.  A runtime select between an LDS and
+  // a global pointer would become a flat load, whose wait also drains every
+  // page load in flight.
+  const int b = clamp_index(rec.x, a.B);
+  int N, o0, o1;
+  if constexpr (kStaged) {
+    N = s_len[b];
+    o0 = s_off[b];
+    o1 = s_off[b + 1];
+  } else {
+    N = seq_lens[b];
+    o0 = offs[b];
+    o1 = offs[b + 1];
+  }
+  return meta_from_row<R>(a, num_tasks, t, rec, N, o0, o1);
 }
 
 template <bool kStaged, int R>
@@ -998,12 +1015,6 @@ __device__ __forceinline__ Round<R> load_round(const DecodeArgs& a, const int32_
   return r;
 }
 
-// v clamped into [0, n) (n >= 1), wave-uniform.
-__device__ __forceinline__ int clamp_index(int v, int n) {
-  v = __builtin_amdgcn_readfirstlane(v);
-  return v < 0 ? 0 : (v >= n ? n - 1 : v);
-}
-
 // The first round's block-table entries of the task in record `rec`, for
 // this wave, from the record alone (the row's length is not yet known):
 // positions p0 + wave + 4i of the chunk [p0, p0 + c), p0 = split * c,
@@ -1014,7 +1025,8 @@ __device__ __forceinline__ int clamp_index(int v, int n) {
 // columns (max_pages = 0: no row has a page) is not read.
 template <int R>
 __device__ __forceinline__ Round<R> first_round(const DecodeArgs& a,
-                                                const int32_t* __restrict__ bt, int4 rec,
+                                                const int32_t* __restrict__ bt,
+                                                const int32_t* __restrict__ spare, int4 rec,
                                                 int wave) {
   Round<R> r;
   const int b = clamp_index(rec.x, a.B);
@@ -1024,17 +1036,19 @@ __device__ __forceinline__ Round<R> first_round(const DecodeArgs& a,
   const int64_t p0 = static_cast<int64_t>(s < 0 ? 0 : s) * cc;
   const int64_t end = p0 + cc < a.max_pages ? p0 + cc : a.max_pages;
   const int64_t last = end - 1 > 0 ? end - 1 : 0;
-  if (a.max_pages > 0) {
-    const int32_t* row = bt + static_cast<int64_t>(b) * a.max_pages;
+  // No branch around the loads (a table without columns reads entry 0 of
+  // `spare`, a readable array, and the values are dropped), so they issue in
+  // the same block as the caller's loads and share one wait.
+  const bool cols = a.max_pages > 0;
+  const int32_t* row = cols ? bt + static_cast<int64_t>(b) * a.max_pages : spare;
+  int e[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int64_t pos = p0 + wave + kWaves * i;
-      r.e[i] = row[pos < last ? pos : last];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < R; ++i) r.e[i] = 0;
+  for (int i = 0; i < R; ++i) {
+    const int64_t pos = p0 + wave + kWaves * i;
+    e[i] = row[cols ? (pos < last ? pos : last) : 0];
   }
+#pragma unroll
+  for (int i = 0; i < R; ++i) r.e[i] = cols ? e[i] : 0;
   return r;
 }
 
@@ -1333,15 +1347,18 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
                     static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[1])),
                     static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[2])),
                     static_cast<int>(__builtin_amdgcn_readfirstlane(rec0v[3]))};
-    const Round<kRing> r0 = first_round<kRing>(a, bt_in, rec0, wave);
-    if (wave == 0) {
-      const int qb = clamp_index(rec0.x, a.B);
-      const int qg = clamp_index(rec0.y, a.Hkv);
-      load_q(qb, qg, true, qf);
-    }
+    // The first round's table entries and the row's length and split
+    // offsets are read together (scalar), for the record's row clamped into
+    // range: one round trip after the record's, then the page loads.
+    const int rb = clamp_index(rec0.x, a.B);
+    const Round<kRing> r0 = first_round<kRing>(a, bt_in, seq_lens_in, rec0, wave);
+    const int rN = seq_lens_in[rb];
+    const int ro0 = offs_in[rb];
+    const int ro1 = offs_in[rb + 1];
+    cur = meta_from_row<kRing>(a, num_tasks, blockIdx.x, rec0, rN, ro0, ro1);
     __builtin_amdgcn_sched_barrier(0);
-    cur = decode_meta<false, kRing>(a, seq_lens_in, offs_in, s_len, s_off, num_tasks, blockIdx.x,
-                                    rec0);
+    // q goes out just ahead of the pages, so that its wait covers no page
+    if (wave == 0) load_q(rb, clamp_index(rec0.y, a.Hkv), true, qf);
 #pragma unroll
     for (int r = 0; r < kRing; ++r) valid[r] = issue(cur, r, r0.e[r], ring[r]);
     PKV_TL_MARK(2);
