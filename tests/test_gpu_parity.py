@@ -190,6 +190,35 @@ def test_repeated_launches_deterministic_and_counter_reset():
     check_close(b.float().cpu().numpy(), ref_out)
 
 
+def test_static_and_dynamic_plans_alternate_on_one_workspace():
+    """A plan with no more tasks than workgroups never touches the task
+    counter and skips the exit count; one with more uses and resets both.
+    Alternated on one workspace, every step matches a fresh decoder bit for
+    bit, and the task counter, the exit counter and the fused merge's arrival
+    counters read zero after each step."""
+    import torch
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    # c = 128: 256 tasks, all static on an MI355X; c = 8 and S = 64: more
+    # tasks than workgroups, fetched from the counter
+    steps = [(1, 128), (1, 8), (1, 128), (1, 128), (0, 64), (1, 128), (1, 8)]
+    fresh = {}
+    for mode, param in sorted(set(steps)):
+        out, lse, _ = run_hip(wl, mode, param)
+        fresh[(mode, param)] = (out.cpu().numpy(), lse.cpu().numpy())
+    dec = None
+    for mode, param in steps:
+        log_case("static/dynamic alternation", "mode", mode, "param", param)
+        out, lse, dec = run_hip(wl, mode, param, decoder=dec)
+        assert np.array_equal(out.cpu().numpy(), fresh[(mode, param)][0])
+        assert np.array_equal(lse.cpu().numpy(), fresh[(mode, param)][1])
+        assert dec.error_flags() == 0
+        words = dec.workspace[:4 * (64 + 64)].view(torch.int32).cpu().numpy()
+        assert words[0] == 0 and words[1] == 0, f"task / exit counter left at {words[:2]}"
+        assert not words[64:].any(), "an arrival counter was left non-zero"
+    ref_out, _ = oracle_rows(wl)
+    check_close(fresh[(1, 128)][0].astype(np.float64), ref_out)
+
+
 def test_plan_device_copy_reuse_and_switch():
     """One runner over steps whose plans repeat and change.  A repeated plan is
     read from the runner's device copy, a changed one from pinned host memory
