@@ -1319,12 +1319,12 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
     // Host plan.  The first task does not wait for the staging: its record
     // went out at entry, the staging loads go out behind it (vector loads
     // complete in order, so the record's wait does not cover them); from the
-    // record alone come the first round's table entries (scalar) and q
-    // (vector); its row bounds are read from global memory (scalar), not from
-    // the staged copy.  Two round trips lie before the first page load, the
-    // record's and the table's; the argument loads and the staging complete
-    // in their shadow, and the staging is stored to LDS for the later tasks.
-    // The scheduling barriers keep that order.
+    // record alone come the first round's table entries and its row bounds
+    // (scalar loads from global memory, not from the staged copy, issued
+    // together), then q (vector).  Two round trips lie before the first page
+    // load, the record's and the table's; the argument loads and the staging
+    // complete in their shadow, and the staging is stored to LDS for the
+    // later tasks.  The scheduling barriers keep that order.
     constexpr int kPer = kStaged ? (kRowStage + kThreads) / kThreads : 1;   // B+1 <= kRowStage+1
     int lv[kPer], ov[kPer];
     if constexpr (kStaged) {
