@@ -455,6 +455,13 @@ int pkv_merge(const int32_t* split_offsets, int64_t num_partial_slots, int32_t B
  *                pkv_workspace_init.  Layout: the pkv_decode workspace for
  *                B * max_splits partial slots, then the plan area: header
  *                (16 int32), split_offsets (B+1, padded to 16 B), records.
+ *                Header words 8..11 keep the last policy decision made on
+ *                the device (with B <= 1024), keyed by a hash of the rows'
+ *                page counts, the shape, num_cus and `policy`: a later step
+ *                with the same key takes it instead of searching the
+ *                candidates.  An entry that fails its check word or is not
+ *                a candidate of the step is ignored, so a stale or
+ *                overwritten entry costs one search, never a wrong plan.
  * Errors: those of pkv_decode; PKV_ERR_INVALID_ARG for mode outside
  * {-1, 0, 1}, max_splits < 1, an explicit schedule that could exceed
  * max_splits for some row of up to max_pages_per_row pages, or invalid

@@ -751,6 +751,76 @@ struct PickLds {
 // every thread takes the first fastest of the four waves'.  active_rows:
 // rows with at least one page; row_n(b): pages of row b (0 for an empty or
 // flagged row).  All threads call it and all get the choice.
+// The policy decision of a self-planned step is kept in the plan header
+// (words 8..11: key, mode, param, check) for the next step on the same
+// workspace.  The key hashes everything the decision depends on: the batch
+// size, the page count of every row (flagged rows as 0), the shape, the CU
+// count and the policy's parameters.  A later step whose key matches takes
+// the kept decision instead of searching; a torn or stale entry fails the
+// check, the key or the candidate-set test and the step searches.  The
+// decision only selects among valid plans, so a kept one can change a step's
+// speed, never its result.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+constexpr int kPlanCacheWord = 8;   // plan header words 8..11
+
+__device__ __forceinline__ uint32_t plan_cache_check(uint32_t key, uint32_t mode,
+                                                     uint32_t param) {
+  return mix32(key ^ mix32(mode * 0x9e3779b1u + 0x632be5abu) ^ mix32(param + 0x85ebca77u));
+}
+
+// Key of the policy's inputs other than the rows: shape, CU count, policy
+// parameters (their bit patterns).
+__device__ __forceinline__ uint32_t plan_cache_config_key(const pkv_policy_params& p, int B,
+                                                          int Hkv, int num_cus, int head_dim,
+                                                          int max_pages) {
+  uint32_t h = mix32(static_cast<uint32_t>(B) + 0x27d4eb2du);
+  h = mix32(h ^ static_cast<uint32_t>(Hkv));
+  h = mix32(h ^ static_cast<uint32_t>(num_cus));
+  h = mix32(h ^ static_cast<uint32_t>(head_dim));
+  h = mix32(h ^ static_cast<uint32_t>(max_pages));
+  h = mix32(h ^ static_cast<uint32_t>(p.split_max));
+  h = mix32(h ^ static_cast<uint32_t>(p.chunk_min));
+  h = mix32(h ^ static_cast<uint32_t>(p.chunk_max));
+  h = mix32(h ^ static_cast<uint32_t>(p.fuse_max_splits));
+  h = mix32(h ^ static_cast<uint32_t>(p.fuse_max_group_splits));
+  const double d[8] = {p.t0_us, p.t_round_us, p.alpha, p.cu_gbps,
+                       p.hbm_gbps, p.t_two_us, p.t_two_split_us, p.t_fused_split_us};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, d[i]);
+    h = mix32(h ^ static_cast<uint32_t>(u));
+    h = mix32(h ^ static_cast<uint32_t>(u >> 32));
+  }
+  return h;
+}
+
+// Whether (mode, param) is one of the candidates the policy would search for
+// a batch with `active_rows` rows with pages (the explainer's mode rule).
+__device__ __forceinline__ bool plan_cache_candidate(const pkv_policy_params& p,
+                                                     int active_rows, uint32_t mode,
+                                                     uint32_t param) {
+  int nchunk = 0;
+  for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2) ++nchunk;
+  const bool use_split = active_rows <= 1 || nchunk == 0;
+  if (active_rows == 0) return mode == PKV_MODE_SPLIT && param == 1;
+  if (use_split) {
+    return mode == PKV_MODE_SPLIT && param >= 1 && (param & (param - 1)) == 0 &&
+           static_cast<int64_t>(param) <= p.split_max;
+  }
+  if (mode != PKV_MODE_WORKQUEUE || p.chunk_min < 1) return false;
+  for (int64_t c = p.chunk_min; c <= p.chunk_max; c *= 2)
+    if (c == static_cast<int64_t>(param)) return true;
+  return false;
+}
+
 template <class RowN>
 __device__ void choose_plan(const pkv_policy_params& p, int B, int Hkv, int num_cus,
                             int head_dim, int page_size, RowN row_n, int64_t active_rows,
@@ -1103,7 +1173,7 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
   __shared__ int s_lastf[kMaxDone];
   // self-planned step only: the policy's candidate search and the row scan
   __shared__ typename std::conditional<kSelfPlan, PickLds, char>::type s_pick;
-  __shared__ int s_plan[kSelfPlan ? 4 * kWaves : 1];
+  __shared__ int s_plan[kSelfPlan ? 5 * kWaves : 1];
   static_assert(kWaves * kGroup * LDS_STRIDE >= merge_lds_floats<D>(), "merge scratch");
   static_assert(!kSelfPlan || kStaged, "a self-planned step stages its rows");
 
@@ -1130,37 +1200,71 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
       const int i = tid + k * kThreads;
       lv[k] = i < a.B ? seq_lens_in[i] : 0;
     }
+    // the decision kept by the previous step on this workspace (coherent
+    // load: it may have been written on another XCD)
+    const uint4x kept = __builtin_bit_cast(uint4x, __builtin_amdgcn_raw_buffer_load_b128(
+        make_rsrc(a.plan_out + kPlanCacheWord, 16u), 0, 0, kCoherent));
     // A row with N < 0 or more than max_pages pages is flagged and planned
     // empty (its length staged as 0).  Rows with pages and flagged rows are
     // counted per wave (ballots) into LDS slots of their own: nothing to
     // clear, one barrier.
     int wact = 0, wbad = 0;
+    uint32_t rkey = 0;   // XOR of the rows' (index, page count) hashes
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kThreads;
       const int N = lv[k];
       const bool ok = N >= 0 && (static_cast<int64_t>(N) + kPage - 1) / kPage <= a.max_pages;
-      if (i < a.B) s_len[i] = ok ? N : 0;
+      if (i < a.B) {
+        s_len[i] = ok ? N : 0;
+        const uint32_t n = ok ? static_cast<uint32_t>((N + kPage - 1) / kPage) : 0u;
+        rkey ^= mix32(mix32(static_cast<uint32_t>(i) + 0x165667b1u) ^ n);
+      }
       wact += __builtin_popcountll(__ballot(i < a.B && ok && N > 0));
       wbad |= __ballot(i < a.B && !ok) != 0 ? 1 : 0;
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) rkey ^= __shfl_xor(rkey, off);
     if (lane == 0) {
       s_plan[wave] = wact;
       s_plan[kWaves + wave] = wbad;
+      s_plan[4 * kWaves + wave] = static_cast<int>(rkey);
     }
     __syncthreads();
     int active_rows = 0, any_bad = 0;
+    uint32_t key = plan_cache_config_key(a.plan_pol, a.B, a.Hkv, a.plan_num_cus,
+                                         a.plan_head_dim, a.max_pages);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       active_rows += s_plan[w];
       any_bad |= s_plan[kWaves + w];
+      key ^= static_cast<uint32_t>(s_plan[4 * kWaves + w]);
     }
+    key = mix32(key);
     auto row_n = [&](int b) -> int32_t { return (s_len[b] + kPage - 1) / kPage; };
     plan_mode = a.plan_mode;
     plan_param = a.plan_param;
-    if (plan_mode < 0)
-      choose_plan(a.plan_pol, a.B, a.Hkv, a.plan_num_cus, a.plan_head_dim, kPage, row_n,
-                  active_rows, s_pick, plan_mode, plan_param);
+    if (plan_mode < 0) {
+      const uint32_t kkey = __builtin_amdgcn_readfirstlane(kept[0]);
+      const uint32_t kmode = __builtin_amdgcn_readfirstlane(kept[1]);
+      const uint32_t kparam = __builtin_amdgcn_readfirstlane(kept[2]);
+      const uint32_t kcheck = __builtin_amdgcn_readfirstlane(kept[3]);
+      if (kkey == key && kcheck == plan_cache_check(kkey, kmode, kparam) &&
+          plan_cache_candidate(a.plan_pol, active_rows, kmode, kparam)) {
+        plan_mode = static_cast<int>(kmode);
+        plan_param = static_cast<int>(kparam);
+      } else {
+        choose_plan(a.plan_pol, a.B, a.Hkv, a.plan_num_cus, a.plan_head_dim, kPage, row_n,
+                    active_rows, s_pick, plan_mode, plan_param);
+        if (blockIdx.x == 0 && tid == 0) {
+          const uint32_t m = static_cast<uint32_t>(plan_mode);
+          const uint32_t pr = static_cast<uint32_t>(plan_param);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              uint4x{key, m, pr, plan_cache_check(key, m, pr)},
+              make_rsrc(a.plan_out + kPlanCacheWord, 16u), 0, 0, kCoherent);
+        }
+      }
+    }
     // splits per row, then their exclusive prefix: thread t takes rows
     // kRows*t .. kRows*t + kRows-1
     int sv[kRows];

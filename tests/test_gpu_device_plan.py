@@ -208,6 +208,61 @@ def test_device_plan_reused_workspace_new_lengths():
             _parity(wl, out, lse)
 
 
+def test_device_plan_kept_decision_follows_lengths_and_limits():
+    """A self-planned step keeps its policy decision in the plan header for the
+    next step on the workspace, keyed by the batch's page counts, shape and
+    policy limits.  Steps that repeat a batch, change it, or change the
+    capacity (and so the candidate sets) each take the host policy's decision
+    under their own limits."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    wls = {s: make_workload("b8_bimodal", s, device="cuda") for s in HELD_OUT_SEEDS[:2]}
+    cfg = wls[HELD_OUT_SEEDS[0]].cfg
+    need = pkv.pkv_workspace_size_device_plan(cfg.B, cfg.Hq, cfg.Hkv, cfg.D, 256)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    pkv.pkv_workspace_init(ws)
+    steps = [(0, 256), (0, 256), (1, 256), (1, 4), (1, 4), (0, 4), (0, 256), (1, 256)]
+    for w, cap in steps:
+        wl = wls[HELD_OUT_SEEDS[w]]
+        log_case("kept decision", "seed", wl.seed, "cap", cap)
+        out, lse, hdr, tasks, offs, _ = _run(wl, cap=cap, workspace=ws)
+        _check_plan(wl, cap, hdr, tasks, offs, -1, 0)
+        _parity(wl, out, lse)
+
+
+def test_device_plan_ignores_a_corrupt_kept_decision():
+    """Garbage in the kept-decision words of the plan header (a torn write, a
+    stale workspace) never reaches the plan: each step still takes the host
+    policy's decision and matches the oracle, bit for bit with a clean run."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    wl = make_workload("b1", SEED, device="cuda")
+    cfg = wl.cfg
+    B = len(wl.seq_lens_np)
+    cap = 64
+    plan_off = pkv.pkv_workspace_size(B * cap, cfg.Hq, cfg.D)
+    ref_out, ref_lse, hdr0, tasks0, offs0, ws = _run(wl, cap=cap)
+    _check_plan(wl, cap, hdr0, tasks0, offs0, -1, 0)
+    rng = np.random.default_rng(7)
+    words = ws[plan_off:plan_off + 64].view(torch.int32)
+    kept = words[8:12].clone()
+    trials = [rng.integers(-2 ** 31, 2 ** 31, size=4, dtype=np.int64) for _ in range(4)]
+    trials.append(np.zeros(4, dtype=np.int64))
+    good = kept.cpu().numpy().astype(np.int64)
+    for k in range(4):           # the kept entry with one word changed
+        t = good.copy()
+        t[k] ^= 1 << (5 + 7 * k)
+        trials.append(t)
+    for t in trials:
+        log_case("corrupt kept decision", t.tolist())
+        words[8:12] = torch.tensor(t.astype(np.int32), device="cuda")
+        torch.cuda.synchronize()
+        out, lse, hdr, tasks, offs, _ = _run(wl, cap=cap, workspace=ws)
+        _check_plan(wl, cap, hdr, tasks, offs, -1, 0)
+        assert np.array_equal(out.cpu().numpy(), ref_out.cpu().numpy())
+        assert np.array_equal(lse.cpu().numpy(), ref_lse.cpu().numpy())
+
+
 def test_device_plan_flags_overlong_row_and_plans_it_empty():
     """A length beyond max_pages_per_row * 16 is caught by the planner's own
     bounds check: that row comes out empty and the error word is set; the
