@@ -623,12 +623,14 @@ constexpr int kMaxDone = 64;
 // done (self-planned step), 2 first page loads issued, 3 prologue barrier
 // passed, 4 first round of the first task consumed, 5 last round of the
 // latest task consumed, 6 task loop left, 7 final arrivals and merges done,
-// 8 exit; slot 9 holds the XCD, slot 10 the tasks run.
+// 8 exit; slot 9 holds the XCD, slot 10 the tasks run; for the latest task,
+// 11 the last of the four waves' last rounds consumed, 12 the wave states in
+// LDS (barrier passed), 13 the combined state written.
 #ifdef PKV_TIMELINE
 constexpr int kTimelineSlots = 16;
 constexpr int kTimelineWorkgroups = 4096;
 __device__ unsigned long long timeline[kTimelineWorkgroups * kTimelineSlots];
-#define PKV_TL_DECL unsigned long long tl_[9] = {}; unsigned tl_tasks_ = 0
+#define PKV_TL_DECL unsigned long long tl_[14] = {}; unsigned tl_tasks_ = 0
 #define PKV_TL_MARK(i) (tl_[i] = __builtin_amdgcn_s_memrealtime())
 #define PKV_TL_TASK() (++tl_tasks_)
 #define PKV_TL_STORE()                                                                     \
@@ -641,6 +643,7 @@ __device__ unsigned long long timeline[kTimelineWorkgroups * kTimelineSlots];
       o[8] = __builtin_amdgcn_s_memrealtime();                                            \
       o[9] = xcc;                                                                         \
       o[10] = tl_tasks_;                                                                  \
+      for (int k_ = 11; k_ < 14; ++k_) o[k_] = tl_[k_];                                   \
     }                                                                                     \
   } while (0)
 #else
@@ -1163,6 +1166,9 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
   __shared__ int s_len[kStaged ? kRowStage : 1];
   __shared__ int s_off[kStaged ? kRowStage + 1 : 1];
   __shared__ int s_next[2];
+#ifdef PKV_TIMELINE
+  __shared__ unsigned long long s_tlw[kWaves];   // each wave's last round of its latest task
+#endif
   __shared__ vecE<E, 8> s_q[2][KK * 64];            // q operand of a task, per lane
   __shared__ float s_m[2][kWaves][16];
   __shared__ float s_l[2][kWaves][16];
@@ -1540,6 +1546,7 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
       if (last) {
         PKV_TL_MARK(5);
         PKV_TL_TASK();
+        if (lane == 0) s_tlw[wave] = __builtin_amdgcn_s_memrealtime();
       }
 #endif
       if (last && wave == 0) {
@@ -1563,6 +1570,11 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
         for (int e = 0; e < VW; ++e) s_o[wave][col][VW * (4 * grp + j) + e] = st.acc[e][j];
     }
     __syncthreads();
+#ifdef PKV_TIMELINE
+    PKV_TL_MARK(12);
+    tl_[11] = s_tlw[0];
+    for (int w_ = 1; w_ < kWaves; ++w_) tl_[11] = s_tlw[w_] > tl_[11] ? s_tlw[w_] : tl_[11];
+#endif
 
     // ---- combine the 4 waves' states; write the output or the partial
     if (cur.ok) {
@@ -1603,6 +1615,9 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
           }
         }
       }
+#ifdef PKV_TIMELINE
+      PKV_TL_MARK(13);
+#endif
       if (fuse && !direct) {
         // Fused merge, deferred: the split is counted in later, so waiting
         // for its stores does not also wait for the page loads of the tasks

@@ -17,6 +17,11 @@ Marks (per workgroup, microseconds from the launch's earliest entry):
   loop_end   task loop left
   merged     final arrivals and merges done
   exit       workgroup exit
+  waves_last the last of the four waves' last rounds of the latest task
+             ("last" is wave 0's)
+  states_lds the waves' states in LDS, barrier passed (latest task)
+  combined   the combined state of the latest task written (output or
+             partial)
 The summary gives each mark's median and maximum over the workgroups, the
 last-round and exit times per XCD, the tasks per workgroup, and a split of
 the launch into start (entry to the median first round), streaming (to the
@@ -41,7 +46,10 @@ ROOT = os.path.dirname(HERE)
 TIMELINE_LIB = os.path.join(HERE, "libpkv_timeline.so")
 SLOTS = 16
 WORKGROUPS = 4096
-MARKS = ("entry", "plan", "issued", "prologue", "first", "last", "loop_end", "merged", "exit")
+MARKS = ("entry", "plan", "issued", "prologue", "first", "last", "loop_end", "merged", "exit",
+         "waves_last", "states_lds", "combined")
+# slots of the marks in a workgroup's row (9 holds the XCD, 10 the tasks run)
+MARK_SLOTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 11, 12, 13)
 DEVICE_PLAN_MAX_SPLITS = 64
 
 
@@ -67,8 +75,9 @@ def _read(lib, grid):
         raise RuntimeError("pkv_timeline_read failed")
     d = buf.reshape(WORKGROUPS, SLOTS)[:grid].astype(np.int64)
     t0 = d[:, 0].min()
-    rel = (d[:, :9] - t0) / 100.0          # 100 MHz counter -> us
-    rel[d[:, :9] == 0] = np.nan            # marks a workgroup never reached
+    raw = d[:, list(MARK_SLOTS)]
+    rel = (raw - t0) / 100.0               # 100 MHz counter -> us
+    rel[raw == 0] = np.nan                 # marks a workgroup never reached
     return rel, d[:, 9], d[:, 10]
 
 
