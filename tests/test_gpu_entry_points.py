@@ -116,3 +116,38 @@ def test_runner_regrows_workspace_on_a_side_stream():
         assert np.array_equal(lse.cpu().numpy(), fresh[(mode, param)][1])
     assert dec.workspace.numel() > small
     assert dec.error_flags() == 0
+
+
+def test_runner_follows_the_current_stream():
+    """With no stream argument a step runs on torch's current stream, found
+    without building a Stream object: inside a side stream's context it is
+    that stream, and the result matches a step on the default stream bit
+    for bit."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    assert pkv.current_stream_ptr() == torch.cuda.current_stream().cuda_stream
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    cfg = wl.cfg
+    dec = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=cfg.B,
+                           max_pages_per_row=cfg.max_pages_per_row)
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
+    dec.set_inputs(wl.q, wl.k_pool, wl.v_pool, wl.block_table, wl.seq_lens, wl.seq_lens_np,
+                   cfg.scale, out, lse)
+    log_case("runner current stream", "default")
+    dec.run()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.cpu().numpy(), lse.cpu().numpy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert pkv.current_stream_ptr() == side.cuda_stream
+        out.fill_(float("nan"))
+        log_case("runner current stream", "side")
+        for _ in range(3):
+            dec.run()
+    side.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref_o)
+    assert np.array_equal(lse.cpu().numpy(), ref_l)
+    assert pkv.current_stream_ptr() == torch.cuda.current_stream().cuda_stream
+    assert dec.error_flags() == 0
