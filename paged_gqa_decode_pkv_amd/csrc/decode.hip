@@ -763,7 +763,7 @@ struct PickLds {
 // check, the key or the candidate-set test and the step searches.  The
 // decision only selects among valid plans, so a kept one can change a step's
 // speed, never its result.
-__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+__host__ __device__ inline uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   x *= 0x7feb352du;
   x ^= x >> 15;
@@ -780,8 +780,11 @@ __device__ __forceinline__ uint32_t plan_cache_check(uint32_t key, uint32_t mode
 }
 
 // Key of the policy's inputs other than the rows: shape, CU count, policy
-// parameters (their bit patterns).
-__device__ __forceinline__ uint32_t plan_cache_config_key(const pkv_policy_params& p, int B,
+// parameters (their bit patterns).  Computed on the host at launch and passed
+// in a preloaded kernel argument: on the device its 64 bytes of parameters
+// were an argument-segment load on the prologue's critical path (the
+// device-planned step measured 0.3-0.4 us faster without it).
+__host__ inline uint32_t plan_cache_config_key(const pkv_policy_params& p, int B,
                                                           int Hkv, int num_cus, int head_dim,
                                                           int max_pages) {
   uint32_t h = mix32(static_cast<uint32_t>(B) + 0x27d4eb2du);
@@ -1127,6 +1130,10 @@ __device__ __forceinline__ Round<R> first_round(const DecodeArgs& a,
 
 // Two workgroups per CU at d <= 128 (256 VGPRs each); one at d = 256, whose
 // larger tiles and accumulators need the AGPR half of the register file.
+// The first two arguments are preloaded into SGPRs: the task list and the
+// records it holds for a host plan; for a self-planned step (which builds
+// its records in the kernel) the second one is the key of the step's shape
+// and policy, the rows' part of which the kernel adds.
 template <int D, bool kStaged, class E, class KV, bool kSelfPlan, int kLoadMode>
 __global__ void __launch_bounds__(kThreads, D == 256 ? 1 : 2)
 pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArgs a,
@@ -1238,8 +1245,8 @@ pkv_decode_kernel(const int4* __restrict__ tasks_in, int32_t task_cap, DecodeArg
     }
     __syncthreads();
     int active_rows = 0, any_bad = 0;
-    uint32_t key = plan_cache_config_key(a.plan_pol, a.B, a.Hkv, a.plan_num_cus,
-                                         a.plan_head_dim, a.max_pages);
+    // a self-planned step gets its shape and policy key in `task_cap`
+    uint32_t key = static_cast<uint32_t>(task_cap);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       active_rows += s_plan[w];
@@ -1916,10 +1923,14 @@ int launch_mode(const DecodeArgs& da, const MergeArgs& ma, int grid, hipStream_t
     const int4* tasks = reinterpret_cast<const int4*>(da.tasks);
     const bool staged = da.B <= kRowStage;
     if (da.plan_out) {   // self-planned step (staged rows only; checked by the caller)
-      // (load_mode never gives mode 2 to a self-planned step)
+      // (load_mode never gives mode 2 to a self-planned step).  It builds
+      // its task list itself and reads no `tasks`: the second (preloaded)
+      // argument carries the key of its shape and policy instead.
+      const uint32_t key = plan_cache_config_key(da.plan_pol, da.B, da.Hkv, da.plan_num_cus,
+                                                 da.plan_head_dim, da.max_pages);
       hipLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, true, kMode == 2 ? 1 : kMode>),
-                         dim3(grid), dim3(kThreads), 0, stream, tasks, da.task_cap, da,
-                         da.block_table, da.seq_lens, da.split_offsets);
+                         dim3(grid), dim3(kThreads), 0, stream, tasks, static_cast<int32_t>(key),
+                         da, da.block_table, da.seq_lens, da.split_offsets);
     } else if (ev0 || ev_dec_end) {
       if (staged)
         hipExtLaunchKernelGGL((pkv_decode_kernel<D, true, E, KV, false, kMode>), dim3(grid),
