@@ -151,3 +151,48 @@ def test_runner_follows_the_current_stream():
     assert np.array_equal(lse.cpu().numpy(), ref_l)
     assert pkv.current_stream_ptr() == torch.cuda.current_stream().cuda_stream
     assert dec.error_flags() == 0
+
+
+def test_runner_plan_across_length_changes():
+    """Steps whose lengths move within their last page keep the plan (the
+    runner's device copy serves them); steps that cross a page boundary get a
+    new one (read in place from pinned memory, then copied for the next
+    steps).  Every step matches a fresh runner's bit for bit, in both launch
+    forms."""
+    import torch
+    import paged_gqa_decode_pkv_amd as pkv
+    wl = make_workload("b8_bimodal", SEED, device="cuda")
+    cfg = wl.cfg
+    base = wl.seq_lens_np.astype(np.int32).copy()
+    base[0] = max(1, (int(base[0]) - 2) // 16 * 16 + 1)    # a row one token into its last page
+    within = base - (base % 16 != 1) * (base > 1)          # same page counts
+    across = base - (base % 16 == 1)                        # fewer pages in some rows
+    assert (across != base).any() and (within != base).any()
+    seq_dev = torch.from_numpy(base.copy()).cuda()
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda")
+    dec = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=cfg.B,
+                           max_pages_per_row=cfg.max_pages_per_row)
+    steps = [base, base, within, within, base, across, across, within, base]
+    for two in (None, True):
+        for i, lens in enumerate(steps):
+            log_case("runner plan across lengths", i, "two" if two else "rule")
+            seq_dev.copy_(torch.from_numpy(lens))
+            dec.set_inputs(wl.q, wl.k_pool, wl.v_pool, wl.block_table, seq_dev, lens, cfg.scale,
+                           out, lse)
+            dec.run(two_launch=two)
+            fresh = pkv.PagedDecoder(cfg.Hq, cfg.Hkv, cfg.D, max_batch=cfg.B,
+                                     max_pages_per_row=cfg.max_pages_per_row)
+            out2 = torch.empty_like(wl.q)
+            lse2 = torch.empty_like(lse)
+            fresh.set_inputs(wl.q, wl.k_pool, wl.v_pool, wl.block_table, seq_dev, lens,
+                             cfg.scale, out2, lse2)
+            fresh.run(two_launch=two)
+            torch.cuda.synchronize()
+            assert dec.last == fresh.last
+            assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())
+            assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+            tasks, offs = dec.plan_arrays()
+            t2, o2 = fresh.plan_arrays()
+            assert np.array_equal(tasks, t2) and np.array_equal(offs, o2)
+    assert dec.error_flags() == 0
