@@ -279,9 +279,9 @@ def pkv_workspace_size(num_partial_slots: int, Hq: int, head_dim: int) -> int:
 def current_stream_ptr() -> int:
     """Raw pointer (hipStream_t) of torch's current stream on the current
     device: the value of ``torch.cuda.current_stream().cuda_stream`` without
-    building a Stream object, which takes about 3 us of Python per call
-    (twice the launch cost of a whole step's enqueue on the synchronised
-    path).  Falls back to the public call where torch lacks the raw getter."""
+    building a Stream object, which takes about 3 us of Python per call, as
+    much as the rest of a step's enqueue (policy, plan and launch).  Falls
+    back to the public call where torch lacks the raw getter."""
     import torch
     get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
     if get is None:
